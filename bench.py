@@ -1,0 +1,242 @@
+"""Benchmark of the dense GEMM hot path on one MI355X.
+
+One step is one gemm() call through the C ABI on the full workload: host
+checks, path and tile selection, and the matrix-core kernel with its fused
+epilogue (inputs already resident in HBM). The default workload is the
+compute-bound 8192^3 bf16 case with B stored [N,K] (transB = 1), alpha = 1,
+beta = 0.
+
+Prints ONE JSON line with TFLOP/s (2MNK/t), the roofline of the kernel
+(measured with HIP events on the stream the kernel runs on), the oracle's
+max relative error on sampled rows, and the CPU oracle timed on a bounded
+sample of the same workload on this host's cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline] [--cpu-seconds S]
+  python bench.py --copy-calibration   # plain copy of known size (counter scale)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}  # MI355X dense MFMA, published
+PEAK_HBM_GBS = 8000.0
+COPY_CAL_BYTES = 1 << 30
+
+
+def kernel_sources_digest() -> str:
+    """Digest of the kernel sources, to tell whether stored counters are stale."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_tile_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None if the
+    summary is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_digest") != kernel_sources_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(cfg, inp, seconds: float):
+    """Time the oracle (as it stands) on a bounded row sample of the workload."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    lda, ldb, ldc, _ = cfg.lds()
+    A = workloads.bits_u16(inp.A).reshape(-1)
+    B = workloads.bits_u16(inp.B).reshape(-1)
+    C = inp.C.numpy().reshape(-1) if inp.C is not None else None
+    dt = workloads.DTYPE_CODE[cfg.dtype]
+
+    def timed(nrows):
+        rows = np.arange(nrows)
+        t0 = time.perf_counter()
+        oracle.gemm_reference(cfg.M, cfg.N, cfg.K, dt, cfg.transA, cfg.transB, cfg.alpha,
+                              cfg.beta, A, lda, B, ldb, C, ldc, rows=rows, with_bound=False)
+        return time.perf_counter() - t0
+
+    rows = min(cfg.M, 64)
+    t = timed(rows)
+    # grow the sample so the measured call takes about `seconds`
+    if t < seconds / 4 and rows < cfg.M:
+        rows = int(min(cfg.M, max(rows, rows * (seconds / max(t, 1e-3)) * 0.8)))
+        rows = max(64, rows // 64 * 64)
+        t = timed(rows)
+    flops = 2.0 * rows * cfg.N * cfg.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of D ({rows}x{cfg.N}x{cfg.K}, fp64 numpy oracle "
+                      f"incl. operand decode), {t:.1f} s"}
+
+
+def copy_calibration():
+    import torch
+    dev = torch.device("cuda:0")
+    n = COPY_CAL_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": COPY_CAL_BYTES,
+                      "copy_calibration_bytes_written": COPY_CAL_BYTES, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gemm8192_nt")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(output-tile sharding needs no collective; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import dense_gemm_tile_amd as dgt
+    import workloads
+
+    cfg = workloads.CONFIGS[args.workload]
+    lda, ldb, ldc, ldd = cfg.lds()
+    inp = workloads.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    A, B = inp.A.to(dev), inp.B.to(dev)
+    C0 = inp.C.to(dev) if inp.C is not None else None
+    if cfg.inplace:
+        D = C0.clone()
+        C = D
+    else:
+        D = torch.empty((cfg.M, ldd), dtype=torch.float32, device=dev)
+        C = C0
+
+    def step():
+        dgt.gemm(cfg.M, cfg.N, cfg.K, cfg.dtype, cfg.transA, cfg.transB, cfg.alpha, cfg.beta,
+                 A, lda, B, ldb, C, ldc, D, ldd, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    path = dgt.gemm_last_path()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+
+    # Parity of what was timed: a fresh call, then sampled rows against the oracle.
+    max_rel = None
+    if not args.no_check:
+        import oracle
+        if cfg.inplace:
+            D.copy_(C0)
+        step()
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(0)
+        rows = np.unique(np.concatenate([[0, cfg.M - 1], rng.integers(0, cfg.M, 14)]))
+        D_ref, bound = oracle.gemm_reference(
+            cfg.M, cfg.N, cfg.K, workloads.DTYPE_CODE[cfg.dtype], cfg.transA, cfg.transB,
+            cfg.alpha, cfg.beta, workloads.bits_u16(inp.A).reshape(-1), lda,
+            workloads.bits_u16(inp.B).reshape(-1), ldb,
+            inp.C.numpy().reshape(-1) if inp.C is not None else None, ldc, rows=rows)
+        got = D[rows, : cfg.N].cpu().numpy().astype(np.float64)
+        rep = oracle.check(got, D_ref, bound)
+        if not rep["ok"]:
+            print(f"PARITY FAILURE on sampled rows: {rep}", file=sys.stderr)
+            sys.exit(1)
+        max_rel = rep["max_rel_err"]
+
+    flops = float(cfg.flops)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    traffic = stored_traffic(cfg.name)
+    out = {
+        "metric": "TFLOP/s (2MNK/t) bf16 M=N=K=8192 + % of MFMA peak; oracle max rel err",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; A, B normal(0, 1/sqrt(K)) in bf16)",
+        "config": {"workload": cfg.name, "M": cfg.M, "N": cfg.N, "K": cfg.K,
+                   "transA": cfg.transA, "transB": cfg.transB, "alpha": cfg.alpha,
+                   "beta": cfg.beta, "parallelism": "single GPU"},
+        "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
+        "oracle_max_rel_err": max_rel,
+        "path": path,
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,93 @@
+// Internal declarations shared by the host dispatcher and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dgt {
+
+// Everything a kernel needs for one call. Plain values only.
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  const float* C;
+  float* D;
+  int64_t lda, ldb, ldc, ldd;  // leading dimensions, in elements
+  int M, N, K;
+  float alpha, beta;
+  int epi;       // Epilogue kind, see below
+  int tiles_m;   // output tiles along M / N for the tile scheduler
+  int tiles_n;
+  int group_m;   // tile-row group height of the grouped order
+};
+
+// Epilogue kinds. All three compute alpha*acc + beta*C; the specialised ones
+// only skip work whose result is known exactly (C not read when beta == 0,
+// multiplies by 1 dropped when alpha == beta == 1).
+enum Epilogue : int {
+  EPI_BETA0 = 0,      // D = alpha*acc          (C never read)
+  EPI_ACC_PLUS_C = 1, // D = acc + C            (alpha == 1, beta == 1)
+  EPI_GENERAL = 2,    // D = fma(beta, C, alpha*acc)
+};
+
+// Number of XCDs (each with its own L2) on MI355X. Workgroups of one launch are
+// handed to XCDs round-robin by workgroup id; the scheduler below regroups ids
+// so that tiles which share operand panels land on the same XCD. Any value
+// gives a correct (bijective) mapping; 8 is the one that matches the chip.
+constexpr int kNumXcd = 8;
+
+// Workgroup id -> logical tile index: XCD x receives ids x, x+8, x+16, ... and
+// the remap gives those ids one contiguous range of logical indices.
+__host__ __device__ inline int xcd_remap(int bid, int nwg) {
+  const int xcd = bid % kNumXcd;
+  const int idx = bid / kNumXcd;
+  const int q = nwg / kNumXcd;
+  const int r = nwg % kNumXcd;
+  return xcd * q + (xcd < r ? xcd : r) + idx;
+}
+
+// Logical tile index -> (tile row, tile column) in grouped order: walk
+// group_m tile rows column by column, so that consecutive indices share the
+// A row panels of the group and each B column panel is reused group_m times.
+__host__ __device__ inline void grouped_tile(int lid, int tiles_m, int tiles_n, int group_m,
+                                             int& tm, int& tn) {
+  const int per_group = group_m * tiles_n;
+  const int g = lid / per_group;
+  const int first_m = g * group_m;
+  const int rows_left = tiles_m - first_m;
+  const int gsz = rows_left < group_m ? rows_left : group_m;
+  const int in = lid - g * per_group;
+  tm = first_m + in % gsz;
+  tn = in / gsz;
+}
+
+__host__ __device__ inline void schedule_tile(int bid, int tiles_m, int tiles_n, int group_m,
+                                              int& tm, int& tn) {
+  const int lid = xcd_remap(bid, tiles_m * tiles_n);
+  grouped_tile(lid, tiles_m, tiles_n, group_m, tm, tn);
+}
+
+// Launchers (defined next to their kernels). They return the HIP status of
+// the launch.
+struct MfmaTileInfo {
+  const char* name;
+  int bm, bn, bk;
+  int waves_m, waves_n;
+  int atom_m, atom_n, atom_k;
+};
+
+// Matrix-core tile configurations, largest first.
+enum MfmaTile : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x64 = 2, TILE_16x16 = 3,
+                      NUM_MFMA_TILES = 4 };
+const MfmaTileInfo& mfma_tile_info(int tile);
+
+hipError_t launch_mfma(int tile, int dtype, bool transA, bool transB, bool masked,
+                       const GemmArgs& a, hipStream_t stream);
+// Output tile of the VALU-FMA fallback.
+constexpr int kFmaTileM = 64, kFmaTileN = 64;
+
+hipError_t launch_fma(int dtype, bool transA, bool transB, const GemmArgs& a,
+                      hipStream_t stream);
+hipError_t launch_scale_c(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace dgt

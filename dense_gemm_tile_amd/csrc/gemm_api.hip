@@ -1,0 +1,298 @@
+// Host side of the C ABI: argument checks, path and tile selection, launch.
+//
+// Checks follow the contract of the TIRx `gemm` primitive, which rejects a
+// call rather than emit a wrong instruction (TVM TIRx `gemm`: "What it
+// accepts"; its Chinese restatement, section 2, lists the rejection reasons and
+// the normalisation to A=[M,K], B=[K,N]). Shapes that do not tile the
+// matrix-core atom are not rejected: they run masked, or on the VALU fallback,
+// and the chosen path and its reason are recorded, like the debug log that
+// names each declined dot (Phobos `@tensorcore`, "When it declines").
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/dense_gemm_tile.h"
+#include "common.h"
+
+namespace dgt {
+namespace {
+
+thread_local std::string g_err;
+thread_local std::string g_path;
+
+// Largest dimension the int32 index arithmetic in the kernels supports.
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1024;
+
+struct Plan {
+  bool noop = false;        // M == 0 or N == 0
+  bool scale_only = false;  // K == 0 or alpha == 0: D = beta*C
+  bool mfma = false;
+  int tile = 0;
+  bool masked = false;
+  int epi = EPI_BETA0;
+  GemmArgs args{};
+};
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+const char* env(const char* name) {
+  const char* v = std::getenv(name);
+  return (v && *v) ? v : nullptr;
+}
+
+// Byte extent of a row-major [rows, cols] matrix with leading dimension ld.
+unsigned __int128 extent_bytes(int64_t rows, int64_t cols, int64_t ld, int elem) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return ((unsigned __int128)(rows - 1) * (unsigned __int128)ld + (unsigned __int128)cols) *
+         (unsigned __int128)elem;
+}
+
+bool overlaps(const void* p, unsigned __int128 np, const void* q, unsigned __int128 nq) {
+  if (np == 0 || nq == 0) return false;
+  const unsigned __int128 a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + nq && b < a + np;
+}
+
+std::string pitch_reason(const char* name, const void* ptr, int64_t ld) {
+  char buf[160];
+  if ((uintptr_t)ptr % 16 != 0) {
+    std::snprintf(buf, sizeof buf, "%s base address is not 16-byte aligned", name);
+  } else {
+    std::snprintf(buf, sizeof buf, "%s row pitch %lld B is not a multiple of 16 B", name,
+                  (long long)(ld * 2));
+  }
+  return buf;
+}
+
+int choose_tile(int64_t M, int64_t N) {
+  auto count = [&](int t) {
+    const MfmaTileInfo& ti = mfma_tile_info(t);
+    return ((M + ti.bm - 1) / ti.bm) * ((N + ti.bn - 1) / ti.bn);
+  };
+  if (count(TILE_256x256) >= 256) return TILE_256x256;
+  if (count(TILE_128x128) >= 128) return TILE_128x128;
+  if (M <= 16 && N <= 16) return TILE_16x16;
+  return TILE_64x64;
+}
+
+int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB, float alpha,
+              float beta, const void* A, int64_t lda, const void* B, int64_t ldb, const float* C,
+              int64_t ldc, const float* D, int64_t ldd, Plan& plan) {
+  g_err.clear();
+  g_path.clear();
+  char buf[256];
+  transA = transA != 0;
+  transB = transB != 0;
+  if (M < 0 || N < 0 || K < 0) {
+    std::snprintf(buf, sizeof buf, "negative dimension: M=%lld N=%lld K=%lld", (long long)M,
+                  (long long)N, (long long)K);
+    return fail(GEMM_ERR_INVALID_ARG, buf);
+  }
+  if (dtype != GEMM_DTYPE_F16 && dtype != GEMM_DTYPE_BF16) {
+    std::snprintf(buf, sizeof buf, "dtype code %d is neither f16 (0) nor bf16 (1)", dtype);
+    return fail(GEMM_ERR_UNSUPPORTED, buf);
+  }
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) {
+    return fail(GEMM_ERR_UNSUPPORTED, "a dimension exceeds 2^31-1024");
+  }
+  const int64_t min_lda = transA ? M : K, min_ldb = transB ? K : N;
+  if (lda < (min_lda > 1 ? min_lda : 1)) {
+    std::snprintf(buf, sizeof buf, "lda=%lld is smaller than %s=%lld", (long long)lda,
+                  transA ? "M" : "K", (long long)min_lda);
+    return fail(GEMM_ERR_INVALID_ARG, buf);
+  }
+  if (ldb < (min_ldb > 1 ? min_ldb : 1)) {
+    std::snprintf(buf, sizeof buf, "ldb=%lld is smaller than %s=%lld", (long long)ldb,
+                  transB ? "K" : "N", (long long)min_ldb);
+    return fail(GEMM_ERR_INVALID_ARG, buf);
+  }
+  if (ldd < (N > 1 ? N : 1)) {
+    std::snprintf(buf, sizeof buf, "ldd=%lld is smaller than N=%lld", (long long)ldd,
+                  (long long)N);
+    return fail(GEMM_ERR_INVALID_ARG, buf);
+  }
+  const bool reads_c = beta != 0.0f;
+  if (reads_c && ldc < (N > 1 ? N : 1)) {
+    std::snprintf(buf, sizeof buf, "ldc=%lld is smaller than N=%lld", (long long)ldc,
+                  (long long)N);
+    return fail(GEMM_ERR_INVALID_ARG, buf);
+  }
+  if (M == 0 || N == 0) {
+    plan.noop = true;
+    g_path = "noop: empty output";
+    return GEMM_OK;
+  }
+  const bool reads_ab = K > 0 && alpha != 0.0f;
+  if (!D) return fail(GEMM_ERR_INVALID_ARG, "D is NULL");
+  if ((uintptr_t)D % 4) return fail(GEMM_ERR_INVALID_ARG, "D is not 4-byte aligned");
+  if (reads_c && !C) return fail(GEMM_ERR_INVALID_ARG, "C is NULL but beta != 0");
+  if (reads_c && (uintptr_t)C % 4) return fail(GEMM_ERR_INVALID_ARG, "C is not 4-byte aligned");
+  if (reads_ab && (!A || !B)) return fail(GEMM_ERR_INVALID_ARG, "A or B is NULL");
+  if (reads_ab && ((uintptr_t)A % 2 || (uintptr_t)B % 2))
+    return fail(GEMM_ERR_INVALID_ARG, "A or B is not 2-byte aligned");
+
+  // Aliasing: D is written, so it must not overlap anything it is computed
+  // from, except C itself in the exact in-place form.
+  const unsigned __int128 d_ext = extent_bytes(M, N, ldd, 4);
+  if (reads_c) {
+    const unsigned __int128 c_ext = extent_bytes(M, N, ldc, 4);
+    const bool same = (const void*)C == (const void*)D && ldc == ldd;
+    if (!same && overlaps(C, c_ext, D, d_ext))
+      return fail(GEMM_ERR_ALIAS, "D overlaps C without being the same matrix (C == D and "
+                                  "ldc == ldd is the only allowed overlap)");
+  }
+  if (reads_ab) {
+    const unsigned __int128 a_ext =
+        extent_bytes(transA ? K : M, transA ? M : K, lda, 2);
+    const unsigned __int128 b_ext =
+        extent_bytes(transB ? N : K, transB ? K : N, ldb, 2);
+    if (overlaps(A, a_ext, D, d_ext)) return fail(GEMM_ERR_ALIAS, "D overlaps A");
+    if (overlaps(B, b_ext, D, d_ext)) return fail(GEMM_ERR_ALIAS, "D overlaps B");
+  }
+
+  GemmArgs& a = plan.args;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = const_cast<float*>(D);
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = reads_c ? ldc : ldd;
+  a.ldd = ldd;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.group_m = 8;
+  plan.epi = !reads_c ? EPI_BETA0 : (alpha == 1.0f && beta == 1.0f ? EPI_ACC_PLUS_C : EPI_GENERAL);
+  a.epi = plan.epi;
+  const char* epi_name = plan.epi == EPI_BETA0 ? "beta0" : plan.epi == EPI_ACC_PLUS_C ? "acc+c" : "general";
+
+  if (!reads_ab) {
+    plan.scale_only = true;
+    std::snprintf(buf, sizeof buf, "scale: D = beta*C (%s)", K == 0 ? "K == 0" : "alpha == 0");
+    g_path = buf;
+    return GEMM_OK;
+  }
+
+  // Path selection. The matrix-core path stages A and B with 16-byte loads,
+  // so each operand's base and row pitch must be multiples of 16 bytes.
+  std::string decline;
+  if ((uintptr_t)A % 16 || (lda * 2) % 16) decline = pitch_reason("A", A, lda);
+  else if ((uintptr_t)B % 16 || (ldb * 2) % 16) decline = pitch_reason("B", B, ldb);
+  const char* force = env("GEMM_FORCE_PATH");
+  if (force && std::strcmp(force, "fma") == 0) {
+    decline = "forced by GEMM_FORCE_PATH=fma";
+  } else if (force && std::strcmp(force, "mfma") == 0) {
+    if (!decline.empty())
+      return fail(GEMM_ERR_UNSUPPORTED, "GEMM_FORCE_PATH=mfma but " + decline);
+  } else if (force) {
+    return fail(GEMM_ERR_INVALID_ARG, std::string("GEMM_FORCE_PATH must be mfma or fma, got ") + force);
+  }
+  const char* ops = transA ? (transB ? "TT" : "TN") : (transB ? "NT" : "NN");
+
+  if (!decline.empty()) {
+    plan.mfma = false;
+    a.tiles_m = (int)((M + kFmaTileM - 1) / kFmaTileM);
+    a.tiles_n = (int)((N + kFmaTileN - 1) / kFmaTileN);
+    std::snprintf(buf, sizeof buf, "fma t%dx%dx16 %s epi=%s: %s", kFmaTileM, kFmaTileN, ops,
+                  epi_name, decline.c_str());
+    g_path = buf;
+    return GEMM_OK;
+  }
+
+  int tile = choose_tile(M, N);
+  if (const char* ft = env("GEMM_FORCE_TILE")) {
+    int found = -1;
+    for (int t = 0; t < NUM_MFMA_TILES; ++t)
+      if (std::strcmp(ft, mfma_tile_info(t).name) == 0) found = t;
+    if (found < 0)
+      return fail(GEMM_ERR_INVALID_ARG, std::string("GEMM_FORCE_TILE names no tile: ") + ft);
+    tile = found;
+  }
+  const MfmaTileInfo& ti = mfma_tile_info(tile);
+  plan.mfma = true;
+  plan.tile = tile;
+  plan.masked = (M % ti.bm) || (N % ti.bn) || (K % ti.bk);
+  a.tiles_m = (int)((M + ti.bm - 1) / ti.bm);
+  a.tiles_n = (int)((N + ti.bn - 1) / ti.bn);
+  if ((int64_t)a.tiles_m * a.tiles_n > 0x7fffffff)
+    return fail(GEMM_ERR_UNSUPPORTED, "too many output tiles for one launch");
+  std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s", ti.name, ti.waves_m,
+                ti.waves_n, ti.atom_m, ti.atom_n, ti.atom_k, ops, epi_name,
+                plan.masked ? " masked" : "");
+  g_path = buf;
+  return GEMM_OK;
+}
+
+void log_call(int64_t M, int64_t N, int64_t K, int status) {
+  const char* lv = env("GEMM_LOG");
+  if (!lv || std::strcmp(lv, "debug") != 0) return;
+  if (status == GEMM_OK)
+    std::fprintf(stderr, "[gemm] M=%lld N=%lld K=%lld -> %s\n", (long long)M, (long long)N,
+                 (long long)K, g_path.c_str());
+  else
+    std::fprintf(stderr, "[gemm] M=%lld N=%lld K=%lld -> error %d: %s\n", (long long)M,
+                 (long long)N, (long long)K, status, g_err.c_str());
+}
+
+}  // namespace
+}  // namespace dgt
+
+extern "C" {
+
+int gemm(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB, float alpha,
+         float beta, const void* A, int64_t lda, const void* B, int64_t ldb, const float* C,
+         int64_t ldc, float* D, int64_t ldd, void* stream) {
+  using namespace dgt;
+  Plan plan;
+  int st = plan_call(M, N, K, dtype, transA, transB, alpha, beta, A, lda, B, ldb, C, ldc, D, ldd,
+                     plan);
+  if (st == GEMM_OK && !plan.noop) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (plan.scale_only) e = launch_scale_c(plan.args, s);
+    else if (plan.mfma)
+      e = launch_mfma(plan.tile, dtype, transA != 0, transB != 0, plan.masked, plan.args, s);
+    else e = launch_fma(dtype, transA != 0, transB != 0, plan.args, s);
+    if (e != hipSuccess)
+      st = fail(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  }
+  log_call(M, N, K, st);
+  return st;
+}
+
+int gemm_validate(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB, float alpha,
+                  float beta, const void* A, int64_t lda, const void* B, int64_t ldb,
+                  const float* C, int64_t ldc, const float* D, int64_t ldd) {
+  dgt::Plan plan;
+  int st = dgt::plan_call(M, N, K, dtype, transA, transB, alpha, beta, A, lda, B, ldb, C, ldc, D,
+                          ldd, plan);
+  dgt::log_call(M, N, K, st);
+  return st;
+}
+
+const char* gemm_last_error(void) { return dgt::g_err.c_str(); }
+
+const char* gemm_last_path(void) { return dgt::g_path.c_str(); }
+
+int gemm_tile_order(int64_t tiles_m, int64_t tiles_n, int group_m, int32_t* tm, int32_t* tn) {
+  if (tiles_m <= 0 || tiles_n <= 0 || group_m < 1 || !tm || !tn ||
+      tiles_m * tiles_n > 0x7fffffff)
+    return dgt::fail(GEMM_ERR_INVALID_ARG, "gemm_tile_order: bad arguments");
+  const int total = (int)(tiles_m * tiles_n);
+  for (int w = 0; w < total; ++w) {
+    int m, n;
+    dgt::schedule_tile(w, (int)tiles_m, (int)tiles_n, group_m, m, n);
+    tm[w] = m;
+    tn[w] = n;
+  }
+  return GEMM_OK;
+}
+
+}  // extern "C"

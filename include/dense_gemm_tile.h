@@ -1,0 +1,124 @@
+/*
+ * dense_gemm_tile.h -- C ABI of the MI355X (gfx950) dense GEMM library
+ * (libdense_gemm_tile_amd.so).
+ *
+ * Operation (all matrices row-major):
+ *
+ *   D = alpha * op(A) @ op(B) + beta * C
+ *
+ *   op(A)[i,k] = transA ? A[k*lda + i] : A[i*lda + k]      (op(A) is M x K)
+ *   op(B)[k,j] = transB ? B[j*ldb + k] : B[k*ldb + j]      (op(B) is K x N)
+ *   C[i,j] = C[i*ldc + j],  D[i,j] = D[i*ldd + j]           (M x N, float32)
+ *
+ * This is the contraction of the TIRx `gemm` tile primitive (Apache TVM docs,
+ * TIRx tile primitives, `gemm`: opening paragraph), with A and B f16 or bf16
+ * and a float32 accumulator ("What it accepts", dtype row). The transpose flags
+ * describe only the stored orientation ("Algorithm" step 1). alpha and beta are
+ * general float32 scalars as in the Phobos gemm example's epilogue (Phobos docs,
+ * `@tensorcore`, the sm_75/sm_80 kernel pair); beta == 0 means C is not read and
+ * D starts from zero (TVM `gemm`, "How inputs change the algorithm", beta row).
+ * D may be the same buffer as C (the in-place accumulate form, as the TVM demo
+ * passes its D fragment as C, and the Phobos kernel stores back into C).
+ *
+ * Shapes that do not tile the matrix-core atom are not an error: they run on a
+ * masked matrix-core path or on a VALU-FMA fallback with the same result up to
+ * rounding (Phobos `@tensorcore`, "When it declines"). gemm_last_path() names
+ * the path taken and, for the fallback, why.
+ *
+ * Pointers: A, B, C, D are DEVICE pointers owned by the caller. The library
+ * allocates, frees and synchronises nothing. Work is enqueued on `stream`
+ * (a hipStream_t; NULL means the default stream) and gemm() returns before it
+ * completes. Error and path strings are thread-local; concurrent calls on
+ * different threads are safe.
+ */
+#ifndef DENSE_GEMM_TILE_H
+#define DENSE_GEMM_TILE_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define GEMM_API __attribute__((visibility("default")))
+#else
+#define GEMM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. Any non-zero return launches nothing (except GEMM_ERR_HIP,
+ * which reports a failed launch) and sets gemm_last_error(). */
+#define GEMM_OK 0
+#define GEMM_ERR_INVALID_ARG 1 /* negative dim, ld too small, NULL or misaligned pointer */
+#define GEMM_ERR_UNSUPPORTED 2 /* dtype code not 0/1, or a forced path that cannot run */
+#define GEMM_ERR_ALIAS 3       /* D overlaps A or B, or overlaps C other than exactly */
+#define GEMM_ERR_HIP 4         /* a HIP runtime call failed; message has its text */
+
+/* Operand dtype codes (A and B share one; C and D are always float32). */
+#define GEMM_DTYPE_F16 0
+#define GEMM_DTYPE_BF16 1
+
+/*
+ * gemm: enqueue D = alpha*op(A)@op(B) + beta*C on `stream`.
+ *
+ * M, N, K   >= 0. M == 0 or N == 0: nothing to do, returns GEMM_OK.
+ *           K == 0 or alpha == 0: D = beta*C (A and B are not read).
+ * dtype     GEMM_DTYPE_F16 or GEMM_DTYPE_BF16, the element type of A and B.
+ * transA/B  0 or 1 (any non-zero means 1). transA: A is stored [K][M];
+ *           transB: B is stored [N][K].
+ * lda       >= max(1, transA ? M : K), in elements; ldb >= max(1, transB ? K : N);
+ *           ldd >= max(1, N); ldc >= max(1, N) when beta != 0.
+ * A, B      device pointers, 2-byte aligned; may be NULL only when K == 0 or
+ *           alpha == 0.
+ * C         device float32 pointer, 4-byte aligned; ignored (may be NULL)
+ *           when beta == 0.
+ * D         device float32 pointer, 4-byte aligned.
+ * Aliasing  D must not overlap A or B. D may equal C exactly (same pointer and
+ *           ldc == ldd); any other overlap of C and D is rejected.
+ * stream    hipStream_t cast to void*.
+ *
+ * Environment: GEMM_LOG=debug prints one line per call to stderr (path, tile,
+ * reason); GEMM_FORCE_PATH=mfma|fma forces the matrix-core or the VALU path
+ * (forcing mfma on operands it cannot stage returns GEMM_ERR_UNSUPPORTED);
+ * GEMM_FORCE_TILE=<tile name> picks a matrix-core tile configuration.
+ */
+GEMM_API int gemm(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB,
+         float alpha, float beta,
+         const void* A, int64_t lda, const void* B, int64_t ldb,
+         const float* C, int64_t ldc, float* D, int64_t ldd, void* stream);
+
+/*
+ * gemm_validate: the host-side part of gemm() without any launch and without
+ * touching a GPU: argument checks, then path and tile selection. Returns the
+ * status gemm() would return before launching, and records the chosen path in
+ * gemm_last_path(). Pointers are only compared, never dereferenced.
+ */
+GEMM_API int gemm_validate(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB,
+                  float alpha, float beta,
+                  const void* A, int64_t lda, const void* B, int64_t ldb,
+                  const float* C, int64_t ldc, const float* D, int64_t ldd);
+
+/* Message for the last non-zero return on this thread ("" if none). The
+ * pointer stays valid until the next call on this thread. */
+GEMM_API const char* gemm_last_error(void);
+
+/* Path of the last gemm()/gemm_validate() on this thread, e.g.
+ * "mfma t256x256x64 w2x2 a32x32x16 NT epi=beta0" or
+ * "fma: A row pitch is not 16-byte aligned". Same lifetime as above. */
+GEMM_API const char* gemm_last_path(void);
+
+/*
+ * gemm_tile_order: the output-tile scheduler's workgroup -> tile map, computed
+ * on the host (the kernels use the same function). For tiles_m x tiles_n tiles
+ * it writes, for each workgroup id w in [0, tiles_m*tiles_n), the tile row
+ * tm[w] and column tn[w]. tm and tn are host arrays of tiles_m*tiles_n int32.
+ * group_m is the tile-row group height of the grouped order (>= 1).
+ * Returns GEMM_OK or GEMM_ERR_INVALID_ARG.
+ */
+GEMM_API int gemm_tile_order(int64_t tiles_m, int64_t tiles_n, int group_m, int32_t* tm, int32_t* tn);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_GEMM_TILE_H */

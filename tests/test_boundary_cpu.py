@@ -1,0 +1,203 @@
+"""Host-side tests of the C-ABI library: exports, argument checks, path choice
+and the tile scheduler. Nothing here launches a kernel or needs a GPU; pointer
+arguments are fake addresses that the library only compares."""
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    so = os.path.join(ROOT, "dense_gemm_tile_amd", "libdense_gemm_tile_amd.so")
+    if not os.path.exists(so):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_dgt_build", os.path.join(ROOT, "dense_gemm_tile_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    import dense_gemm_tile_amd as dgt
+    return dgt
+
+
+def _declared_symbols():
+    names = []
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            names += re.findall(r"GEMM_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+    return names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_symbols()
+    assert {"gemm", "gemm_validate", "gemm_last_error", "gemm_last_path",
+            "gemm_tile_order"} <= set(names)
+    so = lib.LIB_PATH
+    out = subprocess.run(["nm", "-D", "--defined-only", so], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    # nothing but the C ABI is exported from our own code
+    ours = {n for n in exported if n.startswith(("gemm", "_ZN3dgt"))}
+    assert ours == set(names)
+
+
+# Fake, suitably aligned device addresses: never dereferenced on the host.
+A0, B0, C0, D0 = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def _v(lib, M=64, N=64, K=64, dtype=0, tA=0, tB=0, alpha=1.0, beta=0.0, A=A0, lda=None,
+       B=B0, ldb=None, C=C0, ldc=None, D=D0, ldd=None):
+    lda = lda if lda is not None else (M if tA else K)
+    ldb = ldb if ldb is not None else (K if tB else N)
+    ldc = ldc if ldc is not None else N
+    ldd = ldd if ldd is not None else N
+    return lib.gemm_validate(M, N, K, dtype, tA, tB, alpha, beta, A, lda, B, ldb, C, ldc, D, ldd)
+
+
+def test_valid_call_selects_mfma(lib):
+    assert _v(lib) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma ")
+    assert lib.gemm_last_error() == ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), 1), (dict(N=-5), 1), (dict(K=-2), 1),
+    (dict(dtype=2), 2), (dict(dtype=-1), 2),
+    (dict(lda=63), 1), (dict(tA=1, lda=63), 1), (dict(ldb=63), 1), (dict(tB=1, ldb=63), 1),
+    (dict(ldd=63), 1), (dict(beta=1.0, ldc=63), 1),
+    (dict(D=0), 1), (dict(A=0), 1), (dict(B=0), 1), (dict(beta=0.5, C=0), 1),
+    (dict(D=D0 + 2), 1), (dict(beta=1.0, C=C0 + 2), 1), (dict(A=A0 + 1), 1),
+    (dict(M=1 << 31), 2),
+])
+def test_argument_errors(lib, kw, code):
+    assert _v(lib, **kw) == code
+    assert lib.gemm_last_error() != ""
+
+
+def test_ld_check_is_not_needed_for_unread_c(lib):
+    # beta == 0: C is not read, so ldc and C itself are ignored
+    assert _v(lib, beta=0.0, C=0, ldc=0) == lib.GEMM_OK
+
+
+def test_alias_rules(lib):
+    nbytes_d = 64 * 64 * 4
+    assert _v(lib, beta=1.0, C=D0, ldc=64, D=D0, ldd=64) == lib.GEMM_OK  # exact in-place
+    assert _v(lib, beta=1.0, C=D0, ldc=128, D=D0, ldd=64) == lib.GEMM_ERR_ALIAS
+    assert _v(lib, beta=1.0, C=D0 + 64, D=D0) == lib.GEMM_ERR_ALIAS
+    assert _v(lib, beta=1.0, C=D0 + nbytes_d, D=D0) == lib.GEMM_OK  # adjacent, no overlap
+    assert _v(lib, A=D0 + 1024, D=D0) == lib.GEMM_ERR_ALIAS
+    assert _v(lib, B=D0 - 64, D=D0) == lib.GEMM_ERR_ALIAS
+    assert _v(lib, B=D0 - 64 * 64 * 2, D=D0) == lib.GEMM_OK  # B ends where D begins
+    # C overlapping D is fine when C is not read
+    assert _v(lib, beta=0.0, C=D0 + 4, D=D0) == lib.GEMM_OK
+
+
+def test_empty_and_degenerate_calls(lib):
+    assert _v(lib, M=0, A=0, B=0, D=0) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("noop")
+    assert _v(lib, N=0, A=0, B=0, D=0, ldb=1, ldd=1) == lib.GEMM_OK
+    assert _v(lib, N=0, A=0, B=0, D=0) == lib.GEMM_ERR_INVALID_ARG  # ld must be >= 1
+    assert _v(lib, K=0, A=0, B=0, beta=0.5, lda=1) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("scale")
+    assert _v(lib, alpha=0.0, A=0, B=0, beta=2.0) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("scale")
+    assert _v(lib, K=0, A=0, B=0, beta=0.0, C=0, lda=1) == lib.GEMM_OK
+
+
+def test_unaligned_pitch_falls_back_without_error(lib):
+    # transposed f16 A with lda = 4097: an 8194-byte row pitch
+    st = _v(lib, M=4097, N=1000, K=1032, tA=1, lda=4097, alpha=2.0, beta=-1.0)
+    assert st == lib.GEMM_OK
+    path = lib.gemm_last_path()
+    assert path.startswith("fma ") and "A row pitch 8194 B" in path, path
+    assert _v(lib, A=A0 + 2) == lib.GEMM_OK
+    assert "A base address is not 16-byte aligned" in lib.gemm_last_path()
+    assert _v(lib, ldb=72) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma ")  # 144-byte pitch is fine
+    assert _v(lib, ldb=67) == lib.GEMM_OK
+    assert "B row pitch 134 B" in lib.gemm_last_path()
+
+
+def test_ragged_dims_stay_on_mfma_masked(lib):
+    assert _v(lib, M=4097, N=1000, K=1032, tA=1, lda=4104) == lib.GEMM_OK
+    path = lib.gemm_last_path()
+    assert path.startswith("mfma ") and path.endswith("masked"), path
+    assert _v(lib, M=16, N=8, K=16) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma t16x16x64"), lib.gemm_last_path()
+
+
+def test_tile_and_epilogue_choice(lib):
+    assert _v(lib, M=8192, N=8192, K=8192, tB=1, dtype=1) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "mfma t256x256x64 w2x2 a32x32x16 NT epi=beta0"
+    assert _v(lib, M=4096, N=4096, K=4096, dtype=1, beta=1.0, C=D0) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "mfma t256x256x64 w2x2 a32x32x16 NN epi=acc+c"
+    assert _v(lib, M=512, N=512, K=512, alpha=1.5, beta=0.5) == lib.GEMM_OK
+    assert "epi=general" in lib.gemm_last_path()
+
+
+def test_force_path_and_tile(lib, monkeypatch):
+    monkeypatch.setenv("GEMM_FORCE_PATH", "fma")
+    assert _v(lib) == lib.GEMM_OK
+    assert "forced by GEMM_FORCE_PATH=fma" in lib.gemm_last_path()
+    monkeypatch.setenv("GEMM_FORCE_PATH", "mfma")
+    assert _v(lib, A=A0 + 2) == lib.GEMM_ERR_UNSUPPORTED
+    monkeypatch.setenv("GEMM_FORCE_PATH", "bogus")
+    assert _v(lib) == lib.GEMM_ERR_INVALID_ARG
+    monkeypatch.delenv("GEMM_FORCE_PATH")
+    monkeypatch.setenv("GEMM_FORCE_TILE", "t128x128x64")
+    assert _v(lib, M=8192, N=8192, K=8192) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma t128x128x64")
+    monkeypatch.setenv("GEMM_FORCE_TILE", "t7x7")
+    assert _v(lib) == lib.GEMM_ERR_INVALID_ARG
+
+
+def test_debug_log_names_the_declined_path():
+    code = (
+        "import dense_gemm_tile_amd as d\n"
+        "d.gemm_validate(4097,1000,1032,0,1,0,2.0,-1.0,0x10000000,4097,0x20000000,1000,"
+        "0x30000000,1000,0x40000000,1000)\n"
+        "d.gemm_validate(-1,1,1,0,0,0,1.0,0.0,0,1,0,1,0,1,0,1)\n")
+    env = dict(os.environ, GEMM_LOG="debug", PYTHONPATH=ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[gemm]")]
+    assert len(lines) == 2
+    assert "M=4097 N=1000 K=1032 -> fma " in lines[0] and "A row pitch 8194 B" in lines[0]
+    assert "error 1: negative dimension" in lines[1]
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n,group", [
+    (1, 1, 8), (32, 32, 8), (16, 16, 8), (17, 4, 8), (33, 8, 8), (65, 16, 8), (3, 100, 8),
+    (100, 3, 4), (7, 9, 1), (8, 8, 16), (257, 1, 8), (1, 257, 8)])
+def test_tile_order_is_a_bijection(lib, tiles_m, tiles_n, group):
+    tm, tn = lib.gemm_tile_order(tiles_m, tiles_n, group)
+    pairs = set(zip(tm, tn))
+    assert len(pairs) == tiles_m * tiles_n
+    assert all(0 <= m < tiles_m and 0 <= n < tiles_n for m, n in pairs)
+
+
+def test_tile_order_keeps_an_xcd_on_a_compact_block(lib):
+    # 32 x 32 tiles: the first 32 workgroups each XCD runs (ids x, x+8, ...)
+    # should cover few row and column panels (8 rows x 4 columns in grouped order).
+    tm, tn = lib.gemm_tile_order(32, 32, 8)
+    for xcd in range(8):
+        ids = [xcd + 8 * i for i in range(32)]
+        rows = {tm[w] for w in ids}
+        cols = {tn[w] for w in ids}
+        assert len(rows) * len(cols) <= 32, (xcd, len(rows), len(cols))
+
+
+def test_tile_order_rejects_bad_arguments(lib):
+    with pytest.raises(lib.GemmError):
+        lib.gemm_tile_order(0, 4, 8)
+    with pytest.raises(lib.GemmError):
+        lib.gemm_tile_order(4, 4, 0)

@@ -1,0 +1,268 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Bar: |D - D_ref| <= 2e-3*(|alpha|*(|A|@|B|) + |beta*C|) + 1e-6 elementwise;
+bitwise equality where the exact result is representable and every partial
+sum is exact (integer, identity and permutation inputs).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import D_SENTINEL, need_gpu, run, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+C = workloads.CONFIGS
+
+
+@pytest.fixture(autouse=True)
+def _gpu(monkeypatch):
+    need_gpu()
+    monkeypatch.delenv("GEMM_FORCE_PATH", raising=False)
+    monkeypatch.delenv("GEMM_FORCE_TILE", raising=False)
+
+
+def _dt(cfg):
+    return workloads.DTYPE_CODE[cfg.dtype]
+
+
+# ----------------------------------------------- the five workloads ---------
+
+@pytest.mark.parametrize("name", ["atom16x8x16", "gemm512", "ragged4097x1000x1032_tn"])
+def test_workload_parity_full(name):
+    r = run(C[name])
+    r.check()
+    r.check_padding_untouched()
+    if name == "ragged4097x1000x1032_tn":
+        assert r.path.startswith("fma ") and "A row pitch 8194 B" in r.path, r.path
+    else:
+        assert r.path.startswith("mfma "), r.path
+
+
+@pytest.mark.parametrize("name", ["gemm4096_inplace", "gemm8192_nt"])
+def test_workload_parity_full_size_sampled(name):
+    """Full size in the launch configuration the benchmark times; the oracle
+    checks rows that touch every 256-row tile band (all columns)."""
+    cfg = C[name]
+    r = run(cfg)
+    assert r.path.startswith("mfma t256x256x64"), r.path
+    r.check(rows=sample_rows(cfg.M, 256, 1))
+    assert np.all(np.isfinite(r.D.numpy()))
+
+
+def test_ragged_workload_on_mfma_with_aligned_pitch():
+    """Same ragged shape with A's rows padded to a 16-byte pitch: the masked
+    matrix-core path must agree with the oracle too."""
+    cfg = workloads.with_shape(C["ragged4097x1000x1032_tn"], lda=4104)
+    r = run(cfg)
+    assert r.path.startswith("mfma ") and r.path.endswith("masked"), r.path
+    r.check()
+
+
+@pytest.mark.parametrize("name", ["atom16x8x16", "gemm512", "ragged4097x1000x1032_tn"])
+def test_workload_parity_forced_fma(name, monkeypatch):
+    monkeypatch.setenv("GEMM_FORCE_PATH", "fma")
+    r = run(C[name])
+    assert r.path.startswith("fma "), r.path
+    r.check()
+
+
+def test_inplace_workload_forced_fma_sampled(monkeypatch):
+    monkeypatch.setenv("GEMM_FORCE_PATH", "fma")
+    cfg = C["gemm4096_inplace"]
+    r = run(cfg)
+    r.check(rows=sample_rows(cfg.M, 512, 1))
+
+
+# ---------------------------------------------- tiled shape sweep -----------
+
+SHAPES = [(16, 8, 16), (1, 1, 1), (32, 32, 16), (48, 40, 24), (64, 64, 64), (100, 130, 70),
+          (257, 129, 200), (128, 256, 96), (300, 17, 33), (5, 300, 8), (513, 65, 130),
+          (256, 256, 256), (96, 160, 1000)]
+TILES = ["t16x16x64", "t64x64x64", "t128x128x64", "t256x256x64"]
+
+
+def _pad8(x):
+    return (x + 7) // 8 * 8
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_tiled_shapes(tile, dtype, monkeypatch):
+    monkeypatch.setenv("GEMM_FORCE_TILE", tile)
+    seed = 2000
+    for (M, N, K) in SHAPES:
+        for tA, tB in [(0, 0), (0, 1), (1, 0), (1, 1)]:
+            for alpha, beta in [(1.0, 0.0), (1.0, 1.0), (1.5, 0.5)]:
+                seed += 1
+                # padded leading dims keep rows 16-byte aligned (matrix-core path)
+                lda = _pad8(M if tA else K) + (8 if seed % 3 == 0 else 0)
+                ldb = _pad8(K if tB else N)
+                ldd = N + (seed % 5)
+                cfg = workloads.Config(f"sweep{seed}", M, N, K, dtype, tA, tB, alpha, beta,
+                                       "uniform", seed, lda=lda, ldb=ldb, ldc=ldd, ldd=ldd)
+                r = run(cfg)
+                assert r.path.startswith("mfma " + tile), r.path
+                r.check()
+                r.check_padding_untouched()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_tiled_shapes_fma(dtype, monkeypatch):
+    monkeypatch.setenv("GEMM_FORCE_PATH", "fma")
+    seed = 3000
+    for (M, N, K) in SHAPES:
+        for tA, tB in [(0, 0), (0, 1), (1, 0), (1, 1)]:
+            seed += 1
+            cfg = workloads.Config(f"fsweep{seed}", M, N, K, dtype, tA, tB, 2.0, -1.0,
+                                   "uniform", seed,
+                                   lda=(M if tA else K) + seed % 3, ldb=(K if tB else N) + 1)
+            r = run(cfg)
+            assert r.path.startswith("fma "), r.path
+            r.check()
+
+
+# ---------------------------------------------------- exact cases -----------
+
+def _exact_case(dtype, tA, tB, M, N, K, A, B, path):
+    """Run with the given op(A) [M,K] and op(B) [K,N] float matrices whose
+    products and partial sums are exact; require bitwise equality."""
+    As = A.T if tA else A
+    Bs = B.T if tB else B
+    cfg = workloads.Config(f"exact-{dtype}-{tA}{tB}", M, N, K, dtype, tA, tB, 1.0, 0.0,
+                           "uniform", 1, lda=As.shape[1], ldb=Bs.shape[1])
+    inp = workloads.make_inputs(cfg, A_src=torch.tensor(As, dtype=torch.float32),
+                                B_src=torch.tensor(Bs, dtype=torch.float32))
+    r = run(cfg, inp)
+    assert r.path.startswith(path), r.path
+    D_ref, _ = r.reference()
+    got = r.D[:, :N].numpy()
+    assert np.array_equal(got, D_ref.astype(np.float32)), \
+        np.argwhere(got != D_ref.astype(np.float32))[:5]
+
+
+PATHS = ["mfma", "fma"]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_exact_integer_inputs(path, dtype, tA, tB, monkeypatch):
+    monkeypatch.setenv("GEMM_FORCE_PATH", path)
+    rng = np.random.default_rng(7 + tA + 2 * tB)
+    M, N, K = 264, 272, 520
+    A = rng.integers(-2, 3, (M, K)).astype(np.float32)
+    B = rng.integers(-2, 3, (K, N)).astype(np.float32)
+    _exact_case(dtype, tA, tB, M, N, K, A, B, path)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_exact_permutations_pin_lane_ownership(path, tA, tB, monkeypatch):
+    """P @ X and X @ Q move every element to a known place exactly, so any
+    wrong lane/row/column ownership in a fragment or accumulator shows up."""
+    monkeypatch.setenv("GEMM_FORCE_PATH", path)
+    rng = np.random.default_rng(11 + tA + 2 * tB)
+    for tile in (["t256x256x64", "t64x64x64", "t16x16x64"] if path == "mfma" else [None]):
+        if tile:
+            monkeypatch.setenv("GEMM_FORCE_TILE", tile)
+        M = K = N = 256
+        X = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+        X = torch.tensor(X).bfloat16().float().numpy()  # values exact in bf16
+        P = np.eye(M, dtype=np.float32)[rng.permutation(M)]
+        Q = np.eye(N, dtype=np.float32)[:, rng.permutation(N)]
+        _exact_case("bf16", tA, tB, M, N, K, P, X, path)
+        _exact_case("bf16", tA, tB, M, N, K, X, Q, path)
+        I = np.eye(K, dtype=np.float32)
+        _exact_case("bf16", tA, tB, M, N, K, X, I, path)
+
+
+def test_exact_ones_closed_form():
+    M, N, K = 300, 200, 2048
+    cfg = workloads.Config("ones", M, N, K, "bf16", 0, 1, 1.0, 0.0, "uniform", 1)
+    inp = workloads.make_inputs(cfg, A_src=torch.ones(M, K), B_src=torch.ones(N, K))
+    r = run(cfg, inp)
+    assert np.all(r.D.numpy() == float(K))
+
+
+# ----------------------------------------------- epilogue and aliasing ------
+
+def test_inplace_equals_separate_buffers_bitwise():
+    base = workloads.Config("ip", 512, 384, 320, "bf16", 0, 0, 1.0, 1.0, "normal", 77)
+    inp = workloads.make_inputs(base)
+    sep = run(base, inp)
+    ip = run(workloads.with_shape(base, inplace=True), inp)
+    assert torch.equal(sep.D[:, :384], ip.D[:, :384])
+    sep.check()
+
+
+def test_epilogue_forms_are_consistent_bitwise():
+    """alpha=1,beta=1 equals (alpha=1,beta=0) + C in float32; alpha=2 equals 2x."""
+    base = workloads.Config("epi", 320, 288, 192, "f16", 1, 0, 1.0, 0.0, "uniform", 78,
+                            lda=320)
+    inp = workloads.make_inputs(base, want_c=True)
+    d0 = run(base, inp).D
+    d1 = run(workloads.with_shape(base, beta=1.0), inp).D
+    assert torch.equal(d1, d0 + inp.C)
+    d2 = run(workloads.with_shape(base, alpha=2.0), inp).D
+    assert torch.equal(d2, 2.0 * d0)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_beta_zero_never_reads_c(path, monkeypatch):
+    monkeypatch.setenv("GEMM_FORCE_PATH", path)
+    cfg = workloads.Config("nanc", 200, 136, 96, "bf16", 0, 0, 1.0, 0.0, "uniform", 79)
+    inp = workloads.make_inputs(cfg, C=torch.full((200, 136), float("nan")))
+    r = run(cfg, inp)  # a NaN-filled C is passed, and must not be read
+    assert np.all(np.isfinite(r.D.numpy()))
+    r.check()
+
+
+def test_k_zero_and_alpha_zero():
+    import dense_gemm_tile_amd as dgt
+    dev = torch.device("cuda:0")
+    M, N = 70, 90
+    Cm = torch.rand(M, N, device=dev) * 2 - 1
+    D = torch.full((M, N), 5.0, device=dev)
+    say("K=0 beta=-0.5")
+    dgt.gemm(M, N, 0, "f16", 0, 0, 1.0, -0.5, None, 1, None, N, Cm, N, D, N,
+             stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(D, -0.5 * Cm)
+    say("alpha=0 beta=0")
+    A = torch.full((M, 8), float("nan"), device=dev, dtype=torch.float16)
+    B = torch.full((8, N), float("nan"), device=dev, dtype=torch.float16)
+    dgt.gemm(M, N, 8, "f16", 0, 0, 0.0, 0.0, A, 8, B, N, None, N, D, N,
+             stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(D, torch.zeros_like(D))
+
+
+def test_errors_launch_nothing():
+    import dense_gemm_tile_amd as dgt
+    dev = torch.device("cuda:0")
+    D = torch.full((8, 8), 3.0, device=dev)
+    A = torch.ones(8, 8, device=dev, dtype=torch.float16)
+    st = dgt.gemm_status(8, 8, 8, 0, 0, 0, 1.0, 0.0, A, 8, A, 8, None, 8, D, 4,
+                         stream=torch.cuda.current_stream())
+    assert st == dgt.GEMM_ERR_INVALID_ARG
+    st = dgt.gemm_status(8, 8, 8, 0, 0, 0, 1.0, 0.0, A, 8, D, 8, None, 8, D, 8,
+                         stream=torch.cuda.current_stream())
+    assert st == dgt.GEMM_ERR_ALIAS
+    torch.cuda.synchronize()
+    assert torch.equal(D, torch.full((8, 8), 3.0, device=dev))
+
+
+def test_deterministic_repeat_and_side_stream():
+    cfg = workloads.Config("det", 1024, 768, 1536, "bf16", 0, 1, 1.0, 0.0, "normal", 80)
+    inp = workloads.make_inputs(cfg)
+    a = run(cfg, inp).D
+    b = run(cfg, inp).D
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c = run(cfg, inp, stream=s).D
+    assert torch.equal(a, b) and torch.equal(a, c)
