@@ -93,13 +93,18 @@ def cpu_baseline(cfg, inp, seconds: float):
                               cfg.beta, A, lda, B, ldb, C, ldc, rows=rows, with_bound=False)
         return time.perf_counter() - t0
 
-    rows = min(cfg.M, 64)
-    t = timed(rows)
-    # grow the sample so the measured call takes about `seconds`
-    if t < seconds / 4 and rows < cfg.M:
-        rows = int(min(cfg.M, max(rows, rows * (seconds / max(t, 1e-3)) * 0.8)))
-        rows = max(64, rows // 64 * 64)
-        t = timed(rows)
+    # Two short probes give a fixed cost (operand decode) and a per-row cost;
+    # the measured call is then sized to take about `seconds`.
+    r0, r1 = min(cfg.M, 64), min(cfg.M, 256)
+    t0 = timed(r0)
+    rows, t = r0, t0
+    if r1 > r0:
+        t1 = timed(r1)
+        per_row = max((t1 - t0) / (r1 - r0), 1e-6)
+        fixed = max(t0 - r0 * per_row, 0.0)
+        rows = int(min(cfg.M, max(r1, (seconds - fixed) / per_row)))
+        rows = max(r1, rows // 64 * 64) if rows < cfg.M else cfg.M
+        t = timed(rows) if rows != r1 else t1
     flops = 2.0 * rows * cfg.N * cfg.K
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
             "kind": "oracle",

@@ -16,6 +16,8 @@ struct GemmArgs {
   int M, N, K;
   float alpha, beta;
   int epi;       // Epilogue kind, see below
+  int wide_epi;  // 1: D (and C when read) allow 16-byte accesses (base and
+                 //    leading dimension multiples of 16 bytes)
   int tiles_m;   // output tiles along M / N for the tile scheduler
   int tiles_n;
   int group_m;   // tile-row group height of the grouped order

@@ -12,7 +12,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/dense_gemm_tile.h"
+#include "dense_gemm_tile.h"
 #include "common.h"
 
 namespace dgt {
@@ -169,6 +169,10 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   a.alpha = alpha;
   a.beta = beta;
   a.group_m = 8;
+  a.wide_epi = ((uintptr_t)D % 16 == 0 && ldd % 4 == 0 &&
+                (!reads_c || ((uintptr_t)C % 16 == 0 && ldc % 4 == 0)))
+                   ? 1
+                   : 0;
   plan.epi = !reads_c ? EPI_BETA0 : (alpha == 1.0f && beta == 1.0f ? EPI_ACC_PLUS_C : EPI_GENERAL);
   a.epi = plan.epi;
   const char* epi_name = plan.epi == EPI_BETA0 ? "beta0" : plan.epi == EPI_ACC_PLUS_C ? "acc+c" : "general";
@@ -219,13 +223,25 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   plan.mfma = true;
   plan.tile = tile;
   plan.masked = (M % ti.bm) || (N % ti.bn) || (K % ti.bk);
+  // The unmasked kernels address an operand box through a buffer resource
+  // with 32-bit byte offsets spanning up to max(bm, bn, bk) rows of the
+  // operand; larger pitches take the masked kernels' 64-bit addressing.
+  {
+    const int64_t rows = ti.bm > ti.bn ? (ti.bm > ti.bk ? ti.bm : ti.bk)
+                                       : (ti.bn > ti.bk ? ti.bn : ti.bk);
+    const int64_t ldmax = lda > ldb ? lda : ldb;
+    if (ldmax * 2 * rows + 4096 >= (int64_t{1} << 31)) plan.masked = true;
+  }
   a.tiles_m = (int)((M + ti.bm - 1) / ti.bm);
   a.tiles_n = (int)((N + ti.bn - 1) / ti.bn);
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7fffffff)
     return fail(GEMM_ERR_UNSUPPORTED, "too many output tiles for one launch");
-  std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s", ti.name, ti.waves_m,
-                ti.waves_n, ti.atom_m, ti.atom_n, ti.atom_k, ops, epi_name,
-                plan.masked ? " masked" : "");
+  // Whole 256x256 tiles with both operands K-contiguous stage through LDS by
+  // direct loads (32-deep K slices, five stages).
+  const bool lds_dma = tile == TILE_256x256 && !transA && transB && !plan.masked;
+  std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s", ti.name,
+                ti.waves_m, ti.waves_n, ti.atom_m, ti.atom_n, ti.atom_k, ops, epi_name,
+                lds_dma ? " lds-dma" : "", plan.masked ? " masked" : "");
   g_path = buf;
   return GEMM_OK;
 }

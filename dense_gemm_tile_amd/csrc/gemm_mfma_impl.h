@@ -9,8 +9,10 @@
 // kernel pair and its `@pipeline` staging) -- laid out for CDNA4:
 //
 //  * one workgroup per output tile, chosen by an XCD-aware grouped scheduler;
-//  * global -> VGPR -> LDS staging with 128-bit loads, two LDS stages over K
-//    (load stage k+1 while computing stage k, one barrier per K step);
+//  * global -> VGPR -> LDS staging with 128-bit loads (buffer loads with a
+//    scalar base per K step on unmasked tiles), two LDS stages over K, global
+//    loads issued two K steps ahead, fragments read one K sub-step ahead, one
+//    barrier per K step;
 //  * LDS rows hold 64 K-values (128 bytes, eight 16-byte chunks) of one M (or
 //    N) index; chunk c of row r lives at chunk position c ^ ((r ^ (r>>3)) & 7),
 //    an XOR swizzle instead of row padding (the sm_80 Phobos variant keeps its
@@ -108,11 +110,19 @@ __device__ static inline int lds_off(int row, int chunk) {
 }
 
 // --------------------------------------------------------------- staging ----
+// A buffer resource over `base` (bytes), used by the unmasked loaders: the
+// per-lane byte offset stays in one VGPR and the per-piece step is a scalar.
+__device__ static inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF,
+                                           0x00020000);
+}
+
 // One operand's R x 64 box (R rows of M or N, 64 K-values) per K step.
 // KCONTIG: element (r, k) is X[(r0 + r) * ld + k0 + k]  (A with transA = 0,
 //          B with transB = 1); otherwise X[(k0 + k) * ld + r0 + r].
-// Each thread moves NL 16-byte pieces: for KCONTIG, NL chunks of 8 K-values;
-// otherwise one block of NL K-rows x 8 row-values, transposed in registers.
+// Each thread moves NL 16-byte pieces: for KCONTIG, NL chunks of 8 K-values
+// (piece i covers box row (tid >> 3) + i * THREADS / 8); otherwise one block of
+// NL K-rows x 8 row-values, transposed in registers on the way to LDS.
 template <int R, int THREADS, bool KCONTIG, bool MASK>
 struct Stager {
   static constexpr int NL = R * 64 / (8 * THREADS);
@@ -132,19 +142,35 @@ struct Stager {
     return r;
   }
 
-  // rlim / klim: number of valid rows / K-values of the whole operand.
+  // Issue the global loads of the box at (r0, k0). rlim / klim: number of
+  // valid rows / K-values of the whole operand (used only when MASK).
   __device__ inline void load(const uint16_t* __restrict__ X, int64_t ld, int r0, int rlim,
                               int k0, int klim, int tid) {
-    if constexpr (KCONTIG) {
+    if constexpr (!MASK) {
+      if constexpr (KCONTIG) {
+        const auto rs = make_rsrc(X + (int64_t)r0 * ld + k0);
+        const int voff = (int)(((tid >> 3) * ld + ((tid & 7) << 3)) * 2);
+        const int step = (int)((THREADS / 8) * ld * 2);
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+          v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, i * step, 0);
+      } else {
+        const int rc = tid % (R / 8), kb = tid / (R / 8);
+        const auto rs = make_rsrc(X + (int64_t)k0 * ld + r0);
+        const int voff = (int)(((kb * NL) * ld + rc * 8) * 2);
+        const int step = (int)(ld * 2);
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+          v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * step, 0);
+      }
+    } else if constexpr (KCONTIG) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int id = tid + i * THREADS;
         const int r = r0 + (id >> 3);
         const int k = k0 + ((id & 7) << 3);
         const uint16_t* p = X + (int64_t)r * ld + k;
-        if (!MASK) {
-          v[i] = *reinterpret_cast<const u32x4*>(p);
-        } else if (r < rlim && k + 8 <= klim) {
+        if (r < rlim && k + 8 <= klim) {
           v[i] = *reinterpret_cast<const u32x4*>(p);
         } else if (r < rlim && k < klim) {
           v[i] = load_partial(p, klim - k);
@@ -160,9 +186,7 @@ struct Stager {
       for (int j = 0; j < NL; ++j) {
         const int k = k0 + kb * NL + j;
         const uint16_t* p = X + (int64_t)k * ld + r;
-        if (!MASK) {
-          v[j] = *reinterpret_cast<const u32x4*>(p);
-        } else if (k < klim && r + 8 <= rlim) {
+        if (k < klim && r + 8 <= rlim) {
           v[j] = *reinterpret_cast<const u32x4*>(p);
         } else if (k < klim && r < rlim) {
           v[j] = load_partial(p, rlim - r);
@@ -214,8 +238,129 @@ struct Stager {
   }
 };
 
+// One K-step's worth of operand fragments for a wave: TM A atoms, TN B atoms.
+template <class Cfg>
+struct Frags {
+  u32x4 a[Cfg::TM], b[Cfg::TN];
+};
+
+template <class Cfg>
+__device__ inline void read_frags(Frags<Cfg>& f, const char* As, const char* Bs, int a_row0,
+                                  int b_row0, int chunk) {
+  using At = typename Cfg::At;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+    f.a[i] = *reinterpret_cast<const u32x4*>(As + lds_off(a_row0 + i * At::M, chunk));
+#pragma unroll
+  for (int j = 0; j < Cfg::TN; ++j)
+    f.b[j] = *reinterpret_cast<const u32x4*>(Bs + lds_off(b_row0 + j * At::N, chunk));
+}
+
+template <class Cfg, class Tag>
+__device__ inline void mma_step(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::TN],
+                                const Frags<Cfg>& f) {
+  using At = typename Cfg::At;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j) acc[i][j] = At::mma(Tag{}, f.a[i], f.b[j], acc[i][j]);
+}
+
+// -------------------------------------------------------------- epilogue ----
+// Transpose a 4x4 block held by a quad of lanes (lane k of the quad holds
+// x[0..3]) so that lane k ends up with element k of every lane's x: two
+// exchange rounds over quad_perm DPP moves (lane ^ 2, then lane ^ 1).
+__device__ inline void quad_transpose(float (&x)[4], int lane) {
+  const int k = lane & 3;
+  float t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float o = __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x[i ^ 2]), 0x4E, 0xF, 0xF, false));
+    t[i] = (((k >> 1) ^ (i >> 1)) & 1) ? o : x[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float o = __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, t[i ^ 1]), 0xB1, 0xF, 0xF, false));
+    x[i] = ((k ^ i) & 1) ? o : t[i];
+  }
+}
+
+template <int EPI>
+__device__ inline float epi_one(float x, float c, float alpha, float beta) {
+  if constexpr (EPI == EPI_BETA0) return alpha * x;
+  else if constexpr (EPI == EPI_ACC_PLUS_C) return x + c;
+  else return __builtin_fmaf(beta, c, alpha * x);
+}
+
+// D = alpha*acc + beta*C for one wave's sub-tile whose top-left output element
+// is (r0, c0); C is read only for the epilogue kinds that need it.
+//
+// Each accumulator register group holds 4 consecutive rows of one column per
+// lane. On whole tiles with 16-byte aligned D (and C), a quad transpose turns
+// that into 4 consecutive columns of one row per lane, so C is read and D is
+// written with 16-byte accesses; otherwise elements are written one by one
+// with bounds checks.
+template <class Cfg, int EPI, bool MASK>
+__device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::TN],
+                                  const GemmArgs& p, int r0, int c0, int lane) {
+  using At = typename Cfg::At;
+  const float alpha = p.alpha, beta = p.beta;
+  const int col_l = At::acc_col(lane);
+  if (!MASK && p.wide_epi) {
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j) {
+        const int c = c0 + j * At::N + (col_l & ~3);
+#pragma unroll
+        for (int g = 0; g < At::NACC / 4; ++g) {
+          float x[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                        acc[i][j][4 * g + 3]};
+          quad_transpose(x, lane);
+          const int r = r0 + i * At::M + At::acc_row(lane, 4 * g) + (lane & 3);
+          f32x4 cv = {0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (EPI != EPI_BETA0)
+            cv = *reinterpret_cast<const f32x4*>(p.C + (int64_t)r * p.ldc + c);
+          f32x4 o;
+          o[0] = epi_one<EPI>(x[0], cv[0], alpha, beta);
+          o[1] = epi_one<EPI>(x[1], cv[1], alpha, beta);
+          o[2] = epi_one<EPI>(x[2], cv[2], alpha, beta);
+          o[3] = epi_one<EPI>(x[3], cv[3], alpha, beta);
+          *reinterpret_cast<f32x4*>(p.D + (int64_t)r * p.ldd + c) = o;
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j) {
+      const int c = c0 + j * At::N + col_l;
+#pragma unroll
+      for (int v = 0; v < At::NACC; ++v) {
+        const int r = r0 + i * At::M + At::acc_row(lane, v);
+        if (MASK && (r >= p.M || c >= p.N)) continue;
+        float cv = 0.0f;
+        if constexpr (EPI != EPI_BETA0) cv = p.C[(int64_t)r * p.ldc + c];
+        p.D[(int64_t)r * p.ldd + c] = epi_one<EPI>(acc[i][j][v], cv, alpha, beta);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- kernel ----
-template <class Cfg, class Tag, bool TA, bool TB, bool MASK>
+// Pipeline per K step kt (LDS buffer b = kt & 1, the other buffer nb):
+//   K sub-steps 0..KSTEPS-2: read the fragments of sub-step s+1 from b while
+//     the MFMAs of sub-step s run;
+//   then (all reads of b are in registers) write the staged box of step kt+1
+//     into nb, barrier, issue the global loads of step kt+2, read the first
+//     fragments of step kt+1 from nb, and only then run the MFMAs of the last
+//     sub-step of kt, which hide that LDS latency.
+// Global loads therefore have almost two K steps of MFMA work to land.
+template <class Cfg, class Tag, bool TA, bool TB, bool MASK, int EPI>
 __global__ void __launch_bounds__(Cfg::THREADS)
 gemm_mfma_kernel(const GemmArgs p) {
   using At = typename Cfg::At;
@@ -249,101 +394,86 @@ gemm_mfma_kernel(const GemmArgs p) {
       for (int v = 0; v < At::NACC; ++v) acc[i][j][v] = 0.0f;
 
   const int KT = (p.K + Cfg::BK - 1) / Cfg::BK;
+  const int a_row0 = wm * Cfg::WTM + At::frag_row(lane);
+  const int b_row0 = wn * Cfg::WTN + At::frag_row(lane);
+  const int koct = At::frag_koct(lane);
+  constexpr int CPS = At::K / 8;  // 16-byte chunks per K sub-step
 
+  // Prologue: step 0 into buffer 0, step 1 into registers, first fragments.
   sa.load(Ap, p.lda, m0, p.M, 0, p.K, tid);
   sb.load(Bp, p.ldb, n0, p.N, 0, p.K, tid);
   sa.store(smem, tid);
   sb.store(smem + Cfg::A_BYTES, tid);
   __syncthreads();
-
-  // Fragment row offsets (bytes are computed per K step from these).
-  const int a_row0 = wm * Cfg::WTM + At::frag_row(lane);
-  const int b_row0 = wn * Cfg::WTN + At::frag_row(lane);
-  const int koct = At::frag_koct(lane);
+  if (KT > 1) {
+    sa.load(Ap, p.lda, m0, p.M, Cfg::BK, p.K, tid);
+    sb.load(Bp, p.ldb, n0, p.N, Cfg::BK, p.K, tid);
+  }
+  Frags<Cfg> cur, nxt;
+  read_frags<Cfg>(cur, smem, smem + Cfg::A_BYTES, a_row0, b_row0, koct);
 
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      const int k0 = (kt + 1) * Cfg::BK;
-      sa.load(Ap, p.lda, m0, p.M, k0, p.K, tid);
-      sb.load(Bp, p.ldb, n0, p.N, k0, p.K, tid);
-    }
-    const char* As = smem + cur * Cfg::STAGE_BYTES;
+    const char* As = smem + (kt & 1) * Cfg::STAGE_BYTES;
     const char* Bs = As + Cfg::A_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < Cfg::KSTEPS; ++ks) {
-      const int chunk = ks * (At::K / 8) + koct;
-      u32x4 a[Cfg::TM], b[Cfg::TN];
-#pragma unroll
-      for (int i = 0; i < Cfg::TM; ++i)
-        a[i] = *reinterpret_cast<const u32x4*>(As + lds_off(a_row0 + i * At::M, chunk));
-#pragma unroll
-      for (int j = 0; j < Cfg::TN; ++j)
-        b[j] = *reinterpret_cast<const u32x4*>(Bs + lds_off(b_row0 + j * At::N, chunk));
-#pragma unroll
-      for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::TN; ++j) acc[i][j] = At::mma(Tag{}, a[i], b[j], acc[i][j]);
+    for (int ks = 0; ks < Cfg::KSTEPS - 1; ++ks) {
+      read_frags<Cfg>(nxt, As, Bs, a_row0, b_row0, (ks + 1) * CPS + koct);
+      mma_step<Cfg, Tag>(acc, cur);
+      cur = nxt;
     }
-    if (more) {
-      char* nxt = smem + (cur ^ 1) * Cfg::STAGE_BYTES;
-      sa.store(nxt, tid);
-      sb.store(nxt + Cfg::A_BYTES, tid);
+    if (kt + 1 < KT) {
+      char* nA = smem + ((kt + 1) & 1) * Cfg::STAGE_BYTES;
+      sa.store(nA, tid);
+      sb.store(nA + Cfg::A_BYTES, tid);
+      __syncthreads();
+      if (kt + 2 < KT) {
+        const int k0 = (kt + 2) * Cfg::BK;
+        sa.load(Ap, p.lda, m0, p.M, k0, p.K, tid);
+        sb.load(Bp, p.ldb, n0, p.N, k0, p.K, tid);
+      }
+      read_frags<Cfg>(nxt, nA, nA + Cfg::A_BYTES, a_row0, b_row0, koct);
     }
-    __syncthreads();
+    mma_step<Cfg, Tag>(acc, cur);
+    cur = nxt;
   }
 
-  // Epilogue: D = alpha*acc + beta*C, once per output element.
-  const float alpha = p.alpha, beta = p.beta;
-  const int col_l = At::acc_col(lane);
-#pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i) {
-#pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j) {
-      const int cbase = n0 + wn * Cfg::WTN + j * At::N + col_l;
-#pragma unroll
-      for (int v = 0; v < At::NACC; ++v) {
-        const int r = m0 + wm * Cfg::WTM + i * At::M + At::acc_row(lane, v);
-        const int c = cbase;
-        if (MASK && (r >= p.M || c >= p.N)) continue;
-        const float x = acc[i][j][v];
-        float* dp = p.D + (int64_t)r * p.ldd + c;
-        if (p.epi == EPI_BETA0) {
-          *dp = alpha * x;
-        } else {
-          const float cv = p.C[(int64_t)r * p.ldc + c];
-          *dp = (p.epi == EPI_ACC_PLUS_C) ? (x + cv) : __builtin_fmaf(beta, cv, alpha * x);
-        }
-      }
-    }
+  store_tile<Cfg, EPI, MASK>(acc, p, m0 + wm * Cfg::WTM, n0 + wn * Cfg::WTN, lane);
+}
+
+template <class Cfg, class Tag, bool TA, bool TB, bool MASK>
+hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid(a.tiles_m * a.tiles_n), block(Cfg::THREADS);
+  switch (a.epi) {
+    case EPI_BETA0:
+      gemm_mfma_kernel<Cfg, Tag, TA, TB, MASK, EPI_BETA0><<<grid, block, 0, s>>>(a);
+      break;
+    case EPI_ACC_PLUS_C:
+      gemm_mfma_kernel<Cfg, Tag, TA, TB, MASK, EPI_ACC_PLUS_C><<<grid, block, 0, s>>>(a);
+      break;
+    default:
+      gemm_mfma_kernel<Cfg, Tag, TA, TB, MASK, EPI_GENERAL><<<grid, block, 0, s>>>(a);
+      break;
   }
+  return hipGetLastError();
 }
 
 template <class Cfg>
 hipError_t launch_mfma_cfg(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a,
                            hipStream_t s) {
-  const dim3 grid(a.tiles_m * a.tiles_n), block(Cfg::THREADS);
-#define DGT_LAUNCH(TAG, TA_, TB_, MASK_) \
-  gemm_mfma_kernel<Cfg, TAG, TA_, TB_, MASK_><<<grid, block, 0, s>>>(a)
-#define DGT_LAUNCH_MASK(TAG, TA_, TB_)                 \
-  do {                                                 \
-    if (masked) DGT_LAUNCH(TAG, TA_, TB_, true);       \
-    else DGT_LAUNCH(TAG, TA_, TB_, false);             \
-  } while (0)
-#define DGT_LAUNCH_T(TAG)                                  \
-  do {                                                     \
-    if (!ta && !tb) DGT_LAUNCH_MASK(TAG, false, false);    \
-    else if (!ta && tb) DGT_LAUNCH_MASK(TAG, false, true); \
-    else if (ta && !tb) DGT_LAUNCH_MASK(TAG, true, false); \
-    else DGT_LAUNCH_MASK(TAG, true, true);                 \
+#define DGT_LAUNCH_MASK(TAG, TA_, TB_)                               \
+  return masked ? launch_epi<Cfg, TAG, TA_, TB_, true>(a, s)         \
+                : launch_epi<Cfg, TAG, TA_, TB_, false>(a, s)
+#define DGT_LAUNCH_T(TAG)                          \
+  do {                                             \
+    if (!ta && !tb) DGT_LAUNCH_MASK(TAG, false, false); \
+    if (!ta && tb) DGT_LAUNCH_MASK(TAG, false, true);   \
+    if (ta && !tb) DGT_LAUNCH_MASK(TAG, true, false);   \
+    DGT_LAUNCH_MASK(TAG, true, true);                   \
   } while (0)
   if (dtype == 0) DGT_LAUNCH_T(TagF16);
-  else DGT_LAUNCH_T(TagBF16);
+  DGT_LAUNCH_T(TagBF16);
 #undef DGT_LAUNCH_T
 #undef DGT_LAUNCH_MASK
-#undef DGT_LAUNCH
-  return hipGetLastError();
 }
 
 using Cfg256 = TileCfg<256, 256, 2, 2, 32>;

@@ -134,9 +134,17 @@ def test_ragged_dims_stay_on_mfma_masked(lib):
     assert lib.gemm_last_path().startswith("mfma t16x16x64"), lib.gemm_last_path()
 
 
+def test_huge_pitch_takes_64bit_addressing(lib):
+    # 64 rows (the 64x64 tile) of a 16M-element pitch overflow 32-bit offsets
+    assert _v(lib, M=256, N=256, K=256, lda=1 << 24, A=1 << 40) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith("masked"), lib.gemm_last_path()
+    assert _v(lib, M=256, N=256, K=256, lda=1 << 20) == lib.GEMM_OK
+    assert not lib.gemm_last_path().endswith("masked")
+
+
 def test_tile_and_epilogue_choice(lib):
     assert _v(lib, M=8192, N=8192, K=8192, tB=1, dtype=1) == lib.GEMM_OK
-    assert lib.gemm_last_path() == "mfma t256x256x64 w2x2 a32x32x16 NT epi=beta0"
+    assert lib.gemm_last_path() == "mfma t256x256x64 w2x2 a32x32x16 NT epi=beta0 lds-dma"
     assert _v(lib, M=4096, N=4096, K=4096, dtype=1, beta=1.0, C=D0) == lib.GEMM_OK
     assert lib.gemm_last_path() == "mfma t256x256x64 w2x2 a32x32x16 NN epi=acc+c"
     assert _v(lib, M=512, N=512, K=512, alpha=1.5, beta=0.5) == lib.GEMM_OK

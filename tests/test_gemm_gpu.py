@@ -266,3 +266,47 @@ def test_deterministic_repeat_and_side_stream():
     with torch.cuda.stream(s):
         c = run(cfg, inp, stream=s).D
     assert torch.equal(a, b) and torch.equal(a, c)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_lds_dma_path_pipeline_depths(dtype, monkeypatch):
+    """Whole 256x256 NT tiles stage through LDS by direct loads; K from one to
+    several pipeline turns (prologue-only, tail-only and steady-state stages)."""
+    monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
+    seed = 4000
+    for K in (64, 128, 192, 256, 320, 448, 1024):
+        for alpha, beta in [(1.0, 0.0), (1.0, 1.0), (-0.5, 2.0)]:
+            seed += 1
+            cfg = workloads.Config(f"dma{seed}", 512, 768, K, dtype, 0, 1, alpha, beta,
+                                   "uniform", seed, ldd=768 + 4, ldc=768 + 4)
+            r = run(cfg)
+            assert "lds-dma" in r.path, r.path
+            r.check()
+            r.check_padding_untouched()
+
+
+@pytest.mark.parametrize("layout", [(0, 1), (0, 0), (1, 1)])
+def test_wide_and_scalar_epilogues_agree(layout):
+    """Whole tiles store D with 16-byte accesses when D (and C) allow it and
+    element by element otherwise; both must match the oracle, and each other
+    bitwise (same accumulators, same epilogue arithmetic)."""
+    import dense_gemm_tile_amd as dgt
+    tA, tB = layout
+    M, N, K = 512, 512, 256
+    dev = torch.device("cuda:0")
+    base = workloads.Config("epiw", M, N, K, "bf16", tA, tB, 1.5, -0.5, "uniform", 90)
+    inp = workloads.make_inputs(base)
+    wide = run(base, inp)
+    # D one float past a 16-byte boundary, C with an odd leading dimension
+    lda, ldb, _, _ = base.lds()
+    A, B = inp.A.to(dev), inp.B.to(dev)
+    Cp = torch.zeros((M, N + 1), device=dev)
+    Cp[:, :N] = inp.C.to(dev)
+    Dbuf = torch.full((M * N + 1,), float("nan"), device=dev)
+    say(f"scalar epilogue {layout}")
+    dgt.gemm(M, N, K, "bf16", tA, tB, 1.5, -0.5, A, lda, B, ldb, Cp, N + 1,
+             Dbuf.data_ptr() + 4, N, stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    scalar = Dbuf[1:].reshape(M, N).cpu()
+    assert torch.equal(wide.D[:, :N], scalar)
+    wide.check()
