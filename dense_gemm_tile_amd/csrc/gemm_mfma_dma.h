@@ -108,6 +108,7 @@ gemm_mfma_dma_kernel(const GemmArgs p) {
 
   // Load instruction q (0..LOADS_PER_STAGE-1) of stage `stage` into buffer `buf`.
   auto issue_one = [&](int q, int stage, int buf) {
+    if (q < 0 || q >= C::LOADS_PER_STAGE) return;
     char* dst = smem + buf * C::STAGE_BYTES;
     const int koff = stage * C::BK * 2;
     if (q < C::LOADS_A)
@@ -183,24 +184,26 @@ gemm_mfma_dma_kernel(const GemmArgs p) {
     lds_barrier();
     const int nbuf = buf == C::STAGES - 1 ? 0 : buf + 1;
     const int lbuf = buf == 0 ? C::STAGES - 1 : buf - 1;  // == (kt + 4) % STAGES
-    // Sub-step 0 (fragments `cur`): the fragments of sub-step 1, then the
-    // stage's loads, one behind each MFMA. Sub-step 1 (`nxt`): the first
-    // fragments of the next stage. The order is pinned instruction by
-    // instruction so that the MFMA pipe always has the next MFMA queued.
+    // Issue order, pinned instruction by instruction so the MFMA pipe always
+    // has the next MFMA queued: in sub-step 0 (fragments `cur`) the even
+    // MFMA slots read the fragments of sub-step 1 and the odd ones issue half
+    // of the stage's loads; in sub-step 1 (`nxt`) the even slots read the
+    // first fragments of the next stage and the odd ones issue the other half.
 #pragma unroll
     for (int q = 0; q < C::TM * C::TN; ++q) {
       acc[q / C::TN][q % C::TN] =
           At::mma(Tag{}, cur.a[q / C::TN], cur.b[q % C::TN], acc[q / C::TN][q % C::TN]);
-      if (q < C::TM + C::TN) read_one(nxt, buf, 1, q);
-      else if (q - (C::TM + C::TN) < C::LOADS_PER_STAGE)
-        issue_one(q - (C::TM + C::TN), kt + 4, lbuf);
+      if ((q & 1) == 0) read_one(nxt, buf, 1, q >> 1);
+      else if ((q >> 1) < C::LOADS_PER_STAGE / 2) issue_one(q >> 1, kt + 4, lbuf);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int q = 0; q < C::TM * C::TN; ++q) {
       acc[q / C::TN][q % C::TN] =
           At::mma(Tag{}, nxt.a[q / C::TN], nxt.b[q % C::TN], acc[q / C::TN][q % C::TN]);
-      if (q < C::TM + C::TN) read_one(cur, nbuf, 0, q);
+      if ((q & 1) == 0) read_one(cur, nbuf, 0, q >> 1);
+      else if ((q >> 1) < C::LOADS_PER_STAGE / 2)
+        issue_one(C::LOADS_PER_STAGE / 2 + (q >> 1), kt + 4, lbuf);
       __builtin_amdgcn_sched_barrier(0);
     }
     buf = nbuf;
