@@ -328,7 +328,8 @@ __device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::T
           o[1] = epi_one<EPI>(x[1], cv[1], alpha, beta);
           o[2] = epi_one<EPI>(x[2], cv[2], alpha, beta);
           o[3] = epi_one<EPI>(x[3], cv[3], alpha, beta);
-          *reinterpret_cast<f32x4*>(p.D + (int64_t)r * p.ldd + c) = o;
+          // D is written once and not read back here: stream it past the caches.
+          __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(p.D + (int64_t)r * p.ldd + c));
         }
       }
     }
