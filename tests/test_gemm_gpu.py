@@ -269,18 +269,19 @@ def test_deterministic_repeat_and_side_stream():
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_lds_dma_path_pipeline_depths(dtype, monkeypatch):
-    """Whole 256x256 NT tiles stage through LDS by direct loads; K from one to
-    several pipeline turns (prologue-only, tail-only and steady-state stages)."""
+def test_pingpong_path_slice_counts(dtype, monkeypatch):
+    """Whole 256x256 NT tiles take the two-group kernel with direct loads; K
+    from one slice of 64 (prologue only) through two (no load in the loop)
+    to several turns of the five-slot ring."""
     monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
     seed = 4000
-    for K in (64, 128, 192, 256, 320, 448, 1024):
+    for K in (64, 128, 192, 256, 320, 384, 448, 640, 1024):
         for alpha, beta in [(1.0, 0.0), (1.0, 1.0), (-0.5, 2.0)]:
             seed += 1
             cfg = workloads.Config(f"dma{seed}", 512, 768, K, dtype, 0, 1, alpha, beta,
                                    "uniform", seed, ldd=768 + 4, ldc=768 + 4)
             r = run(cfg)
-            assert "lds-dma" in r.path, r.path
+            assert "pingpong" in r.path, r.path
             r.check()
             r.check_padding_untouched()
 
