@@ -30,6 +30,8 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}  # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0
 COPY_CAL_BYTES = 1 << 30
+DIST_TEXT = {"uniform": "uniform[-1, 1]", "normal": "normal(0, 1)",
+             "normal_invsqrtk": "normal(0, 1/sqrt(K))"}
 
 
 def kernel_sources_digest() -> str:
@@ -214,6 +216,15 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
     traffic = stored_traffic(cfg.name)
+    # Algorithmic bytes: A and B once (16-bit), C once when beta != 0, D once.
+    alg_bytes = 2.0 * (cfg.M * cfg.K + cfg.K * cfg.N) + 4.0 * cfg.M * cfg.N * (2 if cfg.beta != 0 else 1)
+    if flops / alg_bytes >= (peak * 1e12) / (PEAK_HBM_GBS * 1e9):
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tflops / peak, 4), "traffic": traffic}
+    else:
+        gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
     out = {
         "metric": "TFLOP/s (2MNK/t) bf16 M=N=K=8192 + % of MFMA peak; oracle max rel err",
         "value": round(tflops, 2),
@@ -226,7 +237,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
-        "data": "synthetic (seeded; A, B normal(0, 1/sqrt(K)) in bf16)",
+        "data": f"synthetic (seed {cfg.seed}; A, B {DIST_TEXT[cfg.dist]} in {cfg.dtype})",
         "config": {"workload": cfg.name, "M": cfg.M, "N": cfg.N, "K": cfg.K,
                    "transA": cfg.transA, "transB": cfg.transB, "alpha": cfg.alpha,
                    "beta": cfg.beta, "parallelism": "single GPU"},
@@ -234,9 +245,7 @@ def main():
         "oracle_max_rel_err": max_rel,
         "path": path,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                     "traffic": traffic},
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)

@@ -21,6 +21,8 @@ struct GemmArgs {
   int tiles_m;   // output tiles along M / N for the tile scheduler
   int tiles_n;
   int group_m;   // tile-row group height of the grouped order
+  int a_elem;    // 1: A's base or row pitch is not a multiple of 16 bytes, so the
+  int b_elem;    //    masked kernel stages it element by element (same for B)
 };
 
 // Epilogue kinds. All three compute alpha*acc + beta*C; the specialised ones

@@ -184,18 +184,20 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     return GEMM_OK;
   }
 
-  // Path selection. The matrix-core path stages A and B with 16-byte loads,
-  // so each operand's base and row pitch must be multiples of 16 bytes.
+  // Path selection. The matrix-core path stages A and B in 16-byte pieces; an
+  // operand whose base or row pitch is not a multiple of 16 bytes is staged
+  // element by element instead (masked kernel), so every f16/bf16 call runs on
+  // the matrix cores unless the VALU path is forced.
+  const bool a_elem = (uintptr_t)A % 16 || (lda * 2) % 16;
+  const bool b_elem = (uintptr_t)B % 16 || (ldb * 2) % 16;
+  std::string elem_reason;
+  if (a_elem) elem_reason = pitch_reason("A", A, lda);
+  if (b_elem) elem_reason += (a_elem ? "; " : "") + pitch_reason("B", B, ldb);
   std::string decline;
-  if ((uintptr_t)A % 16 || (lda * 2) % 16) decline = pitch_reason("A", A, lda);
-  else if ((uintptr_t)B % 16 || (ldb * 2) % 16) decline = pitch_reason("B", B, ldb);
   const char* force = env("GEMM_FORCE_PATH");
   if (force && std::strcmp(force, "fma") == 0) {
     decline = "forced by GEMM_FORCE_PATH=fma";
-  } else if (force && std::strcmp(force, "mfma") == 0) {
-    if (!decline.empty())
-      return fail(GEMM_ERR_UNSUPPORTED, "GEMM_FORCE_PATH=mfma but " + decline);
-  } else if (force) {
+  } else if (force && std::strcmp(force, "mfma") != 0) {
     return fail(GEMM_ERR_INVALID_ARG, std::string("GEMM_FORCE_PATH must be mfma or fma, got ") + force);
   }
   const char* ops = transA ? (transB ? "TT" : "TN") : (transB ? "NT" : "NN");
@@ -232,6 +234,9 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     const int64_t ldmax = lda > ldb ? lda : ldb;
     if (ldmax * 2 * rows + 4096 >= (int64_t{1} << 31)) plan.masked = true;
   }
+  a.a_elem = a_elem ? 1 : 0;
+  a.b_elem = b_elem ? 1 : 0;
+  if (a_elem || b_elem) plan.masked = true;
   a.tiles_m = (int)((M + ti.bm - 1) / ti.bm);
   a.tiles_n = (int)((N + ti.bn - 1) / ti.bn);
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7fffffff)
@@ -239,9 +244,11 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   // Whole 256x256 tiles with both operands K-contiguous take the kernel with
   // two wave groups (2x4 waves) and direct global->LDS loads.
   const bool pingpong = tile == TILE_256x256 && !transA && transB && !plan.masked;
-  std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s", ti.name,
+  std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s", ti.name,
                 ti.waves_m, pingpong ? 4 : ti.waves_n, ti.atom_m, ti.atom_n, ti.atom_k, ops,
-                epi_name, pingpong ? " pingpong" : "", plan.masked ? " masked" : "");
+                epi_name, pingpong ? " pingpong" : "", plan.masked ? " masked" : "",
+                elem_reason.empty() ? "" : " 16-bit staging (", elem_reason.c_str(),
+                elem_reason.empty() ? "" : ")");
   g_path = buf;
   return GEMM_OK;
 }

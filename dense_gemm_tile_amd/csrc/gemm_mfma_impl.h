@@ -143,9 +143,11 @@ struct Stager {
   }
 
   // Issue the global loads of the box at (r0, k0). rlim / klim: number of
-  // valid rows / K-values of the whole operand (used only when MASK).
+  // valid rows / K-values of the whole operand (used only when MASK). elem
+  // (MASK only): the operand's 16-byte pieces are not 16-byte aligned, so
+  // every piece is read as eight 16-bit elements.
   __device__ inline void load(const uint16_t* __restrict__ X, int64_t ld, int r0, int rlim,
-                              int k0, int klim, int tid) {
+                              int k0, int klim, int tid, bool elem = false) {
     if constexpr (!MASK) {
       if constexpr (KCONTIG) {
         const auto rs = make_rsrc(X + (int64_t)r0 * ld + k0);
@@ -170,10 +172,10 @@ struct Stager {
         const int r = r0 + (id >> 3);
         const int k = k0 + ((id & 7) << 3);
         const uint16_t* p = X + (int64_t)r * ld + k;
-        if (r < rlim && k + 8 <= klim) {
+        if (!elem && r < rlim && k + 8 <= klim) {
           v[i] = *reinterpret_cast<const u32x4*>(p);
         } else if (r < rlim && k < klim) {
-          v[i] = load_partial(p, klim - k);
+          v[i] = load_partial(p, klim - k < 8 ? klim - k : 8);
         } else {
           v[i] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -186,10 +188,10 @@ struct Stager {
       for (int j = 0; j < NL; ++j) {
         const int k = k0 + kb * NL + j;
         const uint16_t* p = X + (int64_t)k * ld + r;
-        if (k < klim && r + 8 <= rlim) {
+        if (!elem && k < klim && r + 8 <= rlim) {
           v[j] = *reinterpret_cast<const u32x4*>(p);
         } else if (k < klim && r < rlim) {
-          v[j] = load_partial(p, rlim - r);
+          v[j] = load_partial(p, rlim - r < 8 ? rlim - r : 8);
         } else {
           v[j] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -401,14 +403,14 @@ gemm_mfma_kernel(const GemmArgs p) {
   constexpr int CPS = At::K / 8;  // 16-byte chunks per K sub-step
 
   // Prologue: step 0 into buffer 0, step 1 into registers, first fragments.
-  sa.load(Ap, p.lda, m0, p.M, 0, p.K, tid);
-  sb.load(Bp, p.ldb, n0, p.N, 0, p.K, tid);
+  sa.load(Ap, p.lda, m0, p.M, 0, p.K, tid, p.a_elem);
+  sb.load(Bp, p.ldb, n0, p.N, 0, p.K, tid, p.b_elem);
   sa.store(smem, tid);
   sb.store(smem + Cfg::A_BYTES, tid);
   __syncthreads();
   if (KT > 1) {
-    sa.load(Ap, p.lda, m0, p.M, Cfg::BK, p.K, tid);
-    sb.load(Bp, p.ldb, n0, p.N, Cfg::BK, p.K, tid);
+    sa.load(Ap, p.lda, m0, p.M, Cfg::BK, p.K, tid, p.a_elem);
+    sb.load(Bp, p.ldb, n0, p.N, Cfg::BK, p.K, tid, p.b_elem);
   }
   Frags<Cfg> cur, nxt;
   read_frags<Cfg>(cur, smem, smem + Cfg::A_BYTES, a_row0, b_row0, koct);
@@ -429,8 +431,8 @@ gemm_mfma_kernel(const GemmArgs p) {
       __syncthreads();
       if (kt + 2 < KT) {
         const int k0 = (kt + 2) * Cfg::BK;
-        sa.load(Ap, p.lda, m0, p.M, k0, p.K, tid);
-        sb.load(Bp, p.ldb, n0, p.N, k0, p.K, tid);
+        sa.load(Ap, p.lda, m0, p.M, k0, p.K, tid, p.a_elem);
+        sb.load(Bp, p.ldb, n0, p.N, k0, p.K, tid, p.b_elem);
       }
       read_frags<Cfg>(nxt, nA, nA + Cfg::A_BYTES, a_row0, b_row0, koct);
     }

@@ -71,8 +71,18 @@ class Run:
             assert np.all(pad == D_SENTINEL), "kernel wrote past column N"
 
 
+def _shifted(x: torch.Tensor, dev, off: int) -> torch.Tensor:
+    """x on the device, starting `off` elements past an allocation's start
+    (off = 1 gives a base address 2 bytes past a 16-byte boundary)."""
+    if off == 0:
+        return x.to(dev)
+    flat = torch.zeros(off + x.numel(), dtype=x.dtype)
+    flat[off:] = x.reshape(-1)
+    return flat.to(dev)[off:].view(x.shape)
+
+
 def run(cfg: workloads.Config, inp: workloads.Inputs | None = None, *, poison=True,
-        stream=None, D_init=None) -> Run:
+        stream=None, D_init=None, a_off=0, b_off=0) -> Run:
     import dense_gemm_tile_amd as dgt
     if inp is None:
         inp = workloads.make_inputs(cfg)
@@ -83,8 +93,8 @@ def run(cfg: workloads.Config, inp: workloads.Inputs | None = None, *, poison=Tr
     B_h = poison_padding(inp.B, b_cols, cfg.dtype) if poison else inp.B
     inp = workloads.Inputs(cfg, inp.A_src, inp.B_src, A_h, B_h, inp.C)
     dev = torch.device("cuda:0")
-    A = A_h.to(dev)
-    B = B_h.to(dev)
+    A = _shifted(A_h, dev, a_off)
+    B = _shifted(B_h, dev, b_off)
     if cfg.inplace:
         assert inp.C is not None and ldc == ldd
         D = inp.C.to(dev).clone()
@@ -98,6 +108,7 @@ def run(cfg: workloads.Config, inp: workloads.Inputs | None = None, *, poison=Tr
             D.view(torch.int32).fill_(int(np.uint32(D_SENTINEL).view(np.int32)))
     say(f"{cfg.name} M={cfg.M} N={cfg.N} K={cfg.K} {cfg.dtype} tA={cfg.transA} "
         f"tB={cfg.transB} a={cfg.alpha} b={cfg.beta} lds={cfg.lds()} "
+        f"offs={a_off},{b_off} "
         f"force={os.environ.get('GEMM_FORCE_PATH')}/{os.environ.get('GEMM_FORCE_TILE')}")
     s = stream if stream is not None else torch.cuda.current_stream()
     dgt.gemm(cfg.M, cfg.N, cfg.K, cfg.dtype, cfg.transA, cfg.transB, cfg.alpha, cfg.beta,

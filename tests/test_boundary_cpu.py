@@ -112,18 +112,25 @@ def test_empty_and_degenerate_calls(lib):
     assert _v(lib, K=0, A=0, B=0, beta=0.0, C=0, lda=1) == lib.GEMM_OK
 
 
-def test_unaligned_pitch_falls_back_without_error(lib):
+def test_unaligned_pitch_stays_on_mfma_with_16bit_staging(lib):
     # transposed f16 A with lda = 4097: an 8194-byte row pitch
     st = _v(lib, M=4097, N=1000, K=1032, tA=1, lda=4097, alpha=2.0, beta=-1.0)
     assert st == lib.GEMM_OK
     path = lib.gemm_last_path()
-    assert path.startswith("fma ") and "A row pitch 8194 B" in path, path
+    assert path.startswith("mfma t128x128x64") and " masked " in path, path
+    assert path.endswith("16-bit staging (A row pitch 8194 B is not a multiple of 16 B)"), path
     assert _v(lib, A=A0 + 2) == lib.GEMM_OK
-    assert "A base address is not 16-byte aligned" in lib.gemm_last_path()
+    path = lib.gemm_last_path()
+    assert path.startswith("mfma ") and "A base address is not 16-byte aligned" in path, path
     assert _v(lib, ldb=72) == lib.GEMM_OK
-    assert lib.gemm_last_path().startswith("mfma ")  # 144-byte pitch is fine
+    assert "16-bit staging" not in lib.gemm_last_path()  # 144-byte pitch is fine
     assert _v(lib, ldb=67) == lib.GEMM_OK
-    assert "B row pitch 134 B" in lib.gemm_last_path()
+    assert "16-bit staging (B row pitch 134 B" in lib.gemm_last_path()
+    assert _v(lib, lda=67, ldb=67, M=64, N=64, K=64) == lib.GEMM_OK
+    assert "(A row pitch 134 B is not a multiple of 16 B; B row pitch 134 B" in lib.gemm_last_path()
+    # whole tiles with an unaligned operand still take the masked kernel
+    assert _v(lib, M=8192, N=8192, K=8192, tB=1, dtype=1, ldb=8193) == lib.GEMM_OK
+    assert " masked 16-bit staging (B " in lib.gemm_last_path(), lib.gemm_last_path()
 
 
 def test_ragged_dims_stay_on_mfma_masked(lib):
@@ -156,7 +163,8 @@ def test_force_path_and_tile(lib, monkeypatch):
     assert _v(lib) == lib.GEMM_OK
     assert "forced by GEMM_FORCE_PATH=fma" in lib.gemm_last_path()
     monkeypatch.setenv("GEMM_FORCE_PATH", "mfma")
-    assert _v(lib, A=A0 + 2) == lib.GEMM_ERR_UNSUPPORTED
+    assert _v(lib, A=A0 + 2) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma "), lib.gemm_last_path()
     monkeypatch.setenv("GEMM_FORCE_PATH", "bogus")
     assert _v(lib) == lib.GEMM_ERR_INVALID_ARG
     monkeypatch.delenv("GEMM_FORCE_PATH")
@@ -167,7 +175,7 @@ def test_force_path_and_tile(lib, monkeypatch):
     assert _v(lib) == lib.GEMM_ERR_INVALID_ARG
 
 
-def test_debug_log_names_the_declined_path():
+def test_debug_log_names_the_path_and_its_reason():
     code = (
         "import dense_gemm_tile_amd as d\n"
         "d.gemm_validate(4097,1000,1032,0,1,0,2.0,-1.0,0x10000000,4097,0x20000000,1000,"
@@ -179,7 +187,7 @@ def test_debug_log_names_the_declined_path():
     assert r.returncode == 0, r.stderr
     lines = [l for l in r.stderr.splitlines() if l.startswith("[gemm]")]
     assert len(lines) == 2
-    assert "M=4097 N=1000 K=1032 -> fma " in lines[0] and "A row pitch 8194 B" in lines[0]
+    assert "M=4097 N=1000 K=1032 -> mfma " in lines[0] and "A row pitch 8194 B" in lines[0]
     assert "error 1: negative dimension" in lines[1]
 
 

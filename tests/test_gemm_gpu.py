@@ -37,10 +37,9 @@ def test_workload_parity_full(name):
     r = run(C[name])
     r.check()
     r.check_padding_untouched()
+    assert r.path.startswith("mfma "), r.path
     if name == "ragged4097x1000x1032_tn":
-        assert r.path.startswith("fma ") and "A row pitch 8194 B" in r.path, r.path
-    else:
-        assert r.path.startswith("mfma "), r.path
+        assert "16-bit staging (A row pitch 8194 B" in r.path, r.path
 
 
 @pytest.mark.parametrize("name", ["gemm4096_inplace", "gemm8192_nt"])
@@ -109,6 +108,32 @@ def test_tiled_shapes(tile, dtype, monkeypatch):
                 assert r.path.startswith("mfma " + tile), r.path
                 r.check()
                 r.check_padding_untouched()
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_tiled_shapes_16bit_staging(tile, dtype, monkeypatch):
+    """Operands whose row pitch or base address is not a multiple of 16 bytes
+    stay on the matrix cores, staged element by element: odd pitches, bases
+    2 bytes past a 16-byte boundary, one or both operands, every layout."""
+    monkeypatch.setenv("GEMM_FORCE_TILE", tile)
+    seed = 5000
+    def odd(x):  # a leading dimension whose pitch is not a multiple of 16 bytes
+        return x + 1 if (x + 1) % 8 else x + 3
+
+    for (M, N, K) in SHAPES[1::2] + [(512, 512, 192)]:
+        for tA, tB in [(0, 0), (0, 1), (1, 0), (1, 1)]:
+            seed += 1
+            mode = seed % 4
+            lda = odd(M if tA else K) if mode in (0, 2) else (M if tA else K) + 8
+            ldb = odd(K if tB else N) if mode in (1, 2) else _pad8(K if tB else N)
+            a_off, b_off = (1, 0) if mode == 3 else (0, 1 if mode == 0 else 0)
+            cfg = workloads.Config(f"elem{seed}", M, N, K, dtype, tA, tB, 1.5, -0.5,
+                                   "uniform", seed, lda=lda, ldb=ldb)
+            r = run(cfg, a_off=a_off, b_off=b_off)
+            assert r.path.startswith("mfma " + tile) and "16-bit staging (" in r.path, r.path
+            r.check()
+            r.check_padding_untouched()
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
