@@ -241,9 +241,9 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   a.tiles_n = (int)((N + ti.bn - 1) / ti.bn);
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7fffffff)
     return fail(GEMM_ERR_UNSUPPORTED, "too many output tiles for one launch");
-  // Whole 256x256 tiles with both operands K-contiguous take the kernel with
-  // two wave groups (2x4 waves) and direct global->LDS loads.
-  const bool pingpong = tile == TILE_256x256 && !transA && transB && !plan.masked;
+  // Whole 256x256 tiles (any operand layout) take the kernel with two wave
+  // groups (2x4 waves) and direct global->LDS loads.
+  const bool pingpong = tile == TILE_256x256 && !plan.masked;
   std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s", ti.name,
                 ti.waves_m, pingpong ? 4 : ti.waves_n, ti.atom_m, ti.atom_n, ti.atom_k, ops,
                 epi_name, pingpong ? " pingpong" : "", plan.masked ? " masked" : "",

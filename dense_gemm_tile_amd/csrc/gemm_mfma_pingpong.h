@@ -1,6 +1,7 @@
-// Matrix-core GEMM for whole 256x256 output tiles whose operands are both
-// K-contiguous (A stored [M][K], B stored [N][K]): direct global->LDS staging
-// and two wave groups that take turns on the matrix cores.
+// Matrix-core GEMM for whole 256x256 output tiles: direct global->LDS staging
+// and two wave groups that take turns on the matrix cores. Each operand may be
+// K-contiguous (A stored [M][K], B stored [N][K]) or M/N-contiguous (A stored
+// [K][M], B stored [K][N]).
 //
 // Same contraction and atom nest as the general kernel (TVM TIRx `gemm`:
 // "Algorithm" steps 1-3), with the Phobos `@pipeline` idea of asynchronous
@@ -14,14 +15,13 @@
 //  * Time is cut into phases at workgroup barriers. In each phase one group
 //    multiplies a whole K slice of 64 from registers (32 MFMAs per wave, no
 //    memory instruction in between) while the other group reads its next
-//    slice's 24 fragments from LDS and issues loads; the roles swap at every
+//    slice's fragments from LDS and issues loads; the roles swap at every
 //    barrier. The matrix cores of a SIMD are therefore fed by one wave while
 //    the other one waits on memory.
 //  * Loads are buffer_load_dwordx4 with the LDS bit: each lane's 16 bytes go
 //    straight into LDS (no VGPR round trip, no LDS store instruction). One
-//    instruction fills 1 KiB of LDS in lane order: eight whole 128-byte row
-//    segments (64 K-values of eight rows), so every global access is a full
-//    cache line.
+//    instruction fills 1 KiB of LDS in lane order, and always covers whole
+//    128-byte lines of the operand in memory.
 //  * LDS is a ring of five 32 KiB half-slots; A of K slice t lives in slot
 //    2t % 5 and B in slot (2t+1) % 5. One half slice (32 instructions per
 //    workgroup) is loaded per phase, so the texture path is busy at an even
@@ -29,12 +29,17 @@
 //    group 0 loads B of slice s+1 in its own. A slot is refilled only after
 //    the phase in which the second group read it, and every load has at least
 //    one further phase to land before the barrier that certifies it.
-//  * Rows are 128 bytes (64 K-values, eight 16-byte chunks); chunk c of row r
-//    sits at chunk position c ^ ((r ^ (r>>3)) & 7), the layout that the
-//    general kernel uses, which keeps the fragment reads free of bank
-//    conflicts. Lane l of a load instruction covering rows r0..r0+7 writes
-//    slot l%8 of row r0 + l/8, so it fetches the chunk that the layout puts
-//    there.
+//  * K-contiguous operand slot: 256 rows (M or N) of 128 bytes (64 K-values,
+//    eight 16-byte chunks); chunk c of row r sits at chunk position
+//    c ^ ((r ^ (r>>3)) & 7), as in the general kernel. A fragment (8
+//    consecutive K-values of one row) is one ds_read_b128.
+//  * M/N-contiguous operand slot: 64 rows (K) of 512 bytes (256 M or N values,
+//    32 chunks); chunk c of row r sits at c ^ (4 * (r & 3)). A fragment is two
+//    ds_read_b64_tr_b16: in each group of 16 lanes, lane s names 4 consecutive
+//    values of row s/4, and lane i receives value i of the group's 16 columns
+//    from each of the four rows, i.e. 4 consecutive K-values of one column.
+//    The swizzle spreads the 4 rows x 64 bytes that 32 lanes read over all
+//    banks.
 //  * This compiler inserts no waits between a direct-to-LDS load and LDS
 //    reads of the same bytes: each wave waits on vmcnt for its own loads of a
 //    slice before the barrier that precedes the slice's first read.
@@ -51,21 +56,14 @@ struct PingPongCfg {
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // 128 x 64 per wave
   static constexpr int TM = WTM / At::M, TN = WTN / At::N;
   static constexpr int KSTEPS = BK / At::K;            // MFMA K sub-steps per slice
-  static constexpr int FRAGS = KSTEPS * (TM + TN);     // fragment reads per slice
-  static constexpr int ROW_BYTES = BK * 2;             // 128
-  static constexpr int SLOT_BYTES = 256 * ROW_BYTES;   // one operand of one slice
+  static constexpr int SLOT_BYTES = 256 * BK * 2;      // one operand of one slice
   static constexpr int SLOTS = 5;
   static constexpr int LDS_BYTES = SLOTS * SLOT_BYTES;
   static constexpr int LOADS = SLOT_BYTES / 1024 / (THREADS / 64 / 2);  // per wave per half slice
-  static_assert(BM == 256 && BN == 256, "slots hold 256 rows");
+  static_assert(BM == 256 && BN == 256, "slots hold 256 rows or columns");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
   static_assert(LOADS == 8, "four waves load one 32 KiB half slice");
 };
-
-// Byte offset of 16-byte chunk `chunk` of row `row` in a slot.
-__device__ static inline int pp_lds_off(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
 
 // s_waitcnt with the other counters left alone (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -93,77 +91,99 @@ __device__ __forceinline__ void pp_barrier() {
 }
 
 using pp_lds_ptr_t = __attribute__((address_space(3))) void*;
+typedef short pp_i16x4 __attribute__((ext_vector_type(4)));
 
-// Per-wave addressing: the source of this wave's load instructions (A for
-// group 1, B for group 0) and the LDS offsets of its fragments.
-struct PingPongPipe {
+// One operand's loads (by the wave group that loads it) and fragment reads
+// (by every wave). MN: the operand is stored with M (or N) contiguous.
+// NFRAG atoms of 32 rows/columns per wave, starting at row0 of the tile.
+template <bool MN, int NFRAG>
+struct PpOperand;
+
+template <int NFRAG>
+struct PpOperand<false, NFRAG> {
   using C = PingPongCfg;
-  using At = C::At;
-  char* smem;
-  // Base of this wave's operand box. A plain pointer (the buffer resource is
-  // built at each load and hoisted by the compiler): a member of the
-  // device-only resource type makes the struct unusable in the host pass.
-  const uint16_t* base;
-  int ld2;   // row pitch in bytes
-  int row;   // byte offset of this lane's first row
-  int c0;    // chunk of this lane in instruction 0
-  int lw;    // wave index within its group
-  int offA[C::TM], offB[C::TN];  // fragment offsets within a slot, sub-step 0
+  // Load side: this lane's byte offset for instruction 0 and its chunk.
+  const uint16_t* base;  // tile's first row (M or N index), K = 0
+  int ld2, row, c0;
+  // Read side: byte offset of each atom's fragment within a slot, sub-step 0.
+  int off[NFRAG];
 
-  __device__ inline void init(const GemmArgs& p, char* smem_, int m0, int n0, int group, int wave,
-                              int lane, int wm, int wn) {
-    smem = smem_;
-    lw = wave & 3;
-    if (group == 1) {
-      base = static_cast<const uint16_t*>(p.A) + (int64_t)m0 * p.lda;
-      ld2 = (int)(p.lda * 2);
-    } else {
-      base = static_cast<const uint16_t*>(p.B) + (int64_t)n0 * p.ldb;
-      ld2 = (int)(p.ldb * 2);
-    }
+  __device__ static inline int lds_off(int r, int chunk) {
+    return r * 128 + ((chunk ^ ((r ^ (r >> 3)) & 7)) << 4);
+  }
+  __device__ inline void init_load(const uint16_t* X, int64_t ld, int r0, int lw, int lane) {
+    base = X + (int64_t)r0 * ld;
+    ld2 = (int)(ld * 2);
     // Instruction i of wave lw covers rows 64*lw + 8i .. +7. Lane l fills
-    // slot l%8 of row 64*lw + 8i + l/8, whose swizzle is (l/8) ^ i, so it
-    // fetches chunk (l%8) ^ (l/8) ^ i.
+    // chunk slot l%8 of row 64*lw + 8i + l/8, whose swizzle is (l/8) ^ i, so
+    // it fetches chunk (l%8) ^ (l/8) ^ i of that row.
     row = (lw * 64 + (lane >> 3)) * ld2;
     c0 = (lane & 7) ^ (lane >> 3);
-    // Fragment rows keep their low three bits per lane and the chunk of
-    // sub-step ks is 2*ks + koct, so the offset for sub-step ks is the
-    // sub-step-0 offset with ks << 5 XOR-ed in (bits 5-6 of the chunk slot).
-    const int koct = At::frag_koct(lane);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-      offA[i] = pp_lds_off(wm * C::WTM + i * At::M + At::frag_row(lane), koct);
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      offB[j] = pp_lds_off(wn * C::WTN + j * At::N + At::frag_row(lane), koct);
   }
-
-  // Load instruction i (0..7) of K slice `slice` into half-slot `slot`.
-  __device__ __forceinline__ void issue(int i, int slice, int slot) const {
+  __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
     const int voff = row + ((c0 ^ i) << 4);
-    const int soff = slice * C::ROW_BYTES + i * 8 * ld2;
-    char* dst = smem + slot * C::SLOT_BYTES + (lw * C::LOADS + i) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (pp_lds_ptr_t)dst, 16, voff, soff, 0,
-                                             0);
+    const int soff = slice * (C::BK * 2) + i * 8 * ld2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
+                                             16, voff, soff, 0, 0);
   }
-  __device__ __forceinline__ void issue_half(int slice, int slot) const {
+  __device__ inline void init_read(int row0, int lane) {
+    // Fragment rows keep their low three bits per lane and the chunk of
+    // sub-step ks is 2*ks + koct, so sub-step ks is the sub-step-0 offset with
+    // ks << 5 XOR-ed in (bits 5-6 of the chunk position).
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) issue(i, slice, slot);
+    for (int t = 0; t < NFRAG; ++t)
+      off[t] = lds_off(row0 + t * 32 + (lane & 31), lane >> 5);
   }
+  __device__ __forceinline__ u32x4 read(const char* slot, int t, int ks) const {
+    return *reinterpret_cast<const u32x4*>(slot + (off[t] ^ (ks << 5)));
+  }
+};
 
-  // All fragments of one K slice (A in slot sa, B in slot sb).
-  __device__ __forceinline__ void read(Frags<C> (&f)[C::KSTEPS], int sa, int sb) const {
-    const char* a = smem + sa * C::SLOT_BYTES;
-    const char* b = smem + sb * C::SLOT_BYTES;
+template <int NFRAG>
+struct PpOperand<true, NFRAG> {
+  using C = PingPongCfg;
+  const uint16_t* base;  // tile's first column (M or N index), K = 0
+  int64_t ld;
+  int voff[2];           // instructions with i even / odd
+  int off[NFRAG];
+
+  __device__ inline void init_load(const uint16_t* X, int64_t ld_, int c0, int lw, int lane) {
+    base = X + c0;
+    ld = ld_;
+    // Instruction i of wave lw covers K rows 16*lw + 2i and +1 (512 bytes
+    // each). Lane l fills chunk slot l%32 of row 16*lw + 2i + l/32, whose
+    // swizzle is 4*((2i + l/32) & 3), so it fetches that chunk of the row.
+    const int hi = lane >> 5, p = lane & 31;
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+    for (int par = 0; par < 2; ++par)
+      voff[par] = (int)((lw * 16 + hi) * ld * 2) + ((p ^ (4 * ((2 * par + hi) & 3))) << 4);
+  }
+  __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
+    // The slice's first K row is folded into the resource base so that the
+    // 32-bit offsets stay within 16 rows of the operand.
+    const uint16_t* b = base + (int64_t)slice * C::BK * ld;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(b), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
+                                             16, voff[i & 1], (int)(2 * i * ld * 2), 0, 0);
+  }
+  __device__ inline void init_read(int col0, int lane) {
+    // Lane l (group g = l/16, s = l%16) of the first transposed read of
+    // sub-step 0 names row 8*(l/32) + s/4, columns col0 + 16*(g&1) + 4*(s%4)
+    // .. +3. The second read is 4 rows down, sub-step ks is 16*ks rows down:
+    // both keep r & 3, so they are immediate offsets.
+    const int r = 8 * (lane >> 5) + ((lane & 15) >> 2);
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-        f[ks].a[i] = *reinterpret_cast<const u32x4*>(a + (offA[i] ^ (ks << 5)));
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-        f[ks].b[j] = *reinterpret_cast<const u32x4*>(b + (offB[j] ^ (ks << 5)));
+    for (int t = 0; t < NFRAG; ++t) {
+      const int col = col0 + t * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      off[t] = r * 512 + (((col >> 3) ^ (4 * (r & 3))) << 4) + ((col & 7) << 1);
     }
+  }
+  __device__ __forceinline__ u32x4 read(const char* slot, int t, int ks) const {
+    typedef __attribute__((address_space(3))) pp_i16x4 lds_i16x4;
+    const char* p = slot + off[t] + ks * 16 * 512;
+    const pp_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    const pp_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * 512));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
   }
 };
 
@@ -181,6 +201,61 @@ __device__ __forceinline__ void pp_multiply(typename C::At::acc_t (&acc)[C::TM][
         acc[i][j] = At::mma(Tag{}, f[ks].a[i], f[ks].b[j], acc[i][j]);
 }
 
+template <bool AMN, bool BMN>
+struct PingPongPipe {
+  using C = PingPongCfg;
+  char* smem;
+  int lw;  // wave index within its group
+  PpOperand<AMN, C::TM> a;
+  PpOperand<BMN, C::TN> b;
+
+  __device__ inline void init(const GemmArgs& p, char* smem_, int m0, int n0, int group, int wave,
+                              int lane, int wm, int wn) {
+    smem = smem_;
+    lw = wave & 3;
+    // Only group 1 loads A and only group 0 loads B; both are set up so that
+    // every register the loop keeps is defined.
+    a.init_load(static_cast<const uint16_t*>(p.A), p.lda, m0, lw, lane);
+    b.init_load(static_cast<const uint16_t*>(p.B), p.ldb, n0, lw, lane);
+    a.init_read(wm * C::WTM, lane);
+    b.init_read(wn * C::WTN, lane);
+  }
+  // This wave's eight instructions of A (group 1) or B (group 0) of a slice.
+  __device__ __forceinline__ void issue_a(int slice, int slot) const {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) a.issue(smem + slot * C::SLOT_BYTES, lw, i, slice);
+  }
+  __device__ __forceinline__ void issue_b(int slice, int slot) const {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) b.issue(smem + slot * C::SLOT_BYTES, lw, i, slice);
+  }
+  // All fragments of one K slice (A in slot sa, B in slot sb).
+  __device__ __forceinline__ void read(Frags<C> (&f)[C::KSTEPS], int sa, int sb) const {
+    const char* pa = smem + sa * C::SLOT_BYTES;
+    const char* pb = smem + sb * C::SLOT_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) f[ks].a[i] = a.read(pa, i, ks);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) f[ks].b[j] = b.read(pb, j, ks);
+    }
+  }
+  // Keep the per-lane address terms opaque to loop-invariant code motion, so
+  // that the load and fragment offsets are formed at use instead of
+  // occupying registers next to 128 accumulators.
+  __device__ __forceinline__ void launder() {
+#pragma unroll
+    for (int t = 0; t < C::TM; ++t) asm volatile("" : "+v"(a.off[t]));
+#pragma unroll
+    for (int t = 0; t < C::TN; ++t) asm volatile("" : "+v"(b.off[t]));
+    if constexpr (AMN) asm volatile("" : "+v"(a.voff[0]), "+v"(a.voff[1]));
+    else asm volatile("" : "+v"(a.row), "+v"(a.c0));
+    if constexpr (BMN) asm volatile("" : "+v"(b.voff[0]), "+v"(b.voff[1]));
+    else asm volatile("" : "+v"(b.row), "+v"(b.c0));
+  }
+};
+
 // The phase loop. Phase numbers: the prologue is phase 0; group 0 reads slice
 // s in phase 2s+1 and multiplies it in 2s+2; group 1 reads it in 2s+2 and
 // multiplies it in 2s+3 (its phase 1 is idle). Slice t must be in LDS at the
@@ -190,21 +265,21 @@ __device__ __forceinline__ void pp_multiply(typename C::At::acc_t (&acc)[C::TM][
 // this compiler's host pass rejects a second kernel (same Tag, other
 // epilogue) calling a device function template specialization already
 // instantiated for the first one.
-template <class C, class Tag, int EPI>
+template <class C, class Tag, int EPI, bool AMN, bool BMN>
 __device__ __forceinline__ void pp_mainloop(typename C::At::acc_t (&acc)[C::TM][C::TN],
-                                            const PingPongPipe& pipe, int K, int group) {
+                                            const PingPongPipe<AMN, BMN>& pipe, int K, int group) {
   const int KT = K / C::BK;  // whole slices (unmasked kernel)
   // Prologue: group 1 requests A of slices 0 and 1, group 0 B of slice 0.
   if (group == 1) {
-    pipe.issue_half(0, 0);
+    pipe.issue_a(0, 0);
     if (KT > 1) {
-      pipe.issue_half(1, 2);
+      pipe.issue_a(1, 2);
       pp_wait_vm<C::LOADS>();
     } else {
       pp_wait_vm<0>();
     }
   } else {
-    pipe.issue_half(0, 1);
+    pipe.issue_b(0, 1);
     pp_wait_vm<0>();
   }
   pp_barrier();
@@ -214,25 +289,20 @@ __device__ __forceinline__ void pp_mainloop(typename C::At::acc_t (&acc)[C::TM][
   }
 
   Frags<C> f[C::KSTEPS];
-  PingPongPipe pp = pipe;
+  PingPongPipe<AMN, BMN> pp = pipe;
   int h = 0;  // (2s) % 5: the slot of A of slice s
   for (int s = 0; s < KT; ++s) {
-    // Keep the per-lane address terms opaque to loop-invariant code motion,
-    // so that the 8 load offsets and 24 fragment offsets are formed at use
-    // instead of occupying registers next to 128 accumulators.
-    asm volatile("" : "+v"(pp.c0), "+v"(pp.row));
-    asm volatile("" : "+v"(pp.offA[0]), "+v"(pp.offA[1]), "+v"(pp.offA[2]), "+v"(pp.offA[3]),
-                 "+v"(pp.offB[0]), "+v"(pp.offB[1]));
+    pp.launder();
     const int sa = h, sb = h == 4 ? 0 : h + 1;
     // Memory phase: fragments first (they drain through LDS while the load
     // instructions queue on the texture path), then this group's half slice.
     pp.read(f, sa, sb);
     if (group == 0) {
-      if (s + 1 < KT) pp.issue_half(s + 1, h >= 2 ? h - 2 : h + 3);  // B of s+1: (2s+3) % 5
+      if (s + 1 < KT) pp.issue_b(s + 1, h >= 2 ? h - 2 : h + 3);  // B of s+1: (2s+3) % 5
       pp_wait_lgkm0();
     } else {
       const bool ld = s + 2 < KT;
-      if (ld) pp.issue_half(s + 2, h >= 1 ? h - 1 : h + 4);  // A of s+2: (2s+4) % 5
+      if (ld) pp.issue_a(s + 2, h >= 1 ? h - 1 : h + 4);  // A of s+2: (2s+4) % 5
       // A of slice s+1 (requested one memory phase earlier) is needed from
       // the next phase on.
       if (ld) pp_wait_vm_lgkm0<C::LOADS>();
@@ -248,7 +318,7 @@ __device__ __forceinline__ void pp_mainloop(typename C::At::acc_t (&acc)[C::TM][
   if (group == 0) pp_barrier();  // matches group 1's idle phase: same barrier count
 }
 
-template <class Tag, int EPI>
+template <class Tag, int EPI, bool AMN, bool BMN>
 __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_mfma_pingpong_kernel(const GemmArgs p) {
   using C = PingPongCfg;
   using At = typename C::At;
@@ -266,7 +336,7 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_mfma_pingpong_kerne
   const int m0 = tm * C::BM;
   const int n0 = tn * C::BN;
 
-  PingPongPipe pipe;
+  PingPongPipe<AMN, BMN> pipe;
   pipe.init(p, smem, m0, n0, group, wave, lane, wm, wn);
 
   acc_t acc[C::TM][C::TN];
@@ -277,7 +347,7 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_mfma_pingpong_kerne
 #pragma unroll
       for (int v = 0; v < At::NACC; ++v) acc[i][j][v] = 0.0f;
 
-  pp_mainloop<C, Tag, EPI>(acc, pipe, p.K, group);
+  pp_mainloop<C, Tag, EPI, AMN, BMN>(acc, pipe, p.K, group);
   store_tile<C, EPI, false>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane);
 }
 

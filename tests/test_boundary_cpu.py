@@ -153,7 +153,7 @@ def test_tile_and_epilogue_choice(lib):
     assert _v(lib, M=8192, N=8192, K=8192, tB=1, dtype=1) == lib.GEMM_OK
     assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 pingpong"
     assert _v(lib, M=4096, N=4096, K=4096, dtype=1, beta=1.0, C=D0) == lib.GEMM_OK
-    assert lib.gemm_last_path() == "mfma t256x256x64 w2x2 a32x32x16 NN epi=acc+c"
+    assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 NN epi=acc+c pingpong"
     assert _v(lib, M=512, N=512, K=512, alpha=1.5, beta=0.5) == lib.GEMM_OK
     assert "epi=general" in lib.gemm_last_path()
 

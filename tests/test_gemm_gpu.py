@@ -293,18 +293,25 @@ def test_deterministic_repeat_and_side_stream():
     assert torch.equal(a, b) and torch.equal(a, c)
 
 
+@pytest.mark.parametrize("layout", [(0, 1), (0, 0), (1, 1), (1, 0)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_pingpong_path_slice_counts(dtype, monkeypatch):
-    """Whole 256x256 NT tiles take the two-group kernel with direct loads; K
-    from one slice of 64 (prologue only) through two (no load in the loop)
-    to several turns of the five-slot ring."""
+def test_pingpong_path_slice_counts(dtype, layout, monkeypatch):
+    """Whole 256x256 tiles take the two-group kernel with direct loads, for
+    K-contiguous operands (ds_read_b128 fragments) and M/N-contiguous ones
+    (transposed ds_read_b64_tr_b16 fragments); K from one slice of 64
+    (prologue only) through two (no load in the loop) to several turns of the
+    five-slot ring; padded leading dimensions."""
     monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
-    seed = 4000
+    tA, tB = layout
+    seed = 4000 + 100 * (2 * tA + tB)
     for K in (64, 128, 192, 256, 320, 384, 448, 640, 1024):
         for alpha, beta in [(1.0, 0.0), (1.0, 1.0), (-0.5, 2.0)]:
             seed += 1
-            cfg = workloads.Config(f"dma{seed}", 512, 768, K, dtype, 0, 1, alpha, beta,
-                                   "uniform", seed, ldd=768 + 4, ldc=768 + 4)
+            M, N = 512, 768
+            lda = (M if tA else K) + (8 if seed % 2 else 0)
+            ldb = (K if tB else N) + (16 if seed % 3 == 0 else 0)
+            cfg = workloads.Config(f"pp{seed}", M, N, K, dtype, tA, tB, alpha, beta,
+                                   "uniform", seed, lda=lda, ldb=ldb, ldd=N + 4, ldc=N + 4)
             r = run(cfg)
             assert "pingpong" in r.path, r.path
             r.check()
