@@ -21,8 +21,9 @@ struct GemmArgs {
   int tiles_m;   // output tiles along M / N for the tile scheduler
   int tiles_n;
   int group_m;   // tile-row group height of the grouped order
-  int a_elem;    // 1: A's base or row pitch is not a multiple of 16 bytes, so the
-  int b_elem;    //    masked kernel stages it element by element (same for B)
+  int a_vw;      // staging vector width of A in 16-bit elements (8, 4, 2 or 1):
+  int b_vw;      //    the widest whose byte size divides A's base and row pitch
+                 //    (same for B); below 8 only the masked kernel runs
 };
 
 // Epilogue kinds. All three compute alpha*acc + beta*C; the specialised ones

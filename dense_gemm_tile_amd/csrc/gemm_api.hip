@@ -57,13 +57,22 @@ bool overlaps(const void* p, unsigned __int128 np, const void* q, unsigned __int
   return a < b + nq && b < a + np;
 }
 
-std::string pitch_reason(const char* name, const void* ptr, int64_t ld) {
+// Widest staging vector (in 16-bit elements: 8, 4, 2 or 1) whose byte size
+// divides both the operand's base address and its row pitch.
+int vector_width(const void* ptr, int64_t ld) {
+  int vw = 8;
+  while (vw > 1 && ((uintptr_t)ptr % (2 * vw) != 0 || (ld * 2) % (2 * vw) != 0)) vw /= 2;
+  return vw;
+}
+
+std::string pitch_reason(const char* name, const void* ptr, int64_t ld, int vw) {
   char buf[160];
   if ((uintptr_t)ptr % 16 != 0) {
-    std::snprintf(buf, sizeof buf, "%s base address is not 16-byte aligned", name);
+    std::snprintf(buf, sizeof buf, "%s: %d-byte loads, base address is not 16-byte aligned",
+                  name, 2 * vw);
   } else {
-    std::snprintf(buf, sizeof buf, "%s row pitch %lld B is not a multiple of 16 B", name,
-                  (long long)(ld * 2));
+    std::snprintf(buf, sizeof buf, "%s: %d-byte loads, row pitch %lld B is not a multiple of 16 B",
+                  name, 2 * vw, (long long)(ld * 2));
   }
   return buf;
 }
@@ -185,14 +194,14 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   }
 
   // Path selection. The matrix-core path stages A and B in 16-byte pieces; an
-  // operand whose base or row pitch is not a multiple of 16 bytes is staged
-  // element by element instead (masked kernel), so every f16/bf16 call runs on
-  // the matrix cores unless the VALU path is forced.
-  const bool a_elem = (uintptr_t)A % 16 || (lda * 2) % 16;
-  const bool b_elem = (uintptr_t)B % 16 || (ldb * 2) % 16;
+  // operand whose base or row pitch is not a multiple of 16 bytes is read with
+  // the widest loads they allow (8, 4 or 2 bytes, masked kernel), so every
+  // f16/bf16 call runs on the matrix cores unless the VALU path is forced.
+  const int a_vw = vector_width(A, lda), b_vw = vector_width(B, ldb);
+  const bool a_elem = a_vw < 8, b_elem = b_vw < 8;
   std::string elem_reason;
-  if (a_elem) elem_reason = pitch_reason("A", A, lda);
-  if (b_elem) elem_reason += (a_elem ? "; " : "") + pitch_reason("B", B, ldb);
+  if (a_elem) elem_reason = pitch_reason("A", A, lda, a_vw);
+  if (b_elem) elem_reason += (a_elem ? "; " : "") + pitch_reason("B", B, ldb, b_vw);
   std::string decline;
   const char* force = env("GEMM_FORCE_PATH");
   if (force && std::strcmp(force, "fma") == 0) {
@@ -234,8 +243,8 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     const int64_t ldmax = lda > ldb ? lda : ldb;
     if (ldmax * 2 * rows + 4096 >= (int64_t{1} << 31)) plan.masked = true;
   }
-  a.a_elem = a_elem ? 1 : 0;
-  a.b_elem = b_elem ? 1 : 0;
+  a.a_vw = a_vw;
+  a.b_vw = b_vw;
   if (a_elem || b_elem) plan.masked = true;
   a.tiles_m = (int)((M + ti.bm - 1) / ti.bm);
   a.tiles_n = (int)((N + ti.bn - 1) / ti.bn);
@@ -247,7 +256,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s", ti.name,
                 ti.waves_m, pingpong ? 4 : ti.waves_n, ti.atom_m, ti.atom_n, ti.atom_k, ops,
                 epi_name, pingpong ? " pingpong" : "", plan.masked ? " masked" : "",
-                elem_reason.empty() ? "" : " 16-bit staging (", elem_reason.c_str(),
+                elem_reason.empty() ? "" : " narrow staging (", elem_reason.c_str(),
                 elem_reason.empty() ? "" : ")");
   g_path = buf;
   return GEMM_OK;

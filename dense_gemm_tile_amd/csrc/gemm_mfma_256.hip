@@ -1,6 +1,6 @@
 // Instantiates the matrix-core GEMM kernels for the 256x256 output tile. Whole
 // tiles take the two-group direct-to-LDS kernel, in any of the four operand
-// layouts; tiles that need masking (or 64-bit addressing, or 16-bit staging)
+// layouts; tiles that need masking (or 64-bit addressing, or narrow staging)
 // take the general kernel.
 #include "gemm_mfma_pingpong.h"
 

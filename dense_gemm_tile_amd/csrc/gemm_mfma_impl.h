@@ -142,12 +142,26 @@ struct Stager {
     return r;
   }
 
+  // A whole piece read with vw-element (2*vw-byte) loads, vw in {4, 2, 1}.
+  __device__ static inline u32x4 load_narrow(const uint16_t* p, int vw) {
+    if (vw == 4) {
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 4);
+      return u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+    if (vw == 2) {
+      const unsigned* q = reinterpret_cast<const unsigned*>(p);
+      return u32x4{q[0], q[1], q[2], q[3]};
+    }
+    return load_partial(p, 8);
+  }
+
   // Issue the global loads of the box at (r0, k0). rlim / klim: number of
-  // valid rows / K-values of the whole operand (used only when MASK). elem
-  // (MASK only): the operand's 16-byte pieces are not 16-byte aligned, so
-  // every piece is read as eight 16-bit elements.
+  // valid rows / K-values of the whole operand (used only when MASK). vw
+  // (MASK only): the operand's staging vector width in elements; below 8 its
+  // 16-byte pieces are not 16-byte aligned and are read in narrower loads.
   __device__ inline void load(const uint16_t* __restrict__ X, int64_t ld, int r0, int rlim,
-                              int k0, int klim, int tid, bool elem = false) {
+                              int k0, int klim, int tid, int vw = 8) {
     if constexpr (!MASK) {
       if constexpr (KCONTIG) {
         const auto rs = make_rsrc(X + (int64_t)r0 * ld + k0);
@@ -172,8 +186,8 @@ struct Stager {
         const int r = r0 + (id >> 3);
         const int k = k0 + ((id & 7) << 3);
         const uint16_t* p = X + (int64_t)r * ld + k;
-        if (!elem && r < rlim && k + 8 <= klim) {
-          v[i] = *reinterpret_cast<const u32x4*>(p);
+        if (r < rlim && k + 8 <= klim) {
+          v[i] = vw == 8 ? *reinterpret_cast<const u32x4*>(p) : load_narrow(p, vw);
         } else if (r < rlim && k < klim) {
           v[i] = load_partial(p, klim - k < 8 ? klim - k : 8);
         } else {
@@ -188,8 +202,8 @@ struct Stager {
       for (int j = 0; j < NL; ++j) {
         const int k = k0 + kb * NL + j;
         const uint16_t* p = X + (int64_t)k * ld + r;
-        if (!elem && k < klim && r + 8 <= rlim) {
-          v[j] = *reinterpret_cast<const u32x4*>(p);
+        if (k < klim && r + 8 <= rlim) {
+          v[j] = vw == 8 ? *reinterpret_cast<const u32x4*>(p) : load_narrow(p, vw);
         } else if (k < klim && r < rlim) {
           v[j] = load_partial(p, rlim - r < 8 ? rlim - r : 8);
         } else {
@@ -403,14 +417,14 @@ gemm_mfma_kernel(const GemmArgs p) {
   constexpr int CPS = At::K / 8;  // 16-byte chunks per K sub-step
 
   // Prologue: step 0 into buffer 0, step 1 into registers, first fragments.
-  sa.load(Ap, p.lda, m0, p.M, 0, p.K, tid, p.a_elem);
-  sb.load(Bp, p.ldb, n0, p.N, 0, p.K, tid, p.b_elem);
+  sa.load(Ap, p.lda, m0, p.M, 0, p.K, tid, p.a_vw);
+  sb.load(Bp, p.ldb, n0, p.N, 0, p.K, tid, p.b_vw);
   sa.store(smem, tid);
   sb.store(smem + Cfg::A_BYTES, tid);
   __syncthreads();
   if (KT > 1) {
-    sa.load(Ap, p.lda, m0, p.M, Cfg::BK, p.K, tid, p.a_elem);
-    sb.load(Bp, p.ldb, n0, p.N, Cfg::BK, p.K, tid, p.b_elem);
+    sa.load(Ap, p.lda, m0, p.M, Cfg::BK, p.K, tid, p.a_vw);
+    sb.load(Bp, p.ldb, n0, p.N, Cfg::BK, p.K, tid, p.b_vw);
   }
   Frags<Cfg> cur, nxt;
   read_frags<Cfg>(cur, smem, smem + Cfg::A_BYTES, a_row0, b_row0, koct);
@@ -431,8 +445,8 @@ gemm_mfma_kernel(const GemmArgs p) {
       __syncthreads();
       if (kt + 2 < KT) {
         const int k0 = (kt + 2) * Cfg::BK;
-        sa.load(Ap, p.lda, m0, p.M, k0, p.K, tid, p.a_elem);
-        sb.load(Bp, p.ldb, n0, p.N, k0, p.K, tid, p.b_elem);
+        sa.load(Ap, p.lda, m0, p.M, k0, p.K, tid, p.a_vw);
+        sb.load(Bp, p.ldb, n0, p.N, k0, p.K, tid, p.b_vw);
       }
       read_frags<Cfg>(nxt, nA, nA + Cfg::A_BYTES, a_row0, b_row0, koct);
     }

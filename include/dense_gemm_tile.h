@@ -78,9 +78,10 @@ extern "C" {
  * stream    hipStream_t cast to void*.
  *
  * Path: every call runs on the matrix cores. An operand whose base address or
- * row pitch is not a multiple of 16 bytes is staged 16 bits at a time by the
- * masked kernel (slower, same result up to rounding order); the VALU FMA path
- * computes the same contraction with f32 FMAs and runs only when forced.
+ * row pitch is not a multiple of 16 bytes is read by the masked kernel with
+ * the widest loads both allow (8, 4 or 2 bytes; slower, same result up to
+ * rounding order); the VALU FMA path computes the same contraction with f32
+ * FMAs and runs only when forced.
  *
  * Environment: GEMM_LOG=debug prints one line per call to stderr (path, tile,
  * reason); GEMM_FORCE_PATH=mfma|fma forces the matrix-core or the VALU path;
@@ -108,8 +109,8 @@ GEMM_API const char* gemm_last_error(void);
 
 /* Path of the last gemm()/gemm_validate() on this thread, e.g.
  * "mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 pingpong",
- * "mfma t128x128x64 w2x2 a32x32x16 TN epi=general masked 16-bit staging
- * (A row pitch 8194 B is not a multiple of 16 B)" or
+ * "mfma t128x128x64 w2x2 a32x32x16 TN epi=general masked narrow staging
+ * (A: 2-byte loads, row pitch 8194 B is not a multiple of 16 B)" or
  * "fma t64x64x16 NN epi=beta0: forced by GEMM_FORCE_PATH=fma". Same lifetime
  * as above. */
 GEMM_API const char* gemm_last_path(void);

@@ -112,25 +112,33 @@ def test_empty_and_degenerate_calls(lib):
     assert _v(lib, K=0, A=0, B=0, beta=0.0, C=0, lda=1) == lib.GEMM_OK
 
 
-def test_unaligned_pitch_stays_on_mfma_with_16bit_staging(lib):
+def test_unaligned_pitch_stays_on_mfma_with_narrow_staging(lib):
     # transposed f16 A with lda = 4097: an 8194-byte row pitch
     st = _v(lib, M=4097, N=1000, K=1032, tA=1, lda=4097, alpha=2.0, beta=-1.0)
     assert st == lib.GEMM_OK
     path = lib.gemm_last_path()
     assert path.startswith("mfma t128x128x64") and " masked " in path, path
-    assert path.endswith("16-bit staging (A row pitch 8194 B is not a multiple of 16 B)"), path
+    assert path.endswith(
+        "narrow staging (A: 2-byte loads, row pitch 8194 B is not a multiple of 16 B)"), path
     assert _v(lib, A=A0 + 2) == lib.GEMM_OK
     path = lib.gemm_last_path()
-    assert path.startswith("mfma ") and "A base address is not 16-byte aligned" in path, path
+    assert path.startswith("mfma ") and "A: 2-byte loads, base address is not 16-byte aligned" in path
+    assert _v(lib, A=A0 + 8) == lib.GEMM_OK
+    assert "A: 8-byte loads, base address" in lib.gemm_last_path()
     assert _v(lib, ldb=72) == lib.GEMM_OK
-    assert "16-bit staging" not in lib.gemm_last_path()  # 144-byte pitch is fine
+    assert "narrow staging" not in lib.gemm_last_path()  # 144-byte pitch is fine
     assert _v(lib, ldb=67) == lib.GEMM_OK
-    assert "16-bit staging (B row pitch 134 B" in lib.gemm_last_path()
+    assert "narrow staging (B: 2-byte loads, row pitch 134 B" in lib.gemm_last_path()
+    assert _v(lib, ldb=66) == lib.GEMM_OK
+    assert "(B: 4-byte loads, row pitch 132 B" in lib.gemm_last_path()
+    assert _v(lib, ldb=68) == lib.GEMM_OK
+    assert "(B: 8-byte loads, row pitch 136 B" in lib.gemm_last_path()
     assert _v(lib, lda=67, ldb=67, M=64, N=64, K=64) == lib.GEMM_OK
-    assert "(A row pitch 134 B is not a multiple of 16 B; B row pitch 134 B" in lib.gemm_last_path()
+    assert ("(A: 2-byte loads, row pitch 134 B is not a multiple of 16 B; "
+            "B: 2-byte loads, row pitch 134 B") in lib.gemm_last_path()
     # whole tiles with an unaligned operand still take the masked kernel
     assert _v(lib, M=8192, N=8192, K=8192, tB=1, dtype=1, ldb=8193) == lib.GEMM_OK
-    assert " masked 16-bit staging (B " in lib.gemm_last_path(), lib.gemm_last_path()
+    assert " masked narrow staging (B: 2-byte" in lib.gemm_last_path(), lib.gemm_last_path()
 
 
 def test_ragged_dims_stay_on_mfma_masked(lib):
@@ -187,7 +195,7 @@ def test_debug_log_names_the_path_and_its_reason():
     assert r.returncode == 0, r.stderr
     lines = [l for l in r.stderr.splitlines() if l.startswith("[gemm]")]
     assert len(lines) == 2
-    assert "M=4097 N=1000 K=1032 -> mfma " in lines[0] and "A row pitch 8194 B" in lines[0]
+    assert "M=4097 N=1000 K=1032 -> mfma " in lines[0] and "row pitch 8194 B" in lines[0]
     assert "error 1: negative dimension" in lines[1]
 
 

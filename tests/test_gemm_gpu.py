@@ -39,7 +39,7 @@ def test_workload_parity_full(name):
     r.check_padding_untouched()
     assert r.path.startswith("mfma "), r.path
     if name == "ragged4097x1000x1032_tn":
-        assert "16-bit staging (A row pitch 8194 B" in r.path, r.path
+        assert "narrow staging (A: 2-byte loads, row pitch 8194 B" in r.path, r.path
 
 
 @pytest.mark.parametrize("name", ["gemm4096_inplace", "gemm8192_nt"])
@@ -110,28 +110,40 @@ def test_tiled_shapes(tile, dtype, monkeypatch):
                 r.check_padding_untouched()
 
 
+def _ld_with_width(x, vw):
+    """Smallest leading dimension >= x whose 2-byte row pitch allows loads of
+    exactly vw elements (8: 16-byte aligned, 4: 8-byte, 2: 4-byte, 1: 2-byte)."""
+    ld = x
+    while True:
+        w = 8
+        while w > 1 and (ld * 2) % (2 * w):
+            w //= 2
+        if w == vw:
+            return ld
+        ld += 1
+
+
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_tiled_shapes_16bit_staging(tile, dtype, monkeypatch):
+def test_tiled_shapes_narrow_staging(tile, dtype, monkeypatch):
     """Operands whose row pitch or base address is not a multiple of 16 bytes
-    stay on the matrix cores, staged element by element: odd pitches, bases
-    2 bytes past a 16-byte boundary, one or both operands, every layout."""
+    stay on the matrix cores, read with 8-, 4- or 2-byte loads: pitches of
+    each width, bases 4 or 2 bytes past a 16-byte boundary, one or both
+    operands, every layout."""
     monkeypatch.setenv("GEMM_FORCE_TILE", tile)
     seed = 5000
-    def odd(x):  # a leading dimension whose pitch is not a multiple of 16 bytes
-        return x + 1 if (x + 1) % 8 else x + 3
-
+    # (A width, B width, A offset, B offset in elements)
+    modes = [(1, 8, 0, 1), (8, 4, 0, 0), (2, 1, 0, 0), (4, 2, 2, 0)]
     for (M, N, K) in SHAPES[1::2] + [(512, 512, 192)]:
         for tA, tB in [(0, 0), (0, 1), (1, 0), (1, 1)]:
             seed += 1
-            mode = seed % 4
-            lda = odd(M if tA else K) if mode in (0, 2) else (M if tA else K) + 8
-            ldb = odd(K if tB else N) if mode in (1, 2) else _pad8(K if tB else N)
-            a_off, b_off = (1, 0) if mode == 3 else (0, 1 if mode == 0 else 0)
-            cfg = workloads.Config(f"elem{seed}", M, N, K, dtype, tA, tB, 1.5, -0.5,
+            wa, wb, a_off, b_off = modes[seed % 4]
+            lda = _ld_with_width(M if tA else K, wa)
+            ldb = _ld_with_width(K if tB else N, wb)
+            cfg = workloads.Config(f"narrow{seed}", M, N, K, dtype, tA, tB, 1.5, -0.5,
                                    "uniform", seed, lda=lda, ldb=ldb)
             r = run(cfg, a_off=a_off, b_off=b_off)
-            assert r.path.startswith("mfma " + tile) and "16-bit staging (" in r.path, r.path
+            assert r.path.startswith("mfma " + tile) and "narrow staging (" in r.path, r.path
             r.check()
             r.check_padding_untouched()
 
