@@ -253,9 +253,13 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   // Whole 256x256 tiles (any operand layout) take the kernel with two wave
   // groups (2x4 waves) and direct global->LDS loads.
   const bool pingpong = tile == TILE_256x256 && !plan.masked;
-  std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s", ti.name,
+  // A last K step whose valid part ends within the first half of a 16x16x32
+  // sub-step finishes with v_mfma_f32_16x16x16 (no product of staged zeros).
+  const bool k16_tail = ti.atom_k == 32 && K % 32 >= 1 && K % 32 <= 16;
+  std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s", ti.name,
                 ti.waves_m, pingpong ? 4 : ti.waves_n, ti.atom_m, ti.atom_n, ti.atom_k, ops,
                 epi_name, pingpong ? " pingpong" : "", plan.masked ? " masked" : "",
+                k16_tail ? " k16-tail" : "",
                 elem_reason.empty() ? "" : " narrow staging (", elem_reason.c_str(),
                 elem_reason.empty() ? "" : ")");
   g_path = buf;

@@ -34,6 +34,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -73,6 +75,16 @@ template <>
 struct Atom<16> {  // v_mfma_f32_16x16x32_*: 4 f32 accumulators per lane
   static constexpr int M = 16, N = 16, K = 32, NACC = 4;
   using acc_t = f32x4;
+  // v_mfma_f32_16x16x16_*: the same rows, columns and accumulator layout over
+  // 16 K-values; lane l holds 4 consecutive K-values starting at 4*(l >> 4).
+  __device__ static inline acc_t mma16(TagF16, u32x2 a, u32x2 b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+  __device__ static inline acc_t mma16(TagBF16, u32x2 a, u32x2 b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  }
   __device__ static inline int frag_row(int l) { return l & 15; }
   __device__ static inline int frag_koct(int l) { return l >> 4; }
   __device__ static inline int acc_row(int l, int v) { return 4 * (l >> 4) + v; }
@@ -282,6 +294,45 @@ __device__ inline void mma_step(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::TN]
     for (int j = 0; j < Cfg::TN; ++j) acc[i][j] = At::mma(Tag{}, f.a[i], f.b[j], acc[i][j]);
 }
 
+// The last K step of a masked tile: only the sub-steps that hold valid
+// K-values (krem of them, 1..BK) run. With 16x16x32 atoms, a sub-step whose
+// valid part is at most 16 K-values runs as v_mfma_f32_16x16x16 on its first
+// half instead of multiplying 16 staged zeros. `cur` holds sub-step 0.
+template <class Cfg, class Tag>
+__device__ inline void k_tail(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::TN], Frags<Cfg>& cur,
+                              const char* As, const char* Bs, int a_row0, int b_row0, int lane,
+                              int krem) {
+  using At = typename Cfg::At;
+  constexpr int CPS = At::K / 8;
+  const int koct = At::frag_koct(lane);
+#pragma unroll
+  for (int ks = 0; ks < Cfg::KSTEPS; ++ks) {
+    const int lo = ks * At::K;
+    if (lo >= krem) break;
+    if (ks > 0) read_frags<Cfg>(cur, As, Bs, a_row0, b_row0, ks * CPS + koct);
+    if constexpr (At::K == 32) {
+      if (krem - lo <= 16) {
+        // lane l: 4 K-values at lo + 4*(l >> 4), i.e. 8 bytes into chunk
+        // lo/8 + (l >> 5) at byte 8*((l >> 4) & 1)
+        const int chunk = lo / 8 + (lane >> 5), byte = 8 * ((lane >> 4) & 1);
+        u32x2 a2[Cfg::TM], b2[Cfg::TN];
+#pragma unroll
+        for (int i = 0; i < Cfg::TM; ++i)
+          a2[i] = *reinterpret_cast<const u32x2*>(As + lds_off(a_row0 + i * At::M, chunk) + byte);
+#pragma unroll
+        for (int j = 0; j < Cfg::TN; ++j)
+          b2[j] = *reinterpret_cast<const u32x2*>(Bs + lds_off(b_row0 + j * At::N, chunk) + byte);
+#pragma unroll
+        for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+          for (int j = 0; j < Cfg::TN; ++j) acc[i][j] = At::mma16(Tag{}, a2[i], b2[j], acc[i][j]);
+        continue;
+      }
+    }
+    mma_step<Cfg, Tag>(acc, cur);
+  }
+}
+
 // -------------------------------------------------------------- epilogue ----
 // Transpose a 4x4 block held by a quad of lanes (lane k of the quad holds
 // x[0..3]) so that lane k ends up with element k of every lane's x: two
@@ -432,6 +483,12 @@ gemm_mfma_kernel(const GemmArgs p) {
   for (int kt = 0; kt < KT; ++kt) {
     const char* As = smem + (kt & 1) * Cfg::STAGE_BYTES;
     const char* Bs = As + Cfg::A_BYTES;
+    if constexpr (MASK) {
+      if (kt == KT - 1) {
+        k_tail<Cfg, Tag>(acc, cur, As, Bs, a_row0, b_row0, lane, p.K - kt * Cfg::BK);
+        break;
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < Cfg::KSTEPS - 1; ++ks) {
       read_frags<Cfg>(nxt, As, Bs, a_row0, b_row0, (ks + 1) * CPS + koct);

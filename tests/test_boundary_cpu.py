@@ -149,6 +149,18 @@ def test_ragged_dims_stay_on_mfma_masked(lib):
     assert lib.gemm_last_path().startswith("mfma t16x16x64"), lib.gemm_last_path()
 
 
+def test_k16_tail_is_named(lib):
+    # 16x16x32 atoms (t16, t64): a last K step with 1..16 valid K-values
+    assert _v(lib, M=16, N=8, K=16) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith("masked k16-tail"), lib.gemm_last_path()
+    for K, tail in [(48, True), (40, True), (33, True), (56, False), (64, False), (1, True)]:
+        assert _v(lib, M=200, N=200, K=K, lda=64, ldb=200) == lib.GEMM_OK
+        assert ("k16-tail" in lib.gemm_last_path()) == tail, (K, lib.gemm_last_path())
+    # 32x32x16 atoms skip empty sub-steps but have no half-width atom
+    assert _v(lib, M=4096, N=4096, K=48, lda=64, ldb=4096) == lib.GEMM_OK
+    assert "k16-tail" not in lib.gemm_last_path()
+
+
 def test_huge_pitch_takes_64bit_addressing(lib):
     # 64 rows (the 64x64 tile) of a 16M-element pitch overflow 32-bit offsets
     assert _v(lib, M=256, N=256, K=256, lda=1 << 24, A=1 << 40) == lib.GEMM_OK

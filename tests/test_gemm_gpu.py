@@ -218,6 +218,38 @@ def test_exact_permutations_pin_lane_ownership(path, tA, tB, monkeypatch):
         _exact_case("bf16", tA, tB, M, N, K, X, I, path)
 
 
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_exact_k_tails(tile, dtype, monkeypatch):
+    """The last K step runs only the sub-steps holding valid K-values; with
+    16x16x32 atoms a valid part of at most 16 finishes on 16x16x16. Integer
+    inputs make every order exact, so the result must match bitwise."""
+    monkeypatch.setenv("GEMM_FORCE_TILE", tile)
+    rng = np.random.default_rng(21)
+    atom16 = tile in ("t16x16x64", "t64x64x64")
+    for K in (1, 8, 16, 17, 24, 32, 40, 48, 56, 63, 80, 112):
+        for tA, tB in [(0, 0), (1, 1)] if K % 2 else [(0, 1), (1, 0)]:
+            M, N = 48, 40
+            A = rng.integers(-2, 3, (M, K)).astype(np.float32)
+            B = rng.integers(-2, 3, (K, N)).astype(np.float32)
+            As = A.T if tA else A
+            Bs = B.T if tB else B
+            lda = (As.shape[1] + 7) // 8 * 8
+            ldb = (Bs.shape[1] + 7) // 8 * 8
+            cfg = workloads.Config(f"ktail{K}", M, N, K, dtype, tA, tB, 1.0, 0.0, "uniform", 1,
+                                   lda=lda, ldb=ldb)
+            Ap = np.zeros((As.shape[0], lda), np.float32)
+            Ap[:, :As.shape[1]] = As
+            Bp = np.zeros((Bs.shape[0], ldb), np.float32)
+            Bp[:, :Bs.shape[1]] = Bs
+            inp = workloads.make_inputs(cfg, A_src=torch.tensor(Ap), B_src=torch.tensor(Bp))
+            r = run(cfg, inp)
+            assert r.path.startswith("mfma " + tile), r.path
+            assert (" k16-tail" in r.path) == (atom16 and 1 <= K % 32 <= 16), r.path
+            got = r.D[:, :N].numpy()
+            assert np.array_equal(got, (A @ B).astype(np.float32)), (K, tA, tB)
+
+
 def test_exact_ones_closed_form():
     M, N, K = 300, 200, 2048
     cfg = workloads.Config("ones", M, N, K, "bf16", 0, 1, 1.0, 0.0, "uniform", 1)
