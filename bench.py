@@ -27,7 +27,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}  # MI355X dense MFMA, published
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0,  # MI355X dense MFMA, published
+               "f32_bf16": 2500.0, "f32_f16": 2500.0}  # rounded operands run on the same cores
 PEAK_HBM_GBS = 8000.0
 COPY_CAL_BYTES = 1 << 30
 DIST_TEXT = {"uniform": "uniform[-1, 1]", "normal": "normal(0, 1)",
@@ -83,16 +84,22 @@ def cpu_baseline(cfg, inp, seconds: float):
     import workloads
 
     lda, ldb, ldc, _ = cfg.lds()
-    A = workloads.bits_u16(inp.A).reshape(-1)
-    B = workloads.bits_u16(inp.B).reshape(-1)
     C = inp.C.numpy().reshape(-1) if inp.C is not None else None
-    dt = workloads.DTYPE_CODE[cfg.dtype]
+    if cfg.dtype.startswith("f32_"):  # float32 operands, rounded by the oracle itself
+        ref = oracle.gemm_reference_f32
+        dt = 0 if cfg.dtype == "f32_f16" else 1
+        A, B = inp.A.numpy().reshape(-1), inp.B.numpy().reshape(-1)
+    else:
+        ref = oracle.gemm_reference
+        dt = workloads.DTYPE_CODE[cfg.dtype]
+        A = workloads.bits_u16(inp.A).reshape(-1)
+        B = workloads.bits_u16(inp.B).reshape(-1)
 
     def timed(nrows):
         rows = np.arange(nrows)
         t0 = time.perf_counter()
-        oracle.gemm_reference(cfg.M, cfg.N, cfg.K, dt, cfg.transA, cfg.transB, cfg.alpha,
-                              cfg.beta, A, lda, B, ldb, C, ldc, rows=rows, with_bound=False)
+        ref(cfg.M, cfg.N, cfg.K, dt, cfg.transA, cfg.transB, cfg.alpha, cfg.beta, A, lda, B, ldb,
+            C, ldc, rows=rows, with_bound=False)
         return time.perf_counter() - t0
 
     # Two short probes give a fixed cost (operand decode) and a per-row cost;
@@ -154,7 +161,7 @@ def main():
     import dense_gemm_tile_amd as dgt
     import workloads
 
-    cfg = workloads.CONFIGS[args.workload]
+    cfg = {**workloads.CONFIGS, **workloads.EXTRA_CONFIGS}[args.workload]
     lda, ldb, ldc, ldd = cfg.lds()
     inp = workloads.make_inputs(cfg)
     dev = torch.device("cuda:0")
@@ -200,11 +207,17 @@ def main():
         torch.cuda.synchronize()
         rng = np.random.default_rng(0)
         rows = np.unique(np.concatenate([[0, cfg.M - 1], rng.integers(0, cfg.M, 14)]))
-        D_ref, bound = oracle.gemm_reference(
-            cfg.M, cfg.N, cfg.K, workloads.DTYPE_CODE[cfg.dtype], cfg.transA, cfg.transB,
-            cfg.alpha, cfg.beta, workloads.bits_u16(inp.A).reshape(-1), lda,
-            workloads.bits_u16(inp.B).reshape(-1), ldb,
-            inp.C.numpy().reshape(-1) if inp.C is not None else None, ldc, rows=rows)
+        Cn = inp.C.numpy().reshape(-1) if inp.C is not None else None
+        if cfg.dtype.startswith("f32_"):
+            D_ref, bound = oracle.gemm_reference_f32(
+                cfg.M, cfg.N, cfg.K, 0 if cfg.dtype == "f32_f16" else 1, cfg.transA, cfg.transB,
+                cfg.alpha, cfg.beta, inp.A.numpy().reshape(-1), lda, inp.B.numpy().reshape(-1),
+                ldb, Cn, ldc, rows=rows)
+        else:
+            D_ref, bound = oracle.gemm_reference(
+                cfg.M, cfg.N, cfg.K, workloads.DTYPE_CODE[cfg.dtype], cfg.transA, cfg.transB,
+                cfg.alpha, cfg.beta, workloads.bits_u16(inp.A).reshape(-1), lda,
+                workloads.bits_u16(inp.B).reshape(-1), ldb, Cn, ldc, rows=rows)
         got = D[rows, : cfg.N].cpu().numpy().astype(np.float64)
         rep = oracle.check(got, D_ref, bound)
         if not rep["ok"]:
@@ -217,7 +230,8 @@ def main():
     peak = PEAK_TFLOPS[cfg.dtype]
     traffic = stored_traffic(cfg.name)
     # Algorithmic bytes: A and B once (16-bit), C once when beta != 0, D once.
-    alg_bytes = 2.0 * (cfg.M * cfg.K + cfg.K * cfg.N) + 4.0 * cfg.M * cfg.N * (2 if cfg.beta != 0 else 1)
+    esz = 4.0 if cfg.dtype.startswith("f32_") else 2.0
+    alg_bytes = esz * (cfg.M * cfg.K + cfg.K * cfg.N) + 4.0 * cfg.M * cfg.N * (2 if cfg.beta != 0 else 1)
     if flops / alg_bytes >= (peak * 1e12) / (PEAK_HBM_GBS * 1e9):
         roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(tflops / peak, 4), "traffic": traffic}

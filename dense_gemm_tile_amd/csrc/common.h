@@ -24,6 +24,10 @@ struct GemmArgs {
   int a_vw;      // staging vector width of A in 16-bit elements (8, 4, 2 or 1):
   int b_vw;      //    the widest whose byte size divides A's base and row pitch
                  //    (same for B); below 8 only the masked kernel runs
+  int src32;     // 0: A and B hold 16-bit values; 1 / 2: A and B hold float32
+                 //    values, rounded to f16 / bf16 (nearest, ties to even) as
+                 //    they are staged (masked kernel only); a_vw, b_vw then
+                 //    count float32 elements (4, 2 or 1)
 };
 
 // Epilogue kinds. All three compute alpha*acc + beta*C; the specialised ones

@@ -57,22 +57,22 @@ bool overlaps(const void* p, unsigned __int128 np, const void* q, unsigned __int
   return a < b + nq && b < a + np;
 }
 
-// Widest staging vector (in 16-bit elements: 8, 4, 2 or 1) whose byte size
-// divides both the operand's base address and its row pitch.
-int vector_width(const void* ptr, int64_t ld) {
-  int vw = 8;
-  while (vw > 1 && ((uintptr_t)ptr % (2 * vw) != 0 || (ld * 2) % (2 * vw) != 0)) vw /= 2;
+// Widest staging load (in elements of esz bytes, at most 16 bytes) whose byte
+// size divides both the operand's base address and its row pitch.
+int vector_width(const void* ptr, int64_t ld, int esz) {
+  int vw = 16 / esz;
+  while (vw > 1 && ((uintptr_t)ptr % (esz * vw) != 0 || (ld * esz) % (esz * vw) != 0)) vw /= 2;
   return vw;
 }
 
-std::string pitch_reason(const char* name, const void* ptr, int64_t ld, int vw) {
+std::string pitch_reason(const char* name, const void* ptr, int64_t ld, int vw, int esz) {
   char buf[160];
   if ((uintptr_t)ptr % 16 != 0) {
     std::snprintf(buf, sizeof buf, "%s: %d-byte loads, base address is not 16-byte aligned",
-                  name, 2 * vw);
+                  name, esz * vw);
   } else {
     std::snprintf(buf, sizeof buf, "%s: %d-byte loads, row pitch %lld B is not a multiple of 16 B",
-                  name, 2 * vw, (long long)(ld * 2));
+                  name, esz * vw, (long long)(ld * esz));
   }
   return buf;
 }
@@ -101,10 +101,14 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
                   (long long)N, (long long)K);
     return fail(GEMM_ERR_INVALID_ARG, buf);
   }
-  if (dtype != GEMM_DTYPE_F16 && dtype != GEMM_DTYPE_BF16) {
-    std::snprintf(buf, sizeof buf, "dtype code %d is neither f16 (0) nor bf16 (1)", dtype);
+  if (dtype < GEMM_DTYPE_F16 || dtype > GEMM_DTYPE_F32_BF16) {
+    std::snprintf(buf, sizeof buf,
+                  "dtype code %d is none of f16 (0), bf16 (1), f32->f16 (2), f32->bf16 (3)", dtype);
     return fail(GEMM_ERR_UNSUPPORTED, buf);
   }
+  // f32 operands are rounded to the 16-bit type as they are staged.
+  const bool src32 = dtype >= GEMM_DTYPE_F32_F16;
+  const int esz = src32 ? 4 : 2;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) {
     return fail(GEMM_ERR_UNSUPPORTED, "a dimension exceeds 2^31-1024");
   }
@@ -141,8 +145,8 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   if (reads_c && !C) return fail(GEMM_ERR_INVALID_ARG, "C is NULL but beta != 0");
   if (reads_c && (uintptr_t)C % 4) return fail(GEMM_ERR_INVALID_ARG, "C is not 4-byte aligned");
   if (reads_ab && (!A || !B)) return fail(GEMM_ERR_INVALID_ARG, "A or B is NULL");
-  if (reads_ab && ((uintptr_t)A % 2 || (uintptr_t)B % 2))
-    return fail(GEMM_ERR_INVALID_ARG, "A or B is not 2-byte aligned");
+  if (reads_ab && ((uintptr_t)A % esz || (uintptr_t)B % esz))
+    return fail(GEMM_ERR_INVALID_ARG, src32 ? "A or B is not 4-byte aligned" : "A or B is not 2-byte aligned");
 
   // Aliasing: D is written, so it must not overlap anything it is computed
   // from, except C itself in the exact in-place form.
@@ -156,9 +160,9 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   }
   if (reads_ab) {
     const unsigned __int128 a_ext =
-        extent_bytes(transA ? K : M, transA ? M : K, lda, 2);
+        extent_bytes(transA ? K : M, transA ? M : K, lda, esz);
     const unsigned __int128 b_ext =
-        extent_bytes(transB ? N : K, transB ? K : N, ldb, 2);
+        extent_bytes(transB ? N : K, transB ? K : N, ldb, esz);
     if (overlaps(A, a_ext, D, d_ext)) return fail(GEMM_ERR_ALIAS, "D overlaps A");
     if (overlaps(B, b_ext, D, d_ext)) return fail(GEMM_ERR_ALIAS, "D overlaps B");
   }
@@ -197,14 +201,16 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   // operand whose base or row pitch is not a multiple of 16 bytes is read with
   // the widest loads they allow (8, 4 or 2 bytes, masked kernel), so every
   // f16/bf16 call runs on the matrix cores unless the VALU path is forced.
-  const int a_vw = vector_width(A, lda), b_vw = vector_width(B, ldb);
-  const bool a_elem = a_vw < 8, b_elem = b_vw < 8;
+  const int a_vw = vector_width(A, lda, esz), b_vw = vector_width(B, ldb, esz);
+  const bool a_elem = a_vw * esz < 16, b_elem = b_vw * esz < 16;
   std::string elem_reason;
-  if (a_elem) elem_reason = pitch_reason("A", A, lda, a_vw);
-  if (b_elem) elem_reason += (a_elem ? "; " : "") + pitch_reason("B", B, ldb, b_vw);
+  if (a_elem) elem_reason = pitch_reason("A", A, lda, a_vw, esz);
+  if (b_elem) elem_reason += (a_elem ? "; " : "") + pitch_reason("B", B, ldb, b_vw, esz);
   std::string decline;
   const char* force = env("GEMM_FORCE_PATH");
   if (force && std::strcmp(force, "fma") == 0) {
+    if (src32)
+      return fail(GEMM_ERR_UNSUPPORTED, "GEMM_FORCE_PATH=fma has no f32-operand form");
     decline = "forced by GEMM_FORCE_PATH=fma";
   } else if (force && std::strcmp(force, "mfma") != 0) {
     return fail(GEMM_ERR_INVALID_ARG, std::string("GEMM_FORCE_PATH must be mfma or fma, got ") + force);
@@ -241,11 +247,12 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     const int64_t rows = ti.bm > ti.bn ? (ti.bm > ti.bk ? ti.bm : ti.bk)
                                        : (ti.bn > ti.bk ? ti.bn : ti.bk);
     const int64_t ldmax = lda > ldb ? lda : ldb;
-    if (ldmax * 2 * rows + 4096 >= (int64_t{1} << 31)) plan.masked = true;
+    if (ldmax * esz * rows + 4096 >= (int64_t{1} << 31)) plan.masked = true;
   }
   a.a_vw = a_vw;
   a.b_vw = b_vw;
-  if (a_elem || b_elem) plan.masked = true;
+  a.src32 = src32 ? (dtype == GEMM_DTYPE_F32_BF16 ? 2 : 1) : 0;
+  if (a_elem || b_elem || src32) plan.masked = true;
   a.tiles_m = (int)((M + ti.bm - 1) / ti.bm);
   a.tiles_n = (int)((N + ti.bn - 1) / ti.bn);
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7fffffff)
@@ -256,10 +263,11 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   // A last K step whose valid part ends within the first half of a 16x16x32
   // sub-step finishes with v_mfma_f32_16x16x16 (no product of staged zeros).
   const bool k16_tail = ti.atom_k == 32 && K % 32 >= 1 && K % 32 <= 16;
-  std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s", ti.name,
+  std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s%s", ti.name,
                 ti.waves_m, pingpong ? 4 : ti.waves_n, ti.atom_m, ti.atom_n, ti.atom_k, ops,
                 epi_name, pingpong ? " pingpong" : "", plan.masked ? " masked" : "",
                 k16_tail ? " k16-tail" : "",
+                !src32 ? "" : dtype == GEMM_DTYPE_F32_BF16 ? " f32->bf16" : " f32->f16",
                 elem_reason.empty() ? "" : " narrow staging (", elem_reason.c_str(),
                 elem_reason.empty() ? "" : ")");
   g_path = buf;
@@ -294,7 +302,7 @@ int gemm(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB, flo
     hipError_t e;
     if (plan.scale_only) e = launch_scale_c(plan.args, s);
     else if (plan.mfma)
-      e = launch_mfma(plan.tile, dtype, transA != 0, transB != 0, plan.masked, plan.args, s);
+      e = launch_mfma(plan.tile, dtype & 1, transA != 0, transB != 0, plan.masked, plan.args, s);
     else e = launch_fma(dtype, transA != 0, transB != 0, plan.args, s);
     if (e != hipSuccess)
       st = fail(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));

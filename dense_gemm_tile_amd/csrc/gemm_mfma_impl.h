@@ -168,12 +168,55 @@ struct Stager {
     return load_partial(p, 8);
   }
 
+  // Rounding of one float32 value to a 16-bit pattern, to nearest with ties
+  // to even: mode 1 gives f16 (the hardware conversion, which rounds so in
+  // the default mode), mode 2 bf16 (on the bit pattern; NaN stays a quiet NaN).
+  __device__ static inline unsigned round16(float x, int mode) {
+    if (mode == 1) return __builtin_bit_cast(unsigned short, (_Float16)x);
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  }
+  __device__ static inline u32x4 round8(const float (&f)[8], int mode) {
+    u32x4 r;
+    r.x = round16(f[0], mode) | (round16(f[1], mode) << 16);
+    r.y = round16(f[2], mode) | (round16(f[3], mode) << 16);
+    r.z = round16(f[4], mode) | (round16(f[5], mode) << 16);
+    r.w = round16(f[6], mode) | (round16(f[7], mode) << 16);
+    return r;
+  }
+  // n_valid (0..8) float32 values of a piece, vw-element loads when whole.
+  __device__ static inline u32x4 load_f32(const float* q, int n_valid, int vw, int mode) {
+    float f[8];
+    if (n_valid == 8 && vw == 4) {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(q);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(q + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = lo[e], f[e + 4] = hi[e];
+    } else if (n_valid == 8 && vw == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 t = *reinterpret_cast<const float2*>(q + 2 * e);
+        f[2 * e] = t.x;
+        f[2 * e + 1] = t.y;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = e < n_valid ? q[e] : 0.0f;
+    }
+    return round8(f, mode);
+  }
+
   // Issue the global loads of the box at (r0, k0). rlim / klim: number of
   // valid rows / K-values of the whole operand (used only when MASK). vw
-  // (MASK only): the operand's staging vector width in elements; below 8 its
-  // 16-byte pieces are not 16-byte aligned and are read in narrower loads.
-  __device__ inline void load(const uint16_t* __restrict__ X, int64_t ld, int r0, int rlim,
-                              int k0, int klim, int tid, int vw = 8) {
+  // (MASK only): the operand's staging vector width in elements; below 16
+  // bytes its pieces are not 16-byte aligned and are read in narrower loads.
+  // src32 (MASK only): 0 for 16-bit operands; 1 / 2 for float32 operands
+  // rounded to f16 / bf16 here.
+  __device__ inline void load(const void* __restrict__ Xv, int64_t ld, int r0, int rlim, int k0,
+                              int klim, int tid, int vw = 8, int src32 = 0) {
+    const uint16_t* __restrict__ X = static_cast<const uint16_t*>(Xv);
+    const float* __restrict__ X32 = static_cast<const float*>(Xv);
     if constexpr (!MASK) {
       if constexpr (KCONTIG) {
         const auto rs = make_rsrc(X + (int64_t)r0 * ld + k0);
@@ -197,8 +240,11 @@ struct Stager {
         const int id = tid + i * THREADS;
         const int r = r0 + (id >> 3);
         const int k = k0 + ((id & 7) << 3);
-        const uint16_t* p = X + (int64_t)r * ld + k;
-        if (r < rlim && k + 8 <= klim) {
+        const int64_t off = (int64_t)r * ld + k;
+        const uint16_t* p = X + off;
+        if (r < rlim && k < klim && src32) {
+          v[i] = load_f32(X32 + off, klim - k < 8 ? klim - k : 8, vw, src32);
+        } else if (r < rlim && k + 8 <= klim) {
           v[i] = vw == 8 ? *reinterpret_cast<const u32x4*>(p) : load_narrow(p, vw);
         } else if (r < rlim && k < klim) {
           v[i] = load_partial(p, klim - k < 8 ? klim - k : 8);
@@ -213,8 +259,11 @@ struct Stager {
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
         const int k = k0 + kb * NL + j;
-        const uint16_t* p = X + (int64_t)k * ld + r;
-        if (k < klim && r + 8 <= rlim) {
+        const int64_t off = (int64_t)k * ld + r;
+        const uint16_t* p = X + off;
+        if (k < klim && r < rlim && src32) {
+          v[j] = load_f32(X32 + off, rlim - r < 8 ? rlim - r : 8, vw, src32);
+        } else if (k < klim && r + 8 <= rlim) {
           v[j] = vw == 8 ? *reinterpret_cast<const u32x4*>(p) : load_narrow(p, vw);
         } else if (k < klim && r < rlim) {
           v[j] = load_partial(p, rlim - r < 8 ? rlim - r : 8);
@@ -294,8 +343,8 @@ __device__ inline void mma_step(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::TN]
     for (int j = 0; j < Cfg::TN; ++j) acc[i][j] = At::mma(Tag{}, f.a[i], f.b[j], acc[i][j]);
 }
 
-// The last K step of a masked tile: only the sub-steps that hold valid
-// K-values (krem of them, 1..BK) run. With 16x16x32 atoms, a sub-step whose
+// The last K step of a masked tile on 16x16x32 atoms: only the sub-steps
+// that hold valid K-values (krem of them, 1..BK) run, and a sub-step whose
 // valid part is at most 16 K-values runs as v_mfma_f32_16x16x16 on its first
 // half instead of multiplying 16 staged zeros. `cur` holds sub-step 0.
 template <class Cfg, class Tag>
@@ -450,8 +499,6 @@ gemm_mfma_kernel(const GemmArgs p) {
   // unless transposed; B is K-contiguous only when transposed.
   Stager<Cfg::BM, Cfg::THREADS, !TA, MASK> sa;
   Stager<Cfg::BN, Cfg::THREADS, TB, MASK> sb;
-  const uint16_t* Ap = static_cast<const uint16_t*>(p.A);
-  const uint16_t* Bp = static_cast<const uint16_t*>(p.B);
 
   acc_t acc[Cfg::TM][Cfg::TN];
 #pragma unroll
@@ -468,14 +515,14 @@ gemm_mfma_kernel(const GemmArgs p) {
   constexpr int CPS = At::K / 8;  // 16-byte chunks per K sub-step
 
   // Prologue: step 0 into buffer 0, step 1 into registers, first fragments.
-  sa.load(Ap, p.lda, m0, p.M, 0, p.K, tid, p.a_vw);
-  sb.load(Bp, p.ldb, n0, p.N, 0, p.K, tid, p.b_vw);
+  sa.load(p.A, p.lda, m0, p.M, 0, p.K, tid, p.a_vw, p.src32);
+  sb.load(p.B, p.ldb, n0, p.N, 0, p.K, tid, p.b_vw, p.src32);
   sa.store(smem, tid);
   sb.store(smem + Cfg::A_BYTES, tid);
   __syncthreads();
   if (KT > 1) {
-    sa.load(Ap, p.lda, m0, p.M, Cfg::BK, p.K, tid, p.a_vw);
-    sb.load(Bp, p.ldb, n0, p.N, Cfg::BK, p.K, tid, p.b_vw);
+    sa.load(p.A, p.lda, m0, p.M, Cfg::BK, p.K, tid, p.a_vw, p.src32);
+    sb.load(p.B, p.ldb, n0, p.N, Cfg::BK, p.K, tid, p.b_vw, p.src32);
   }
   Frags<Cfg> cur, nxt;
   read_frags<Cfg>(cur, smem, smem + Cfg::A_BYTES, a_row0, b_row0, koct);
@@ -483,7 +530,10 @@ gemm_mfma_kernel(const GemmArgs p) {
   for (int kt = 0; kt < KT; ++kt) {
     const char* As = smem + (kt & 1) * Cfg::STAGE_BYTES;
     const char* Bs = As + Cfg::A_BYTES;
-    if constexpr (MASK) {
+    // K tails on the 16x16x32 atom only: on the 32x32 atoms the tail saves
+    // little and the extra control flow around 256 accumulators makes the
+    // compiler spill them.
+    if constexpr (MASK && At::K == 32) {
       if (kt == KT - 1) {
         k_tail<Cfg, Tag>(acc, cur, As, Bs, a_row0, b_row0, lane, p.K - kt * Cfg::BK);
         break;
@@ -502,8 +552,8 @@ gemm_mfma_kernel(const GemmArgs p) {
       __syncthreads();
       if (kt + 2 < KT) {
         const int k0 = (kt + 2) * Cfg::BK;
-        sa.load(Ap, p.lda, m0, p.M, k0, p.K, tid, p.a_vw);
-        sb.load(Bp, p.ldb, n0, p.N, k0, p.K, tid, p.b_vw);
+        sa.load(p.A, p.lda, m0, p.M, k0, p.K, tid, p.a_vw, p.src32);
+        sb.load(p.B, p.ldb, n0, p.N, k0, p.K, tid, p.b_vw, p.src32);
       }
       read_frags<Cfg>(nxt, nA, nA + Cfg::A_BYTES, a_row0, b_row0, koct);
     }

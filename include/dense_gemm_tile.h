@@ -50,25 +50,36 @@ extern "C" {
  * which reports a failed launch) and sets gemm_last_error(). */
 #define GEMM_OK 0
 #define GEMM_ERR_INVALID_ARG 1 /* negative dim, ld too small, NULL or misaligned pointer */
-#define GEMM_ERR_UNSUPPORTED 2 /* dtype code not 0/1, or a forced path that cannot run */
+#define GEMM_ERR_UNSUPPORTED 2 /* dtype code not 0..3, or a forced path that cannot run */
 #define GEMM_ERR_ALIAS 3       /* D overlaps A or B, or overlaps C other than exactly */
 #define GEMM_ERR_HIP 4         /* a HIP runtime call failed; message has its text */
 
 /* Operand dtype codes (A and B share one; C and D are always float32). */
 #define GEMM_DTYPE_F16 0
 #define GEMM_DTYPE_BF16 1
+/* A and B hold float32 values that are rounded to f16 / bf16 (to nearest,
+ * ties to even) as they are staged; the product then runs on the f16 / bf16
+ * matrix cores with the float32 accumulator (Phobos @tensorcore, "The forms":
+ * float32 tensors traded to 16-bit inputs for matrix-core speed). Leading
+ * dimensions still count elements (now 4 bytes each). */
+#define GEMM_DTYPE_F32_F16 2
+#define GEMM_DTYPE_F32_BF16 3
 
 /*
  * gemm: enqueue D = alpha*op(A)@op(B) + beta*C on `stream`.
  *
  * M, N, K   >= 0. M == 0 or N == 0: nothing to do, returns GEMM_OK.
  *           K == 0 or alpha == 0: D = beta*C (A and B are not read).
- * dtype     GEMM_DTYPE_F16 or GEMM_DTYPE_BF16, the element type of A and B.
+ * dtype     GEMM_DTYPE_F16 or GEMM_DTYPE_BF16, the element type of A and B;
+ *           or GEMM_DTYPE_F32_F16 / GEMM_DTYPE_F32_BF16 for float32 A and B
+ *           rounded to f16 / bf16 while staged (matrix-core path only:
+ *           GEMM_FORCE_PATH=fma returns GEMM_ERR_UNSUPPORTED for them).
  * transA/B  0 or 1 (any non-zero means 1). transA: A is stored [K][M];
  *           transB: B is stored [N][K].
  * lda       >= max(1, transA ? M : K), in elements; ldb >= max(1, transB ? K : N);
  *           ldd >= max(1, N); ldc >= max(1, N) when beta != 0.
- * A, B      device pointers, 2-byte aligned; may be NULL only when K == 0 or
+ * A, B      device pointers, 2-byte aligned (4-byte for float32 operands); may
+ *           be NULL only when K == 0 or
  *           alpha == 0.
  * C         device float32 pointer, 4-byte aligned; ignored (may be NULL)
  *           when beta == 0.

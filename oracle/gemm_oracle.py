@@ -169,6 +169,20 @@ def gemm_reference(M, N, K, dtype, transA, transB, alpha, beta,
     return D, bound
 
 
+def gemm_reference_f32(M, N, K, dtype, transA, transB, alpha, beta,
+                       A_f32, lda, B_f32, ldb, C=None, ldc=None, **kw):
+    """D_ref and bound for float32 operands that are rounded to ``dtype``
+    (f16 or bf16, round-to-nearest-even) before the product: the Phobos
+    ``@tensorcore`` form where float32 tensors give up input precision to run
+    on the tensor cores ("The forms"). Element (i, k) of a stored operand is
+    rounded on its own, so rounding the whole stored buffer first is the same
+    computation; then the product is the plain definition above."""
+    A_bits = round_f32_bits(np.asarray(A_f32, dtype=np.float32).reshape(-1), dtype)
+    B_bits = round_f32_bits(np.asarray(B_f32, dtype=np.float32).reshape(-1), dtype)
+    return gemm_reference(M, N, K, dtype, transA, transB, alpha, beta, A_bits, lda, B_bits, ldb,
+                          C, ldc, **kw)
+
+
 def gemm_reference_elements(M, N, K, dtype, transA, transB, alpha, beta,
                             A_bits, lda, B_bits, ldb, C, ldc, I, J):
     """D_ref and bound at individual (I[t], J[t]) positions, one dot product each."""

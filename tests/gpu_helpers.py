@@ -32,7 +32,10 @@ def poison_padding(x: torch.Tensor, cols: int, dtype: str) -> torch.Tensor:
     """Fill the columns past `cols` of a padded [rows, ld] operand with NaNs."""
     x = x.clone()
     if x.shape[1] > cols:
-        x.view(torch.int16)[:, cols:] = int(np.uint16(NAN16[dtype]).view(np.int16))
+        if x.dtype == torch.float32:
+            x[:, cols:] = float("nan")
+        else:
+            x.view(torch.int16)[:, cols:] = int(np.uint16(NAN16[dtype]).view(np.int16))
     return x
 
 
@@ -52,6 +55,16 @@ class Run:
         return (c.M, c.N, c.K, dt, c.transA, c.transB, c.alpha, c.beta, A, lda, B, ldb, C, ldc)
 
     def reference(self, rows=None):
+        c = self.cfg
+        if c.dtype.startswith("f32_"):
+            # float32 operands: the oracle rounds them itself (f16 or bf16)
+            lda, ldb, ldc, _ = c.lds()
+            dt = 0 if c.dtype == "f32_f16" else 1
+            C = self.inp.C.numpy().reshape(-1) if self.inp.C is not None else None
+            return oracle.gemm_reference_f32(
+                c.M, c.N, c.K, dt, c.transA, c.transB, c.alpha, c.beta,
+                self.inp.A.numpy().reshape(-1), lda, self.inp.B.numpy().reshape(-1), ldb,
+                C, ldc, rows=rows)
         return oracle.gemm_reference(*self.oracle_args(), rows=rows)
 
     def check(self, rows=None):

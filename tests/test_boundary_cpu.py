@@ -70,7 +70,7 @@ def test_valid_call_selects_mfma(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(M=-1), 1), (dict(N=-5), 1), (dict(K=-2), 1),
-    (dict(dtype=2), 2), (dict(dtype=-1), 2),
+    (dict(dtype=4), 2), (dict(dtype=-1), 2),
     (dict(lda=63), 1), (dict(tA=1, lda=63), 1), (dict(ldb=63), 1), (dict(tB=1, ldb=63), 1),
     (dict(ldd=63), 1), (dict(beta=1.0, ldc=63), 1),
     (dict(D=0), 1), (dict(A=0), 1), (dict(B=0), 1), (dict(beta=0.5, C=0), 1),
@@ -159,6 +159,26 @@ def test_k16_tail_is_named(lib):
     # 32x32x16 atoms skip empty sub-steps but have no half-width atom
     assert _v(lib, M=4096, N=4096, K=48, lda=64, ldb=4096) == lib.GEMM_OK
     assert "k16-tail" not in lib.gemm_last_path()
+
+
+def test_f32_operand_dtypes(lib, monkeypatch):
+    # float32 A/B rounded while staged: always the masked matrix-core kernel
+    assert _v(lib, M=8192, N=8192, K=8192, tB=1, dtype=lib.GEMM_DTYPE_F32_BF16) == lib.GEMM_OK
+    path = lib.gemm_last_path()
+    assert path.startswith("mfma t256x256x64 w2x2") and path.endswith("masked f32->bf16"), path
+    assert _v(lib, dtype=lib.GEMM_DTYPE_F32_F16) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith("masked f32->f16"), lib.gemm_last_path()
+    # pitches count 4-byte elements: 66 floats = 264 B is 8-byte aligned only
+    assert _v(lib, dtype=2, ldb=66) == lib.GEMM_OK
+    assert "(B: 8-byte loads, row pitch 264 B" in lib.gemm_last_path(), lib.gemm_last_path()
+    assert _v(lib, dtype=2, A=A0 + 4) == lib.GEMM_OK
+    assert "(A: 4-byte loads, base address" in lib.gemm_last_path(), lib.gemm_last_path()
+    assert _v(lib, dtype=2, A=A0 + 2) == lib.GEMM_ERR_INVALID_ARG  # floats must be 4-byte aligned
+    # D must not overlap A's float32 extent (twice the 16-bit extent)
+    assert _v(lib, dtype=0, M=64, K=64, D=A0 + 64 * 64 * 2 + 256) == lib.GEMM_OK
+    assert _v(lib, dtype=2, M=64, K=64, D=A0 + 64 * 64 * 2 + 256) == lib.GEMM_ERR_ALIAS
+    monkeypatch.setenv("GEMM_FORCE_PATH", "fma")
+    assert _v(lib, dtype=3) == lib.GEMM_ERR_UNSUPPORTED
 
 
 def test_huge_pitch_takes_64bit_addressing(lib):

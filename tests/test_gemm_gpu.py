@@ -148,6 +148,43 @@ def test_tiled_shapes_narrow_staging(tile, dtype, monkeypatch):
             r.check_padding_untouched()
 
 
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("dtype", ["f32_f16", "f32_bf16"])
+def test_tiled_shapes_f32_operands(tile, dtype, monkeypatch):
+    """float32 A and B rounded to f16/bf16 while staged (always the masked
+    kernel): every layout, general epilogue, aligned and 8-/4-byte pitches,
+    bases 4 bytes past a 16-byte boundary; NaN in the padding is never read."""
+    monkeypatch.setenv("GEMM_FORCE_TILE", tile)
+    seed = 6000
+    for (M, N, K) in SHAPES[::2] + [(512, 256, 192)]:
+        for tA, tB in [(0, 0), (0, 1), (1, 0), (1, 1)]:
+            seed += 1
+            mode = seed % 3
+            lda = (M if tA else K) + (0, 1, 2)[mode]
+            ldb = (K if tB else N) + (3, 0, 2)[mode]
+            a_off = 1 if mode == 1 else 0  # elements of 4 bytes
+            cfg = workloads.Config(f"f32op{seed}", M, N, K, dtype, tA, tB, 1.5, -0.5,
+                                   "uniform", seed, lda=lda, ldb=ldb)
+            r = run(cfg, a_off=a_off)
+            assert r.path.startswith("mfma " + tile) and (" f32->" + dtype[4:]) in r.path, r.path
+            r.check()
+            r.check_padding_untouched()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_f32_operands_equal_prerounded_16bit_bitwise(dtype):
+    """Rounding inside the staging is the same rounding torch applies, and
+    the rest of the path is the same kernel: D must match bitwise."""
+    cfg32 = workloads.Config("f32eq", 300, 200, 136, "f32_" + dtype, 0, 1, 1.0, 0.0,
+                             "normal", 91)
+    inp32 = workloads.make_inputs(cfg32)
+    r32 = run(cfg32, inp32)
+    cfg16 = workloads.Config("f32eq16", 300, 200, 136, dtype, 0, 1, 1.0, 0.0, "normal", 91)
+    r16 = run(cfg16, workloads.make_inputs(cfg16, A_src=inp32.A_src, B_src=inp32.B_src))
+    assert r32.path.replace(" f32->" + dtype, "") == r16.path, (r32.path, r16.path)
+    assert torch.equal(r32.D, r16.D)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_tiled_shapes_fma(dtype, monkeypatch):
     monkeypatch.setenv("GEMM_FORCE_PATH", "fma")

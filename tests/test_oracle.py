@@ -176,6 +176,33 @@ def test_oracle_equals_exact_bruteforce(tA, tB, dt):
                     assert abs(Fraction(D[i, j]) - E[i][j]) <= Fraction(tol), (M, N, K, i, j)
 
 
+@pytest.mark.parametrize("tA,tB", [(0, 1), (1, 0)])
+@pytest.mark.parametrize("dt", [0, 1])
+def test_f32_operand_reference_equals_exact_on_library_rounding(tA, tB, dt):
+    """float32 operands: the oracle's f32 entry (its own rounding, then the
+    product) against exact Fraction sums of the values torch's rounding
+    (`.half()` / `.bfloat16()`) gives each stored element. The sources are
+    random float32 values, so almost every element actually rounds."""
+    rng = np.random.default_rng(300 + 10 * tA + 2 * tB + dt)
+    for (M, N, K) in [(3, 2, 7), (7, 8, 15), (8, 16, 17)]:
+        for alpha, beta in [(1.0, 0.0), (-1.5, 0.5)]:
+            lda, ldb, ldc = (M if tA else K) + 2, (K if tB else N) + 1, N
+            Af = rng.uniform(-3, 3, (K if tA else M) * lda).astype(np.float32)
+            Bf = rng.uniform(-3, 3, (N if tB else K) * ldb).astype(np.float32)
+            C = rng.uniform(-1, 1, M * ldc).astype(np.float32)
+            D, bound = oracle.gemm_reference_f32(M, N, K, dt, tA, tB, alpha, beta,
+                                                 Af, lda, Bf, ldb, C, ldc)
+            tdt = torch.float16 if dt == 0 else torch.bfloat16
+            A16 = torch.tensor(Af).to(tdt).view(torch.int16).numpy().view(np.uint16)
+            B16 = torch.tensor(Bf).to(tdt).view(torch.int16).numpy().view(np.uint16)
+            assert np.mean(A16 != oracle.round_f32_bits(Af * 0 + 1, dt)) > 0.5  # not all ones
+            E = _brute_force(M, N, K, dt, tA, tB, alpha, beta, A16, lda, B16, ldb, C, ldc)
+            for i in range(M):
+                for j in range(N):
+                    tol = (K + 3) * 2.0 ** -52 * bound[i, j]
+                    assert abs(Fraction(D[i, j]) - E[i][j]) <= Fraction(tol), (M, N, K, i, j)
+
+
 def test_single_atom_16x8x16_workload_exact():
     cfg = workloads.CONFIGS["atom16x8x16"]
     inp = workloads.make_inputs(cfg)

@@ -25,8 +25,11 @@ from typing import Optional
 
 import torch
 
-DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
-DTYPE_CODE = {"f16": 0, "bf16": 1}
+# "f32_f16" / "f32_bf16": A and B are handed over as float32 and rounded to
+# f16 / bf16 by the library while it stages them.
+DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32_f16": torch.float32,
+          "f32_bf16": torch.float32}
+DTYPE_CODE = {"f16": 0, "bf16": 1, "f32_f16": 2, "f32_bf16": 3}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -75,6 +78,13 @@ CONFIGS = {
 }
 CONFIG_ORDER = ["atom16x8x16", "gemm512", "gemm4096_inplace", "gemm8192_nt",
                 "ragged4097x1000x1032_tn"]
+
+# Extra measurement case (not one of the five): float32 operands rounded to
+# bf16 while staged, the 4096^3 NT shape with normal(0, 1/sqrt(K)) inputs.
+EXTRA_CONFIGS = {
+    "gemm4096_f32in_nt": Config("gemm4096_f32in_nt", 4096, 4096, 4096, "f32_bf16", 0, 1, 1.0,
+                                0.0, "normal_invsqrtk", 1006),
+}
 
 
 def _draw(gen: torch.Generator, shape, dist: str, K: int) -> torch.Tensor:
