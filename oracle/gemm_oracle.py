@@ -26,7 +26,13 @@ What it computes, and where each step comes from:
   ``@tensorcore``: "The forms", the sentence on rounding operands to f16);
   round-to-nearest-even is the reading taken, as the page names no mode.
 
-Every step uses numpy in float64; the only library primitive is ``np.matmul``.
+* int8 operands with an int32 result (``gemm_reference_i8``): the integer
+  tensor-core form of the same contraction (Phobos ``@tensorcore``: "When it
+  declines", the note on i8); sums taken exactly in int64 and wrapped to
+  int32, the reading taken for an overflow rule the pages do not state.
+
+Every step uses numpy in float64 (int64 for int8); the only library primitive
+is ``np.matmul``.
 There is no blocking beyond splitting rows into slabs to bound memory, which
 does not change any individual dot product.
 """
@@ -181,6 +187,38 @@ def gemm_reference_f32(M, N, K, dtype, transA, transB, alpha, beta,
     B_bits = round_f32_bits(np.asarray(B_f32, dtype=np.float32).reshape(-1), dtype)
     return gemm_reference(M, N, K, dtype, transA, transB, alpha, beta, A_bits, lda, B_bits, ldb,
                           C, ldc, **kw)
+
+
+def gemm_reference_i8(M, N, K, transA, transB, alpha, beta, A, lda, B, ldb, C=None, ldc=None,
+                      rows=None):
+    """int8 operands, int32 result: D = alpha*op(A)@op(B) + beta*C over the
+    integers, reduced modulo 2^32 to two's-complement int32.
+
+    The integer form of the same contraction: an i8 dot runs on the integer
+    tensor cores whenever its shape allows (Phobos docs, ``@tensorcore``:
+    "When it declines", the closing note on i8). The pages give no output
+    type or overflow rule; the reading taken is an int32 accumulator whose
+    sums, and the alpha/beta epilogue, wrap like int32 arithmetic. alpha and
+    beta are integers; beta == 0 means C is not read; K == 0 or alpha == 0
+    gives beta*C. ``A``/``B`` are the stored int8 buffers (flat, leading
+    dimensions lda/ldb, same transpose formulas as the floating-point case).
+    Returns the int32 [len(rows), N] result."""
+    rows = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    mask = np.uint64(0xFFFFFFFF)
+    acc = np.zeros((rows.size, N), dtype=np.uint64)
+    if K > 0 and alpha != 0 and rows.size and N:
+        a = _stored_2d(np.asarray(A, dtype=np.int8).reshape(-1), *((K, M) if transA else (M, K)), lda)
+        b = _stored_2d(np.asarray(B, dtype=np.int8).reshape(-1), *((N, K) if transB else (K, N)), ldb)
+        a = (a.T if transA else a).astype(np.int64)[rows, :]
+        b = (b.T if transB else b).astype(np.int64)
+        # |each sum| <= 2^14 * K < 2^45: exact in int64; then wrap to 32 bits
+        prod = np.matmul(a, b).astype(np.uint64) & mask
+        acc = (prod * (np.uint64(int(alpha) & 0xFFFFFFFF))) & mask
+    if beta != 0 and rows.size and N:
+        c = _stored_2d(np.asarray(C, dtype=np.int32).reshape(-1), M, N, ldc)[rows, :]
+        acc = (acc + ((c.astype(np.int64).astype(np.uint64) & mask) *
+                      np.uint64(int(beta) & 0xFFFFFFFF))) & mask
+    return acc.astype(np.uint32).view(np.int32)
 
 
 def gemm_reference_elements(M, N, K, dtype, transA, transB, alpha, beta,

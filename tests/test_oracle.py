@@ -203,6 +203,77 @@ def test_f32_operand_reference_equals_exact_on_library_rounding(tA, tB, dt):
                     assert abs(Fraction(D[i, j]) - E[i][j]) <= Fraction(tol), (M, N, K, i, j)
 
 
+# ------------------------------------------------------- int8 -> int32 ----
+
+def _wrap32(v: int) -> int:
+    v &= 0xFFFFFFFF
+    return v - (1 << 32) if v >= (1 << 31) else v
+
+
+def _brute_force_i8(M, N, K, tA, tB, alpha, beta, A, lda, B, ldb, C, ldc):
+    """Python-integer triple loop over the stored int8 buffers, then int32 wrap."""
+    D = np.zeros((M, N), dtype=np.int64)
+    for i in range(M):
+        for j in range(N):
+            s = 0
+            for k in range(K):
+                a = int(A[k * lda + i] if tA else A[i * lda + k])
+                b = int(B[j * ldb + k] if tB else B[k * ldb + j])
+                s += a * b
+            d = alpha * s + (beta * int(C[i * ldc + j]) if beta != 0 else 0)
+            D[i, j] = _wrap32(d)
+    return D
+
+
+@pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_i8_oracle_equals_integer_bruteforce(tA, tB):
+    rng = np.random.default_rng(500 + 2 * tA + tB)
+    for (M, N, K) in [(1, 1, 1), (3, 2, 7), (7, 8, 33), (16, 5, 64)]:
+        for alpha, beta in [(1, 0), (1, 1), (-3, 2), (2**31 - 1, -2**31), (7, -1)]:
+            lda, ldb, ldc = (M if tA else K) + 2, (K if tB else N) + 3, N + 1
+            A = rng.integers(-128, 128, (K if tA else M) * lda).astype(np.int8)
+            B = rng.integers(-128, 128, (N if tB else K) * ldb).astype(np.int8)
+            C = rng.integers(-2**31, 2**31, M * ldc).astype(np.int32)
+            D = oracle.gemm_reference_i8(M, N, K, tA, tB, alpha, beta, A, lda, B, ldb, C, ldc)
+            E = _brute_force_i8(M, N, K, tA, tB, alpha, beta, A, lda, B, ldb, C, ldc)
+            assert D.dtype == np.int32 and np.array_equal(D.astype(np.int64), E), (M, N, K, alpha)
+
+
+def test_i8_oracle_wraps_like_int32_and_skips_c():
+    # 127*127*K exceeds 2^31 for K = 140000: the int32 sum wraps
+    M, N, K = 2, 3, 140000
+    A = np.full(M * K, 127, np.int8)
+    B = np.full(N * K, 127, np.int8)
+    D = oracle.gemm_reference_i8(M, N, K, 0, 1, 1, 0, A, K, B, K)
+    assert np.all(D == _wrap32(127 * 127 * K)) and _wrap32(127 * 127 * K) < 0
+    D = oracle.gemm_reference_i8(M, N, K, 0, 1, -1, 0, A, K, B, K)
+    assert np.all(D == _wrap32(-127 * 127 * K))
+    A = np.full(M * K, -128, np.int8)
+    D = oracle.gemm_reference_i8(M, N, K, 0, 1, 1, 0, A, K, B, K)
+    assert np.all(D == _wrap32(-128 * 127 * K))
+    # beta == 0 never reads C; K == 0 and alpha == 0 give beta*C
+    D = oracle.gemm_reference_i8(M, N, 5, 0, 0, 1, 0, A[:10], 5, B[:15], 3, None, None)
+    assert np.all(D == 5 * (-128) * 127)
+    C = np.arange(M * N, dtype=np.int32) - 3
+    for K0, al in [(0, 1), (4, 0)]:
+        D = oracle.gemm_reference_i8(M, N, K0, 0, 0, al, 3, A[:8], 4, B[:12], 3, C, N)
+        assert np.array_equal(D.reshape(-1), 3 * C)
+
+
+def test_i8_oracle_transpose_equivalence_and_ones():
+    rng = np.random.default_rng(9)
+    M, N, K = 9, 11, 40
+    a = rng.integers(-128, 128, (M, K)).astype(np.int8)
+    b = rng.integers(-128, 128, (K, N)).astype(np.int8)
+    ref = oracle.gemm_reference_i8(M, N, K, 0, 0, 1, 0, a.reshape(-1), K, b.reshape(-1), N)
+    assert np.array_equal(ref, oracle.gemm_reference_i8(
+        M, N, K, 1, 1, 1, 0, a.T.copy().reshape(-1), M, b.T.copy().reshape(-1), K))
+    assert np.array_equal(ref.astype(np.int64), a.astype(np.int64) @ b.astype(np.int64))
+    ones = oracle.gemm_reference_i8(4, 5, 300, 0, 1, 1, 0, np.ones(1200, np.int8), 300,
+                                    np.ones(1500, np.int8), 300)
+    assert np.all(ones == 300)
+
+
 def test_single_atom_16x8x16_workload_exact():
     cfg = workloads.CONFIGS["atom16x8x16"]
     inp = workloads.make_inputs(cfg)
