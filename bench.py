@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0,  # MI355X dense MFMA, published
                "f32_bf16": 2500.0, "f32_f16": 2500.0}  # rounded operands run on the same cores
 PEAK_HBM_GBS = 8000.0
+PEAK_INT8_TOPS = 5000.0  # MI355X dense int8 MFMA, published
 COPY_CAL_BYTES = 1 << 30
 DIST_TEXT = {"uniform": "uniform[-1, 1]", "normal": "normal(0, 1)",
              "normal_invsqrtk": "normal(0, 1/sqrt(K))"}
@@ -134,6 +135,59 @@ def copy_calibration():
                       "copy_calibration_bytes_written": COPY_CAL_BYTES, "launches": 3}))
 
 
+def bench_i8(args):
+    """The int8 form on 8192^3 NT (A [M,K], B [N,K], alpha 1, beta 0): integer
+    ops per second against the int8 matrix-core peak; bit-exact oracle check
+    on sampled rows."""
+    import numpy as np
+    import torch
+
+    import dense_gemm_tile_amd as dgt
+    import workloads
+    M = N = K = 8192
+    A, B = workloads.make_i8_inputs(M, N, K, 0, 1, 1007)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    Ad, Bd = A.to(dev), B.to(dev)
+    D = torch.empty((M, N), dtype=torch.int32, device=dev)
+
+    def step():
+        dgt.gemm_i8(M, N, K, 0, 1, 1, 0, Ad, K, Bd, K, None, N, D, N, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    ok = None
+    if not args.no_check:
+        import oracle
+        rows = np.array([0, 1, 127, 128, 4095, 4096, 8191])
+        ref = oracle.gemm_reference_i8(M, N, K, 0, 1, 1, 0, A.numpy().reshape(-1), K,
+                                       B.numpy().reshape(-1), K, rows=rows)
+        ok = bool(np.array_equal(D[rows].cpu().numpy(), ref))
+        if not ok:
+            print("PARITY FAILURE on sampled rows", file=sys.stderr)
+            sys.exit(1)
+    tops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "TOP/s (2MNK/t) int8 -> int32 M=N=K=8192", "value": round(tops, 2),
+        "unit": "TOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8", "data": "synthetic (seed 1007; uniform int8)",
+        "config": {"workload": "gemm8192_i8_nt", "M": M, "N": N, "K": K, "transA": 0,
+                   "transB": 1, "alpha": 1, "beta": 0, "parallelism": "single GPU"},
+        "oracle_bit_exact_sampled_rows": ok, "path": dgt.gemm_last_path(),
+        "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TOP/s", "frac": round(tops / PEAK_INT8_TOPS, 4), "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +207,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload == "gemm8192_i8_nt":
+        bench_i8(args)
         return
 
     import numpy as np

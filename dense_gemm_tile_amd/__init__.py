@@ -35,6 +35,10 @@ _SIGNATURES = {
                     _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "gemm_validate": (_int, [_i64, _i64, _i64, _int, _int, _int, _f32, _f32,
                              _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64]),
+    "gemm_i8": (_int, [_i64, _i64, _i64, _int, _int, ctypes.c_int32, ctypes.c_int32,
+                       _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "gemm_i8_validate": (_int, [_i64, _i64, _i64, _int, _int, ctypes.c_int32, ctypes.c_int32,
+                                _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64]),
     "gemm_last_error": (ctypes.c_char_p, []),
     "gemm_last_path": (ctypes.c_char_p, []),
     "gemm_tile_order": (_int, [_i64, _i64, _int, ctypes.POINTER(ctypes.c_int32),
@@ -110,6 +114,22 @@ def gemm_validate(M, N, K, dtype, transA, transB, alpha, beta, A, lda, B, ldb, C
                               _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(D), ldd)
 
 
+def gemm_i8(M, N, K, transA, transB, alpha, beta, A, lda, B, ldb, C, ldc, D, ldd, stream=None):
+    """Enqueue the int8 form D = alpha*op(A)@op(B) + beta*C (int32 C/D, integer
+    alpha/beta, int32 wraparound); raises GemmError on a non-zero status."""
+    st = _lib.gemm_i8(M, N, K, int(transA), int(transB), int(alpha), int(beta), _ptr(A), lda,
+                      _ptr(B), ldb, _ptr(C), ldc, _ptr(D), ldd, _stream(stream))
+    if st != GEMM_OK:
+        raise GemmError(st, gemm_last_error())
+
+
+def gemm_i8_validate(M, N, K, transA, transB, alpha, beta, A, lda, B, ldb, C, ldc, D,
+                     ldd) -> int:
+    """Host-only checks of the int8 form; returns the status code."""
+    return _lib.gemm_i8_validate(M, N, K, int(transA), int(transB), int(alpha), int(beta),
+                                 _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(D), ldd)
+
+
 def gemm_last_error() -> str:
     return _lib.gemm_last_error().decode()
 
@@ -129,7 +149,7 @@ def gemm_tile_order(tiles_m: int, tiles_n: int, group_m: int):
     return list(tm[:n]), list(tn[:n])
 
 
-__all__ = ["gemm", "gemm_status", "gemm_validate", "gemm_last_error", "gemm_last_path",
+__all__ = ["gemm_i8", "gemm_i8_validate", "gemm", "gemm_status", "gemm_validate", "gemm_last_error", "gemm_last_path",
            "gemm_tile_order", "GemmError", "GEMM_OK", "GEMM_ERR_INVALID_ARG",
            "GEMM_ERR_UNSUPPORTED", "GEMM_ERR_ALIAS", "GEMM_ERR_HIP", "GEMM_DTYPE_F16",
            "GEMM_DTYPE_BF16", "GEMM_DTYPE_F32_F16", "GEMM_DTYPE_F32_BF16", "LIB_PATH"]

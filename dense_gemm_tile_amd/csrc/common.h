@@ -30,6 +30,20 @@ struct GemmArgs {
                  //    count float32 elements (4, 2 or 1)
 };
 
+// Arguments of the int8 -> int32 kernel (see gemm_i8.hip).
+struct GemmI8Args {
+  const int8_t* A;
+  const int8_t* B;
+  const int32_t* C;
+  int32_t* D;
+  int64_t lda, ldb, ldc, ldd;  // in elements
+  int M, N, K;
+  int alpha, beta;
+  int read_c;            // beta != 0
+  int a_vec16, b_vec16;  // base and row pitch multiples of 16 bytes
+  int tiles_m, tiles_n, group_m;
+};
+
 // Epilogue kinds. All three compute alpha*acc + beta*C; the specialised ones
 // only skip work whose result is known exactly (C not read when beta == 0,
 // multiplies by 1 dropped when alpha == beta == 1).
@@ -97,6 +111,9 @@ constexpr int kFmaTileM = 64, kFmaTileN = 64;
 
 hipError_t launch_fma(int dtype, bool transA, bool transB, const GemmArgs& a,
                       hipStream_t stream);
+hipError_t launch_i8(bool ta, bool tb, const GemmI8Args& a, hipStream_t s);
+int i8_tile_m();
+int i8_tile_n();
 hipError_t launch_scale_c(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace dgt

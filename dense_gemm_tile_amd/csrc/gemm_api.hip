@@ -274,6 +274,86 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   return GEMM_OK;
 }
 
+// Checks and launch arguments of the int8 form (same rules as the float form,
+// with 1-byte operands and int32 C/D).
+int plan_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alpha, int32_t beta,
+            const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const int32_t* C,
+            int64_t ldc, const int32_t* D, int64_t ldd, GemmI8Args& a, bool& noop) {
+  g_err.clear();
+  g_path.clear();
+  noop = false;
+  char buf[256];
+  transA = transA != 0;
+  transB = transB != 0;
+  if (M < 0 || N < 0 || K < 0) {
+    std::snprintf(buf, sizeof buf, "negative dimension: M=%lld N=%lld K=%lld", (long long)M,
+                  (long long)N, (long long)K);
+    return fail(GEMM_ERR_INVALID_ARG, buf);
+  }
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(GEMM_ERR_UNSUPPORTED, "a dimension exceeds 2^31-1024");
+  const int64_t min_lda = transA ? M : K, min_ldb = transB ? K : N;
+  if (lda < (min_lda > 1 ? min_lda : 1) || ldb < (min_ldb > 1 ? min_ldb : 1) ||
+      ldd < (N > 1 ? N : 1))
+    return fail(GEMM_ERR_INVALID_ARG, "a leading dimension is smaller than its row length");
+  const bool reads_c = beta != 0;
+  if (reads_c && ldc < (N > 1 ? N : 1))
+    return fail(GEMM_ERR_INVALID_ARG, "ldc is smaller than N");
+  if (M == 0 || N == 0) {
+    noop = true;
+    g_path = "noop: empty output";
+    return GEMM_OK;
+  }
+  const bool reads_ab = K > 0 && alpha != 0;
+  if (!D) return fail(GEMM_ERR_INVALID_ARG, "D is NULL");
+  if ((uintptr_t)D % 4) return fail(GEMM_ERR_INVALID_ARG, "D is not 4-byte aligned");
+  if (reads_c && !C) return fail(GEMM_ERR_INVALID_ARG, "C is NULL but beta != 0");
+  if (reads_c && (uintptr_t)C % 4) return fail(GEMM_ERR_INVALID_ARG, "C is not 4-byte aligned");
+  if (reads_ab && (!A || !B)) return fail(GEMM_ERR_INVALID_ARG, "A or B is NULL");
+  const unsigned __int128 d_ext = extent_bytes(M, N, ldd, 4);
+  if (reads_c) {
+    const bool same = (const void*)C == (const void*)D && ldc == ldd;
+    if (!same && overlaps(C, extent_bytes(M, N, ldc, 4), D, d_ext))
+      return fail(GEMM_ERR_ALIAS, "D overlaps C without being the same matrix (C == D and "
+                                  "ldc == ldd is the only allowed overlap)");
+  }
+  if (reads_ab) {
+    if (overlaps(A, extent_bytes(transA ? K : M, transA ? M : K, lda, 1), D, d_ext))
+      return fail(GEMM_ERR_ALIAS, "D overlaps A");
+    if (overlaps(B, extent_bytes(transB ? N : K, transB ? K : N, ldb, 1), D, d_ext))
+      return fail(GEMM_ERR_ALIAS, "D overlaps B");
+  }
+  a = GemmI8Args{};
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = const_cast<int32_t*>(D);
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = reads_c ? ldc : ldd;
+  a.ldd = ldd;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = reads_ab ? (int)K : 0;  // no K loop when the product does not contribute
+  a.alpha = alpha;
+  a.beta = beta;
+  a.read_c = reads_c ? 1 : 0;
+  a.a_vec16 = ((uintptr_t)A % 16 == 0 && lda % 16 == 0) ? 1 : 0;
+  a.b_vec16 = ((uintptr_t)B % 16 == 0 && ldb % 16 == 0) ? 1 : 0;
+  a.tiles_m = (int)((M + i8_tile_m() - 1) / i8_tile_m());
+  a.tiles_n = (int)((N + i8_tile_n() - 1) / i8_tile_n());
+  a.group_m = 8;
+  if ((int64_t)a.tiles_m * a.tiles_n > 0x7fffffff)
+    return fail(GEMM_ERR_UNSUPPORTED, "too many output tiles for one launch");
+  const char* ops = transA ? (transB ? "TT" : "TN") : (transB ? "NT" : "NN");
+  std::snprintf(buf, sizeof buf, "i8 mfma t%dx%dx128 w2x2 a32x32x32 %s epi=%s%s%s", i8_tile_m(),
+                i8_tile_n(), ops, reads_c ? "general" : "beta0",
+                reads_ab ? "" : " (K == 0 or alpha == 0: D = beta*C)",
+                (reads_ab && (!a.a_vec16 || !a.b_vec16)) ? " bytewise staging" : "");
+  g_path = buf;
+  return GEMM_OK;
+}
+
 void log_call(int64_t M, int64_t N, int64_t K, int status) {
   const char* lv = env("GEMM_LOG");
   if (!lv || std::strcmp(lv, "debug") != 0) return;
@@ -317,6 +397,33 @@ int gemm_validate(int64_t M, int64_t N, int64_t K, int dtype, int transA, int tr
   dgt::Plan plan;
   int st = dgt::plan_call(M, N, K, dtype, transA, transB, alpha, beta, A, lda, B, ldb, C, ldc, D,
                           ldd, plan);
+  dgt::log_call(M, N, K, st);
+  return st;
+}
+
+int gemm_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alpha, int32_t beta,
+            const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const int32_t* C,
+            int64_t ldc, int32_t* D, int64_t ldd, void* stream) {
+  using namespace dgt;
+  GemmI8Args a;
+  bool noop;
+  int st = plan_i8(M, N, K, transA, transB, alpha, beta, A, lda, B, ldb, C, ldc, D, ldd, a, noop);
+  if (st == GEMM_OK && !noop) {
+    const hipError_t e = launch_i8(transA != 0, transB != 0, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+      st = fail(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  }
+  log_call(M, N, K, st);
+  return st;
+}
+
+int gemm_i8_validate(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alpha,
+                     int32_t beta, const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
+                     const int32_t* C, int64_t ldc, const int32_t* D, int64_t ldd) {
+  dgt::GemmI8Args a;
+  bool noop;
+  int st = dgt::plan_i8(M, N, K, transA, transB, alpha, beta, A, lda, B, ldb, C, ldc, D, ldd, a,
+                        noop);
   dgt::log_call(M, N, K, st);
   return st;
 }

@@ -127,6 +127,29 @@ GEMM_API const char* gemm_last_error(void);
 GEMM_API const char* gemm_last_path(void);
 
 /*
+ * gemm_i8: enqueue D = alpha*op(A)@op(B) + beta*C for int8 A and B with an
+ * int32 accumulator and int32 C and D: the integer tensor-core form of the
+ * same contraction (Phobos @tensorcore, "When it declines": an i8 dot takes
+ * the integer tensor cores whenever its shape allows). Every sum, and the
+ * epilogue, wraps modulo 2^32 like int32 arithmetic.
+ *
+ * Arguments as for gemm(), with: alpha, beta int32; A, B int8 device pointers
+ * (any alignment; leading dimensions in bytes = elements); C, D int32 device
+ * pointers, 4-byte aligned. beta == 0: C is not read (may be NULL). K == 0 or
+ * alpha == 0: D = beta*C (A and B are not read). M == 0 or N == 0: nothing
+ * to do. D may equal C exactly; it must not overlap A or B. Same return
+ * codes, thread-local error/path strings and GEMM_LOG=debug line as gemm().
+ */
+GEMM_API int gemm_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alpha,
+            int32_t beta, const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
+            const int32_t* C, int64_t ldc, int32_t* D, int64_t ldd, void* stream);
+
+/* gemm_i8_validate: the host-side checks of gemm_i8() without any launch. */
+GEMM_API int gemm_i8_validate(int64_t M, int64_t N, int64_t K, int transA, int transB,
+            int32_t alpha, int32_t beta, const int8_t* A, int64_t lda, const int8_t* B,
+            int64_t ldb, const int32_t* C, int64_t ldc, const int32_t* D, int64_t ldd);
+
+/*
  * gemm_tile_order: the output-tile scheduler's workgroup -> tile map, computed
  * on the host (the kernels use the same function). For tiles_m x tiles_n tiles
  * it writes, for each workgroup id w in [0, tiles_m*tiles_n), the tile row

@@ -37,7 +37,7 @@ def _declared_symbols():
 def test_library_exports_every_declared_symbol(lib):
     names = _declared_symbols()
     assert {"gemm", "gemm_validate", "gemm_last_error", "gemm_last_path",
-            "gemm_tile_order"} <= set(names)
+            "gemm_tile_order", "gemm_i8", "gemm_i8_validate"} <= set(names)
     so = lib.LIB_PATH
     out = subprocess.run(["nm", "-D", "--defined-only", so], capture_output=True, text=True,
                          check=True).stdout
@@ -179,6 +179,42 @@ def test_f32_operand_dtypes(lib, monkeypatch):
     assert _v(lib, dtype=2, M=64, K=64, D=A0 + 64 * 64 * 2 + 256) == lib.GEMM_ERR_ALIAS
     monkeypatch.setenv("GEMM_FORCE_PATH", "fma")
     assert _v(lib, dtype=3) == lib.GEMM_ERR_UNSUPPORTED
+
+
+def _v8(lib, M=64, N=64, K=64, tA=0, tB=0, alpha=1, beta=0, A=A0, lda=None, B=B0, ldb=None,
+        C=C0, ldc=None, D=D0, ldd=None):
+    lda = lda if lda is not None else (M if tA else K)
+    ldb = ldb if ldb is not None else (K if tB else N)
+    ldc = ldc if ldc is not None else N
+    ldd = ldd if ldd is not None else N
+    return lib.gemm_i8_validate(M, N, K, tA, tB, alpha, beta, A, lda, B, ldb, C, ldc, D, ldd)
+
+
+def test_i8_form_checks_and_paths(lib):
+    assert _v8(lib, tB=1) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "i8 mfma t128x128x128 w2x2 a32x32x32 NT epi=beta0"
+    assert _v8(lib, beta=-2, tA=1) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "i8 mfma t128x128x128 w2x2 a32x32x32 TN epi=general"
+    assert _v8(lib, lda=65) == lib.GEMM_OK  # any alignment: bytewise staging
+    assert lib.gemm_last_path().endswith("bytewise staging")
+    assert _v8(lib, A=A0 + 1) == lib.GEMM_OK
+    assert _v8(lib, K=0, A=0, B=0, beta=3, lda=1) == lib.GEMM_OK
+    assert "D = beta*C" in lib.gemm_last_path()
+    assert _v8(lib, alpha=0, A=0, B=0, beta=0) == lib.GEMM_OK
+    assert _v8(lib, M=0, A=0, B=0, D=0) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("noop")
+    assert _v8(lib, M=-1) == lib.GEMM_ERR_INVALID_ARG
+    assert _v8(lib, lda=63) == lib.GEMM_ERR_INVALID_ARG
+    assert _v8(lib, D=0) == lib.GEMM_ERR_INVALID_ARG
+    assert _v8(lib, D=D0 + 2) == lib.GEMM_ERR_INVALID_ARG
+    assert _v8(lib, beta=1, C=0) == lib.GEMM_ERR_INVALID_ARG
+    assert _v8(lib, A=0) == lib.GEMM_ERR_INVALID_ARG
+    assert _v8(lib, beta=1, C=D0) == lib.GEMM_OK  # exact in-place
+    assert _v8(lib, beta=1, C=D0 + 4) == lib.GEMM_ERR_ALIAS
+    assert _v8(lib, D=A0 + 64) == lib.GEMM_ERR_ALIAS
+    # A is 64 x 64 bytes: a D placed right after it does not overlap
+    assert _v8(lib, D=A0 + 64 * 64) == lib.GEMM_OK
+    assert _v8(lib, M=1 << 31) == lib.GEMM_ERR_UNSUPPORTED
 
 
 def test_huge_pitch_takes_64bit_addressing(lib):

@@ -156,3 +156,15 @@ def bits_u16(x: torch.Tensor):
 
 def with_shape(cfg: Config, **kw) -> Config:
     return dataclasses.replace(cfg, **kw)
+
+
+def make_i8_inputs(M: int, N: int, K: int, transA: int, transB: int, seed: int):
+    """Seeded int8 operands, uniform over [-128, 127], in their stored shapes
+    (A then B, packed leading dimensions)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    a_shape = (K, M) if transA else (M, K)
+    b_shape = (N, K) if transB else (K, N)
+    A = torch.randint(-128, 128, a_shape, generator=gen, dtype=torch.int8)
+    B = torch.randint(-128, 128, b_shape, generator=gen, dtype=torch.int8)
+    return A, B
+
