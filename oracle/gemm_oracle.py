@@ -26,6 +26,10 @@ What it computes, and where each step comes from:
   ``@tensorcore``: "The forms", the sentence on rounding operands to f16);
   round-to-nearest-even is the reading taken, as the page names no mode.
 
+* 8-bit float operands (dtypes 4 and 5, ``decode_fp8``): the fp8 precisions
+  the ``gemm_async`` variants list (TVM ``gemm`` page, restated, the
+  precision list); the operands are stored codes, decoded exactly, and the
+  product is the same definition.
 * int8 operands with an int32 result (``gemm_reference_i8``): the integer
   tensor-core form of the same contraction (Phobos ``@tensorcore``: "When it
   declines", the note on i8); sums taken exactly in int64 and wrapped to
@@ -42,6 +46,8 @@ import numpy as np
 
 F16 = 0
 BF16 = 1
+F8E4M3 = 4  # 8-bit float operands (OCP E4M3), f32 accumulator and C/D
+F8E5M2 = 5  # 8-bit float operands (OCP E5M2)
 
 # Per-element pass criterion for a device result (its own tolerance, written
 # here rather than borrowed from the device side).
@@ -87,8 +93,36 @@ def round_f32_bits(x, dtype: int) -> np.ndarray:
     raise ValueError(f"dtype code {dtype} is neither f16 (0) nor bf16 (1)")
 
 
+def decode_fp8(codes, dtype: int) -> np.ndarray:
+    """8-bit float codes -> their exact values as float64, from the field
+    layout of the two OCP 8-bit formats:
+
+    * E4M3 (dtype 4): sign, 4 exponent bits (bias 7), 3 mantissa bits;
+      exponent 0 is subnormal (m * 2^-9); exponent 15 with mantissa 7 is NaN
+      and there is no infinity (largest finite 448).
+    * E5M2 (dtype 5): sign, 5 exponent bits (bias 15), 2 mantissa bits;
+      exponent 0 is subnormal (m * 2^-16); exponent 31 is infinity (m = 0)
+      or NaN.
+    """
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c >> 7, -1.0, 1.0)
+    if dtype == F8E4M3:
+        e, m = (c >> 3) & 0xF, c & 0x7
+        val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+        val = np.where((e == 15) & (m == 7), np.nan, val)
+    elif dtype == F8E5M2:
+        e, m = (c >> 2) & 0x1F, c & 0x3
+        val = np.where(e == 0, m * 2.0 ** -16, (1.0 + m / 4.0) * np.exp2(e - 15.0))
+        val = np.where(e == 31, np.where(m == 0, np.inf, np.nan), val)
+    else:
+        raise ValueError(f"dtype code {dtype} is not an 8-bit float (4 or 5)")
+    return sign * val
+
+
 def decode_bits(bits, dtype: int) -> np.ndarray:
-    """16-bit patterns -> their exact values as float64."""
+    """16-bit patterns (8-bit codes for dtypes 4 and 5) -> exact float64 values."""
+    if dtype in (F8E4M3, F8E5M2):
+        return decode_fp8(bits, dtype)
     bits = np.asarray(bits, dtype=np.uint16)
     if dtype == F16:
         return bits.view(np.float16).astype(np.float64)

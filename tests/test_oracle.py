@@ -203,6 +203,71 @@ def test_f32_operand_reference_equals_exact_on_library_rounding(tA, tB, dt):
                     assert abs(Fraction(D[i, j]) - E[i][j]) <= Fraction(tol), (M, N, K, i, j)
 
 
+# -------------------------------------------------------- 8-bit floats ----
+
+def _fp8_value(text):
+    if text in ("nan", "inf", "-inf", "-0"):
+        return float(text)
+    if "*p" in text:
+        a, b = text.split("*p")
+        return float(a) * 2.0 ** int(b)
+    return float(text)
+
+
+def test_fp8_decode_matches_hand_table():
+    n = 0
+    with open(os.path.join(GOLDEN, "fp8_codes.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].split()
+            if not line:
+                continue
+            fmt, code, val = line[0], int(line[1], 16), _fp8_value(line[2])
+            got = oracle.decode_fp8(np.array([code]), 4 if fmt == "e4m3" else 5)[0]
+            if np.isnan(val):
+                assert np.isnan(got), (fmt, hex(code))
+            else:
+                assert got == val and np.signbit(got) == np.signbit(val), (fmt, hex(code), got)
+            n += 1
+    assert n >= 20
+
+
+@pytest.mark.parametrize("dt,tdt", [(4, "float8_e4m3fn"), (5, "float8_e5m2")])
+def test_fp8_decode_every_code_equals_torch(dt, tdt):
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.decode_fp8(codes, dt)
+    lib = torch.from_numpy(codes).view(getattr(torch, tdt)).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(lib))
+    ok = ~np.isnan(ours)
+    assert np.array_equal(ours[ok], lib[ok])
+
+
+@pytest.mark.parametrize("dt,tdt", [(4, "float8_e4m3fn"), (5, "float8_e5m2")])
+@pytest.mark.parametrize("tA,tB", [(0, 1), (1, 0)])
+def test_fp8_reference_equals_exact_on_library_values(dt, tdt, tA, tB):
+    """The product on 8-bit float codes against exact Fraction sums of the
+    values torch decodes them to."""
+    rng = np.random.default_rng(700 + dt + 2 * tA)
+    finite = [c for c in range(256) if np.isfinite(oracle.decode_fp8(np.array([c]), dt)[0])]
+    for (M, N, K) in [(3, 2, 7), (8, 5, 33)]:
+        lda, ldb, ldc = (M if tA else K) + 1, (K if tB else N) + 2, N
+        A = rng.choice(finite, (K if tA else M) * lda).astype(np.uint8)
+        B = rng.choice(finite, (N if tB else K) * ldb).astype(np.uint8)
+        C = rng.uniform(-1, 1, M * ldc).astype(np.float32)
+        D, bound = oracle.gemm_reference(M, N, K, dt, tA, tB, 0.5, -1.0, A, lda, B, ldb, C, ldc)
+        av = torch.from_numpy(A).view(getattr(torch, tdt)).double().numpy()
+        bv = torch.from_numpy(B).view(getattr(torch, tdt)).double().numpy()
+        for i in range(M):
+            for j in range(N):
+                s = Fraction(0)
+                for k in range(K):
+                    a = av[k * lda + i] if tA else av[i * lda + k]
+                    b = bv[j * ldb + k] if tB else bv[k * ldb + j]
+                    s += Fraction(float(a)) * Fraction(float(b))
+                e = Fraction(0.5) * s + Fraction(-1.0) * Fraction(float(C[i * ldc + j]))
+                tol = (K + 3) * 2.0 ** -52 * bound[i, j]
+                assert abs(Fraction(D[i, j]) - e) <= Fraction(tol), (M, N, K, i, j)
+
+
 # ------------------------------------------------------- int8 -> int32 ----
 
 def _wrap32(v: int) -> int:
