@@ -31,6 +31,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0,  # MI355X dense MFMA, published
                "f32_bf16": 2500.0, "f32_f16": 2500.0}  # rounded operands run on the same cores
 PEAK_HBM_GBS = 8000.0
 PEAK_INT8_TOPS = 5000.0  # MI355X dense int8 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, published
 COPY_CAL_BYTES = 1 << 30
 DIST_TEXT = {"uniform": "uniform[-1, 1]", "normal": "normal(0, 1)",
              "normal_invsqrtk": "normal(0, 1/sqrt(K))"}
@@ -188,6 +189,60 @@ def bench_i8(args):
     }), flush=True)
 
 
+def bench_fp8(args):
+    """The 8-bit float form (OCP E4M3) on 8192^3 NT, alpha 1, beta 0: TFLOP/s
+    against the fp8 matrix-core peak; oracle check on sampled rows."""
+    import numpy as np
+    import torch
+
+    import dense_gemm_tile_amd as dgt
+    import workloads
+    M = N = K = 8192
+    A, B = workloads.make_fp8_inputs(M, N, K, 0, 1, 4, 1008)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    Ad, Bd = A.to(dev), B.to(dev)
+    D = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+    def step():
+        dgt.gemm(M, N, K, "f8e4m3", 0, 1, 1.0, 0.0, Ad, K, Bd, K, None, N, D, N, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    max_rel = None
+    if not args.no_check:
+        import oracle
+        rows = np.array([0, 1, 127, 128, 4095, 4096, 8191])
+        D_ref, bound = oracle.gemm_reference(M, N, K, 4, 0, 1, 1.0, 0.0, A.numpy().reshape(-1),
+                                             K, B.numpy().reshape(-1), K, rows=rows)
+        rep = oracle.check(D[rows].cpu().numpy().astype(np.float64), D_ref, bound)
+        if not rep["ok"]:
+            print(f"PARITY FAILURE on sampled rows: {rep}", file=sys.stderr)
+            sys.exit(1)
+        max_rel = rep["max_rel_err"]
+    tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "TFLOP/s (2MNK/t) fp8 e4m3 M=N=K=8192", "value": round(tf, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f8e4m3",
+        "data": "synthetic (seed 1008; uniform over finite E4M3 codes)",
+        "config": {"workload": "gemm8192_f8e4m3_nt", "M": M, "N": N, "K": K, "transA": 0,
+                   "transB": 1, "alpha": 1.0, "beta": 0.0, "parallelism": "single GPU"},
+        "oracle_max_rel_err": max_rel, "path": dgt.gemm_last_path(),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +265,9 @@ def main():
         return
     if args.workload == "gemm8192_i8_nt":
         bench_i8(args)
+        return
+    if args.workload == "gemm8192_f8e4m3_nt":
+        bench_fp8(args)
         return
 
     import numpy as np

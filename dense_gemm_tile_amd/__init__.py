@@ -27,6 +27,8 @@ GEMM_DTYPE_F16 = 0
 GEMM_DTYPE_BF16 = 1
 GEMM_DTYPE_F32_F16 = 2   # float32 A and B, rounded to f16 while staged
 GEMM_DTYPE_F32_BF16 = 3  # float32 A and B, rounded to bf16 while staged
+GEMM_DTYPE_F8_E4M3 = 4   # 8-bit float codes, OCP E4M3
+GEMM_DTYPE_F8_E5M2 = 5   # 8-bit float codes, OCP E5M2
 
 # Every symbol the header declares, with its ctypes signature.
 _i64, _int, _f32, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
@@ -87,7 +89,8 @@ def _stream(s):
 def _dtype(d):
     if isinstance(d, str):
         return {"f16": GEMM_DTYPE_F16, "bf16": GEMM_DTYPE_BF16, "f32_f16": GEMM_DTYPE_F32_F16,
-                "f32_bf16": GEMM_DTYPE_F32_BF16}[d]
+                "f32_bf16": GEMM_DTYPE_F32_BF16, "f8e4m3": GEMM_DTYPE_F8_E4M3,
+                "f8e5m2": GEMM_DTYPE_F8_E5M2}[d]
     return int(d)
 
 
@@ -152,4 +155,5 @@ def gemm_tile_order(tiles_m: int, tiles_n: int, group_m: int):
 __all__ = ["gemm_i8", "gemm_i8_validate", "gemm", "gemm_status", "gemm_validate", "gemm_last_error", "gemm_last_path",
            "gemm_tile_order", "GemmError", "GEMM_OK", "GEMM_ERR_INVALID_ARG",
            "GEMM_ERR_UNSUPPORTED", "GEMM_ERR_ALIAS", "GEMM_ERR_HIP", "GEMM_DTYPE_F16",
-           "GEMM_DTYPE_BF16", "GEMM_DTYPE_F32_F16", "GEMM_DTYPE_F32_BF16", "LIB_PATH"]
+           "GEMM_DTYPE_BF16", "GEMM_DTYPE_F32_F16", "GEMM_DTYPE_F32_BF16", "GEMM_DTYPE_F8_E4M3",
+           "GEMM_DTYPE_F8_E5M2", "LIB_PATH"]

@@ -30,19 +30,23 @@ struct GemmArgs {
                  //    count float32 elements (4, 2 or 1)
 };
 
-// Arguments of the int8 -> int32 kernel (see gemm_i8.hip).
-struct GemmI8Args {
-  const int8_t* A;
-  const int8_t* B;
-  const int32_t* C;
-  int32_t* D;
+// Arguments of the 1-byte-operand kernels (see gemm_byte.hip): int8 ->
+// int32 (integer alpha/beta, int32 C/D) or 8-bit float -> f32 (f32 alpha/beta
+// and C/D).
+struct GemmByteArgs {
+  const void* A;
+  const void* B;
+  const void* C;
+  void* D;
   int64_t lda, ldb, ldc, ldd;  // in elements
   int M, N, K;
-  int alpha, beta;
-  int read_c;            // beta != 0
-  int a_vec16, b_vec16;  // base and row pitch multiples of 16 bytes
+  int alpha_i, beta_i;     // int8 form
+  float alpha_f, beta_f;   // 8-bit float form
+  int read_c;              // beta != 0
+  int a_vec16, b_vec16;    // base and row pitch multiples of 16 bytes
   int tiles_m, tiles_n, group_m;
 };
+enum ByteKind : int { BYTE_I8 = 0, BYTE_F8E4M3 = 1, BYTE_F8E5M2 = 2 };
 
 // Epilogue kinds. All three compute alpha*acc + beta*C; the specialised ones
 // only skip work whose result is known exactly (C not read when beta == 0,
@@ -111,9 +115,9 @@ constexpr int kFmaTileM = 64, kFmaTileN = 64;
 
 hipError_t launch_fma(int dtype, bool transA, bool transB, const GemmArgs& a,
                       hipStream_t stream);
-hipError_t launch_i8(bool ta, bool tb, const GemmI8Args& a, hipStream_t s);
-int i8_tile_m();
-int i8_tile_n();
+hipError_t launch_byte(int kind, bool ta, bool tb, const GemmByteArgs& a, hipStream_t s);
+int byte_tile_m();
+int byte_tile_n();
 hipError_t launch_scale_c(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace dgt

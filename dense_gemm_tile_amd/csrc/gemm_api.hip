@@ -32,6 +32,9 @@ struct Plan {
   bool masked = false;
   int epi = EPI_BETA0;
   GemmArgs args{};
+  bool byte8 = false;  // 8-bit float operands: the 1-byte-operand kernel
+  int byte_kind = 0;
+  GemmByteArgs bargs{};
 };
 
 int fail(int code, const std::string& msg) {
@@ -101,14 +104,17 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
                   (long long)N, (long long)K);
     return fail(GEMM_ERR_INVALID_ARG, buf);
   }
-  if (dtype < GEMM_DTYPE_F16 || dtype > GEMM_DTYPE_F32_BF16) {
+  if (dtype < GEMM_DTYPE_F16 || dtype > GEMM_DTYPE_F8_E5M2) {
     std::snprintf(buf, sizeof buf,
-                  "dtype code %d is none of f16 (0), bf16 (1), f32->f16 (2), f32->bf16 (3)", dtype);
+                  "dtype code %d is none of f16 (0), bf16 (1), f32->f16 (2), f32->bf16 (3), "
+                  "fp8 e4m3 (4), fp8 e5m2 (5)", dtype);
     return fail(GEMM_ERR_UNSUPPORTED, buf);
   }
-  // f32 operands are rounded to the 16-bit type as they are staged.
-  const bool src32 = dtype >= GEMM_DTYPE_F32_F16;
-  const int esz = src32 ? 4 : 2;
+  // f32 operands are rounded to the 16-bit type as they are staged; 8-bit
+  // float operands run on the 1-byte-operand kernel.
+  const bool fp8 = dtype >= GEMM_DTYPE_F8_E4M3;
+  const bool src32 = !fp8 && dtype >= GEMM_DTYPE_F32_F16;
+  const int esz = fp8 ? 1 : src32 ? 4 : 2;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) {
     return fail(GEMM_ERR_UNSUPPORTED, "a dimension exceeds 2^31-1024");
   }
@@ -197,6 +203,46 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     return GEMM_OK;
   }
 
+  if (fp8) {
+    if (const char* force = env("GEMM_FORCE_PATH")) {
+      if (std::strcmp(force, "fma") == 0)
+        return fail(GEMM_ERR_UNSUPPORTED, "GEMM_FORCE_PATH=fma has no 8-bit float form");
+      if (std::strcmp(force, "mfma") != 0)
+        return fail(GEMM_ERR_INVALID_ARG,
+                    std::string("GEMM_FORCE_PATH must be mfma or fma, got ") + force);
+    }
+    GemmByteArgs& b = plan.bargs;
+    b.A = A;
+    b.B = B;
+    b.C = C;
+    b.D = const_cast<float*>(D);
+    b.lda = lda;
+    b.ldb = ldb;
+    b.ldc = a.ldc;
+    b.ldd = ldd;
+    b.M = (int)M;
+    b.N = (int)N;
+    b.K = (int)K;
+    b.alpha_f = alpha;
+    b.beta_f = beta;
+    b.read_c = reads_c ? 1 : 0;
+    b.a_vec16 = ((uintptr_t)A % 16 == 0 && lda % 16 == 0) ? 1 : 0;
+    b.b_vec16 = ((uintptr_t)B % 16 == 0 && ldb % 16 == 0) ? 1 : 0;
+    b.tiles_m = (int)((M + byte_tile_m() - 1) / byte_tile_m());
+    b.tiles_n = (int)((N + byte_tile_n() - 1) / byte_tile_n());
+    b.group_m = 8;
+    if ((int64_t)b.tiles_m * b.tiles_n > 0x7fffffff)
+      return fail(GEMM_ERR_UNSUPPORTED, "too many output tiles for one launch");
+    plan.byte8 = true;
+    plan.byte_kind = dtype == GEMM_DTYPE_F8_E4M3 ? BYTE_F8E4M3 : BYTE_F8E5M2;
+    const char* ops8 = transA ? (transB ? "TT" : "TN") : (transB ? "NT" : "NN");
+    std::snprintf(buf, sizeof buf, "fp8 %s mfma t%dx%dx128 w2x2 a32x32x64 %s epi=%s%s",
+                  dtype == GEMM_DTYPE_F8_E4M3 ? "e4m3" : "e5m2", byte_tile_m(), byte_tile_n(),
+                  ops8, epi_name, (!b.a_vec16 || !b.b_vec16) ? " bytewise staging" : "");
+    g_path = buf;
+    return GEMM_OK;
+  }
+
   // Path selection. The matrix-core path stages A and B in 16-byte pieces; an
   // operand whose base or row pitch is not a multiple of 16 bytes is read with
   // the widest loads they allow (8, 4 or 2 bytes, masked kernel), so every
@@ -278,7 +324,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
 // with 1-byte operands and int32 C/D).
 int plan_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alpha, int32_t beta,
             const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const int32_t* C,
-            int64_t ldc, const int32_t* D, int64_t ldd, GemmI8Args& a, bool& noop) {
+            int64_t ldc, const int32_t* D, int64_t ldd, GemmByteArgs& a, bool& noop) {
   g_err.clear();
   g_path.clear();
   noop = false;
@@ -323,7 +369,7 @@ int plan_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alp
     if (overlaps(B, extent_bytes(transB ? N : K, transB ? K : N, ldb, 1), D, d_ext))
       return fail(GEMM_ERR_ALIAS, "D overlaps B");
   }
-  a = GemmI8Args{};
+  a = GemmByteArgs{};
   a.A = A;
   a.B = B;
   a.C = C;
@@ -335,19 +381,19 @@ int plan_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alp
   a.M = (int)M;
   a.N = (int)N;
   a.K = reads_ab ? (int)K : 0;  // no K loop when the product does not contribute
-  a.alpha = alpha;
-  a.beta = beta;
+  a.alpha_i = alpha;
+  a.beta_i = beta;
   a.read_c = reads_c ? 1 : 0;
   a.a_vec16 = ((uintptr_t)A % 16 == 0 && lda % 16 == 0) ? 1 : 0;
   a.b_vec16 = ((uintptr_t)B % 16 == 0 && ldb % 16 == 0) ? 1 : 0;
-  a.tiles_m = (int)((M + i8_tile_m() - 1) / i8_tile_m());
-  a.tiles_n = (int)((N + i8_tile_n() - 1) / i8_tile_n());
+  a.tiles_m = (int)((M + byte_tile_m() - 1) / byte_tile_m());
+  a.tiles_n = (int)((N + byte_tile_n() - 1) / byte_tile_n());
   a.group_m = 8;
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7fffffff)
     return fail(GEMM_ERR_UNSUPPORTED, "too many output tiles for one launch");
   const char* ops = transA ? (transB ? "TT" : "TN") : (transB ? "NT" : "NN");
-  std::snprintf(buf, sizeof buf, "i8 mfma t%dx%dx128 w2x2 a32x32x32 %s epi=%s%s%s", i8_tile_m(),
-                i8_tile_n(), ops, reads_c ? "general" : "beta0",
+  std::snprintf(buf, sizeof buf, "i8 mfma t%dx%dx128 w2x2 a32x32x32 %s epi=%s%s%s", byte_tile_m(),
+                byte_tile_n(), ops, reads_c ? "general" : "beta0",
                 reads_ab ? "" : " (K == 0 or alpha == 0: D = beta*C)",
                 (reads_ab && (!a.a_vec16 || !a.b_vec16)) ? " bytewise staging" : "");
   g_path = buf;
@@ -381,6 +427,8 @@ int gemm(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB, flo
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (plan.scale_only) e = launch_scale_c(plan.args, s);
+    else if (plan.byte8)
+      e = launch_byte(plan.byte_kind, transA != 0, transB != 0, plan.bargs, s);
     else if (plan.mfma)
       e = launch_mfma(plan.tile, dtype & 1, transA != 0, transB != 0, plan.masked, plan.args, s);
     else e = launch_fma(dtype, transA != 0, transB != 0, plan.args, s);
@@ -405,11 +453,12 @@ int gemm_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alp
             const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, const int32_t* C,
             int64_t ldc, int32_t* D, int64_t ldd, void* stream) {
   using namespace dgt;
-  GemmI8Args a;
+  GemmByteArgs a;
   bool noop;
   int st = plan_i8(M, N, K, transA, transB, alpha, beta, A, lda, B, ldb, C, ldc, D, ldd, a, noop);
   if (st == GEMM_OK && !noop) {
-    const hipError_t e = launch_i8(transA != 0, transB != 0, a, static_cast<hipStream_t>(stream));
+    const hipError_t e =
+        launch_byte(BYTE_I8, transA != 0, transB != 0, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
       st = fail(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   }
@@ -420,7 +469,7 @@ int gemm_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alp
 int gemm_i8_validate(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alpha,
                      int32_t beta, const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
                      const int32_t* C, int64_t ldc, const int32_t* D, int64_t ldd) {
-  dgt::GemmI8Args a;
+  dgt::GemmByteArgs a;
   bool noop;
   int st = dgt::plan_i8(M, N, K, transA, transB, alpha, beta, A, lda, B, ldb, C, ldc, D, ldd, a,
                         noop);

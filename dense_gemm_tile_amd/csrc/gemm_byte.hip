@@ -1,0 +1,259 @@
+// Matrix-core GEMM for 1-byte operands, D = alpha*op(A)@op(B) + beta*C:
+//
+//  * int8 x int8 -> int32 (v_mfma_i32_32x32x32_i8): int32 C/D, integer
+//    alpha/beta, all sums and the epilogue wrapping like int32 arithmetic. The
+//    integer form of the same contraction (Phobos `@tensorcore`: an i8 dot
+//    takes the integer tensor cores whenever its shape allows, "When it
+//    declines").
+//  * 8-bit floats (OCP E4M3 or E5M2) -> f32 (v_mfma_scale_f32_32x32x64_f8f6f4
+//    with unit scales): f32 C/D and alpha/beta, the epilogue of the 16-bit
+//    kernels. The fp8 precision of the `gemm_async` variants (TVM `gemm`,
+//    restated: the precision list).
+//
+// Both follow the contraction of TVM TIRx `gemm` ("Algorithm" steps 1-3):
+//
+//  * 128x128 output tile per workgroup, 4 waves (2x2) of 64x64 outputs, each a
+//    2x2 block of 32x32 atoms (16 accumulators per lane per atom);
+//  * K steps of 128 one-byte values: one LDS row per M (or N) index holds 128
+//    bytes, eight 16-byte chunks, chunk c of row r at c ^ ((r ^ (r>>3)) & 7)
+//    (the 16-bit kernels' layout, in bytes). An int8 atom (K = 32) takes 16
+//    consecutive K-values per lane (lanes 0-31 the first 16, lanes 32-63 the
+//    second), one ds_read_b128; an 8-bit float atom (K = 64) takes 32 (two
+//    reads). Any K order shared by A and B gives the same sum, so only the
+//    lane's row/column and its half of the atom's K range have to match the
+//    hardware;
+//  * global -> VGPR -> LDS staging, two LDS stages, the next K step loaded
+//    while the current one is multiplied. K-contiguous operands move in
+//    16-byte pieces when the piece is whole and aligned, bytewise otherwise;
+//    M/N-contiguous operands are read 16 values along M (or N) and written
+//    into their K-contiguous LDS rows byte by byte;
+//  * out-of-range elements are staged as zeros (their products are zero), C
+//    loads and D stores are predicated.
+#include "common.h"
+
+#include <cstdint>
+
+namespace dgt {
+
+namespace {
+
+// Byte offset of 16-byte chunk `chunk` of LDS row `row` (128-byte rows).
+__device__ inline int lds_off_b(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// int8 -> int32 atom: 32 K-values per MFMA, 16 bytes per lane.
+struct KindI8 {
+  using acc_t = i32x16;
+  using frag_t = i32x4;
+  static constexpr int KATOM = 32;
+  __device__ static inline frag_t read(const char* base, int row, int ks, int half) {
+    return *reinterpret_cast<const i32x4*>(base + lds_off_b(row, 2 * ks + half));
+  }
+  __device__ static inline acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline void store(const GemmByteArgs& p, int64_t r, int c, acc_t v, int e) {
+    const int32_t* C = static_cast<const int32_t*>(p.C);
+    unsigned d = (unsigned)p.alpha_i * (unsigned)v[e];
+    if (p.read_c) d += (unsigned)p.beta_i * (unsigned)C[r * p.ldc + c];
+    static_cast<int32_t*>(p.D)[r * p.ldd + c] = (int32_t)d;
+  }
+};
+
+// 8-bit float atom (FMT 0: E4M3, 1: E5M2): 64 K-values per MFMA, 32 bytes per
+// lane; block scales of 1 (E8M0 code 127).
+template <int FMT>
+struct KindF8 {
+  using acc_t = f32x16_t;
+  using frag_t = i32x8;
+  static constexpr int KATOM = 64;
+  __device__ static inline frag_t read(const char* base, int row, int ks, int half) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(base + lds_off_b(row, 4 * ks + 2 * half));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(base + lds_off_b(row, 4 * ks + 2 * half + 1));
+    return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  }
+  __device__ static inline acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, 127, 0, 127);
+  }
+  __device__ static inline void store(const GemmByteArgs& p, int64_t r, int c, acc_t v, int e) {
+    float d = p.alpha_f * v[e];
+    if (p.read_c) d = __builtin_fmaf(p.beta_f, static_cast<const float*>(p.C)[r * p.ldc + c], d);
+    static_cast<float*>(p.D)[r * p.ldd + c] = d;
+  }
+};
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = 128, kBN = 128, kBK = 128, kThreads = 256;
+constexpr int kTM = 2, kTN = 2;           // atoms per wave
+constexpr int kBox = kBM * kBK;           // bytes of one operand box (BM == BN)
+constexpr int kStage = 2 * kBox;
+constexpr int kPieces = kBox / 16 / kThreads;  // 16-byte pieces per thread per operand: 4
+
+// One operand's 128 x 128 box (rows: M or N indices; K) at (r0, k0).
+// KCONTIG: element (r, k) is X[r * ld + k]; otherwise X[k * ld + r].
+template <bool KCONTIG>
+struct ByteStager {
+  u32x4_t v[kPieces];
+
+  __device__ static inline u32x4_t load_bytes(const int8_t* p, int n, int64_t stride) {
+    unsigned w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const unsigned b = q < n ? (unsigned)(uint8_t)p[q * stride] : 0u;
+      w[q >> 2] |= b << (8 * (q & 3));
+    }
+    return u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+
+  // vec16: the operand's base and row pitch are multiples of 16 bytes.
+  __device__ inline void load(const int8_t* __restrict__ X, int64_t ld, int r0, int rlim, int k0,
+                              int klim, int tid, bool vec16) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int id = tid + i * kThreads;
+      if constexpr (KCONTIG) {
+        // piece id: row id / 8, K chunk id % 8
+        const int r = r0 + (id >> 3), k = k0 + ((id & 7) << 4);
+        const int8_t* p = X + (int64_t)r * ld + k;
+        if (r < rlim && k < klim) {
+          v[i] = (vec16 && k + 16 <= klim) ? *reinterpret_cast<const u32x4_t*>(p)
+                                            : load_bytes(p, klim - k, 1);
+        } else {
+          v[i] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+      } else {
+        // piece id: K row id / 8, 16 rows of M (or N) starting at 16 * (id % 8)
+        const int k = k0 + (id >> 3), r = r0 + ((id & 7) << 4);
+        const int8_t* p = X + (int64_t)k * ld + r;
+        if (k < klim && r < rlim) {
+          v[i] = (vec16 && r + 16 <= rlim) ? *reinterpret_cast<const u32x4_t*>(p)
+                                            : load_bytes(p, rlim - r, 1);
+        } else {
+          v[i] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  }
+
+  __device__ inline void store(char* __restrict__ lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int id = tid + i * kThreads;
+      if constexpr (KCONTIG) {
+        *reinterpret_cast<u32x4_t*>(lds + lds_off_b(id >> 3, id & 7)) = v[i];
+      } else {
+        // byte q of the piece is element (row 16 * (id % 8) + q, K id / 8)
+        const int kk = id >> 3, rb = (id & 7) << 4;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const uint8_t b = (uint8_t)(v[i][q >> 2] >> (8 * (q & 3)));
+          lds[lds_off_b(rb + q, kk >> 4) + (kk & 15)] = (char)b;
+        }
+      }
+    }
+  }
+};
+
+template <class Kind, bool TA, bool TB>
+__global__ void __launch_bounds__(kThreads) gemm_byte_kernel(const GemmByteArgs p) {
+  using acc_t = typename Kind::acc_t;
+  using frag_t = typename Kind::frag_t;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int m0 = tm * kBM, n0 = tn * kBN;
+
+  ByteStager<!TA> sa;  // A is K-contiguous unless transposed
+  ByteStager<TB> sb;   // B is K-contiguous only when transposed
+  const int8_t* A = static_cast<const int8_t*>(p.A);
+  const int8_t* B = static_cast<const int8_t*>(p.B);
+  acc_t acc[kTM][kTN];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+
+  const int KT = (p.K + kBK - 1) / kBK;
+  const int a_row0 = wm * 64 + (lane & 31), b_row0 = wn * 64 + (lane & 31);
+  const int half = lane >> 5;  // which half of an atom's K range this lane holds
+
+  if (KT > 0) {
+    sa.load(A, p.lda, m0, p.M, 0, p.K, tid, p.a_vec16);
+    sb.load(B, p.ldb, n0, p.N, 0, p.K, tid, p.b_vec16);
+    sa.store(smem, tid);
+    sb.store(smem + kBox, tid);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < KT; ++kt) {
+    const char* As = smem + (kt & 1) * kStage;
+    const char* Bs = As + kBox;
+    if (kt + 1 < KT) {
+      sa.load(A, p.lda, m0, p.M, (kt + 1) * kBK, p.K, tid, p.a_vec16);
+      sb.load(B, p.ldb, n0, p.N, (kt + 1) * kBK, p.K, tid, p.b_vec16);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kBK / Kind::KATOM; ++ks) {
+      frag_t fa[kTM], fb[kTN];
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) fa[i] = Kind::read(As, a_row0 + 32 * i, ks, half);
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) fb[j] = Kind::read(Bs, b_row0 + 32 * j, ks, half);
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) acc[i][j] = Kind::mma(fa[i], fb[j], acc[i][j]);
+    }
+    if (kt + 1 < KT) {
+      char* nA = smem + ((kt + 1) & 1) * kStage;
+      sa.store(nA, tid);
+      sb.store(nA + kBox, tid);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: accumulator v of lane l in atom (i, j) is row 8*(v/4) + 4*(l/32)
+  // + v%4, column l%32 of the atom.
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int c = n0 + wn * 64 + 32 * j + (lane & 31);
+        if (r < p.M && c < p.N) Kind::store(p, r, c, acc[i][j], v);
+      }
+}
+
+template <class Kind>
+void launch_kind(bool ta, bool tb, const GemmByteArgs& a, hipStream_t s) {
+  const dim3 grid(a.tiles_m * a.tiles_n), block(kThreads);
+  if (!ta && tb) gemm_byte_kernel<Kind, false, true><<<grid, block, 0, s>>>(a);
+  else if (!ta && !tb) gemm_byte_kernel<Kind, false, false><<<grid, block, 0, s>>>(a);
+  else if (ta && tb) gemm_byte_kernel<Kind, true, true><<<grid, block, 0, s>>>(a);
+  else gemm_byte_kernel<Kind, true, false><<<grid, block, 0, s>>>(a);
+}
+
+}  // namespace
+
+hipError_t launch_byte(int kind, bool ta, bool tb, const GemmByteArgs& a, hipStream_t s) {
+  if (kind == BYTE_I8) launch_kind<KindI8>(ta, tb, a, s);
+  else if (kind == BYTE_F8E4M3) launch_kind<KindF8<0>>(ta, tb, a, s);
+  else launch_kind<KindF8<1>>(ta, tb, a, s);
+  return hipGetLastError();
+}
+
+int byte_tile_m() { return kBM; }
+int byte_tile_n() { return kBN; }
+
+}  // namespace dgt

@@ -50,7 +50,7 @@ extern "C" {
  * which reports a failed launch) and sets gemm_last_error(). */
 #define GEMM_OK 0
 #define GEMM_ERR_INVALID_ARG 1 /* negative dim, ld too small, NULL or misaligned pointer */
-#define GEMM_ERR_UNSUPPORTED 2 /* dtype code not 0..3, or a forced path that cannot run */
+#define GEMM_ERR_UNSUPPORTED 2 /* dtype code not 0..5, or a forced path that cannot run */
 #define GEMM_ERR_ALIAS 3       /* D overlaps A or B, or overlaps C other than exactly */
 #define GEMM_ERR_HIP 4         /* a HIP runtime call failed; message has its text */
 
@@ -64,6 +64,13 @@ extern "C" {
  * dimensions still count elements (now 4 bytes each). */
 #define GEMM_DTYPE_F32_F16 2
 #define GEMM_DTYPE_F32_BF16 3
+/* A and B hold 8-bit float codes, OCP E4M3 (bias 7, no infinity, max 448) or
+ * E5M2 (bias 15, IEEE-style specials), multiplied on the 8-bit float matrix
+ * cores with the float32 accumulator and unit block scales: the fp8
+ * precision of the gemm_async variants (TVM gemm, restated: the precision
+ * list). Leading dimensions count bytes; any alignment. */
+#define GEMM_DTYPE_F8_E4M3 4
+#define GEMM_DTYPE_F8_E5M2 5
 
 /*
  * gemm: enqueue D = alpha*op(A)@op(B) + beta*C on `stream`.
@@ -72,15 +79,15 @@ extern "C" {
  *           K == 0 or alpha == 0: D = beta*C (A and B are not read).
  * dtype     GEMM_DTYPE_F16 or GEMM_DTYPE_BF16, the element type of A and B;
  *           or GEMM_DTYPE_F32_F16 / GEMM_DTYPE_F32_BF16 for float32 A and B
- *           rounded to f16 / bf16 while staged (matrix-core path only:
- *           GEMM_FORCE_PATH=fma returns GEMM_ERR_UNSUPPORTED for them).
+ *           rounded to f16 / bf16 while staged; or GEMM_DTYPE_F8_E4M3 /
+ *           GEMM_DTYPE_F8_E5M2 for 8-bit float codes (matrix-core paths only:
+ *           GEMM_FORCE_PATH=fma returns GEMM_ERR_UNSUPPORTED for 2..5).
  * transA/B  0 or 1 (any non-zero means 1). transA: A is stored [K][M];
  *           transB: B is stored [N][K].
  * lda       >= max(1, transA ? M : K), in elements; ldb >= max(1, transB ? K : N);
  *           ldd >= max(1, N); ldc >= max(1, N) when beta != 0.
- * A, B      device pointers, 2-byte aligned (4-byte for float32 operands); may
- *           be NULL only when K == 0 or
- *           alpha == 0.
+ * A, B      device pointers, 2-byte aligned (4-byte for float32 operands, any
+ *           for 8-bit codes); may be NULL only when K == 0 or alpha == 0.
  * C         device float32 pointer, 4-byte aligned; ignored (may be NULL)
  *           when beta == 0.
  * D         device float32 pointer, 4-byte aligned.

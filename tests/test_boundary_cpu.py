@@ -70,7 +70,7 @@ def test_valid_call_selects_mfma(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(M=-1), 1), (dict(N=-5), 1), (dict(K=-2), 1),
-    (dict(dtype=4), 2), (dict(dtype=-1), 2),
+    (dict(dtype=6), 2), (dict(dtype=-1), 2),
     (dict(lda=63), 1), (dict(tA=1, lda=63), 1), (dict(ldb=63), 1), (dict(tB=1, ldb=63), 1),
     (dict(ldd=63), 1), (dict(beta=1.0, ldc=63), 1),
     (dict(D=0), 1), (dict(A=0), 1), (dict(B=0), 1), (dict(beta=0.5, C=0), 1),
@@ -188,6 +188,22 @@ def _v8(lib, M=64, N=64, K=64, tA=0, tB=0, alpha=1, beta=0, A=A0, lda=None, B=B0
     ldc = ldc if ldc is not None else N
     ldd = ldd if ldd is not None else N
     return lib.gemm_i8_validate(M, N, K, tA, tB, alpha, beta, A, lda, B, ldb, C, ldc, D, ldd)
+
+
+def test_fp8_dtypes_take_the_byte_kernel(lib, monkeypatch):
+    assert _v(lib, dtype=lib.GEMM_DTYPE_F8_E4M3, tB=1) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "fp8 e4m3 mfma t128x128x128 w2x2 a32x32x64 NT epi=beta0"
+    assert _v(lib, dtype=lib.GEMM_DTYPE_F8_E5M2, tA=1, beta=0.5) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "fp8 e5m2 mfma t128x128x128 w2x2 a32x32x64 TN epi=general"
+    assert _v(lib, dtype=4, A=A0 + 1, lda=65) == lib.GEMM_OK  # any alignment
+    assert lib.gemm_last_path().endswith("bytewise staging")
+    assert _v(lib, dtype=4, K=0, lda=1, A=0, B=0, beta=2.0) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("scale")
+    # D must not overlap A's 64 x 64 bytes
+    assert _v(lib, dtype=4, D=A0 + 64 * 64 - 4) == lib.GEMM_ERR_ALIAS
+    assert _v(lib, dtype=4, D=A0 + 64 * 64) == lib.GEMM_OK
+    monkeypatch.setenv("GEMM_FORCE_PATH", "fma")
+    assert _v(lib, dtype=5) == lib.GEMM_ERR_UNSUPPORTED
 
 
 def test_i8_form_checks_and_paths(lib):

@@ -168,3 +168,29 @@ def make_i8_inputs(M: int, N: int, K: int, transA: int, transB: int, seed: int):
     B = torch.randint(-128, 128, b_shape, generator=gen, dtype=torch.int8)
     return A, B
 
+
+def fp8_finite_codes(fmt: int) -> torch.Tensor:
+    """The 8-bit codes of finite values: E4M3 (fmt 4) excludes its two NaN
+    codes S.1111.111, E5M2 (fmt 5) its exponent-31 codes (infinities, NaNs)."""
+    c = torch.arange(256, dtype=torch.int32)
+    if fmt == 4:
+        keep = (c & 0x7F) != 0x7F
+    else:
+        keep = ((c >> 2) & 0x1F) != 0x1F
+    return c[keep].to(torch.uint8)
+
+
+def make_fp8_inputs(M: int, N: int, K: int, transA: int, transB: int, fmt: int, seed: int,
+                    lda: Optional[int] = None, ldb: Optional[int] = None):
+    """Seeded 8-bit float operands: codes drawn uniformly from the format's
+    finite codes, in their stored shapes [rows, ld] (A then B)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    codes = fp8_finite_codes(fmt)
+    a_rows, a_cols = (K, M) if transA else (M, K)
+    b_rows, b_cols = (N, K) if transB else (K, N)
+    lda = lda or a_cols
+    ldb = ldb or b_cols
+    A = codes[torch.randint(0, codes.numel(), (a_rows, lda), generator=gen)]
+    B = codes[torch.randint(0, codes.numel(), (b_rows, ldb), generator=gen)]
+    return A, B
+
