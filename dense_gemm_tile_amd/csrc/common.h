@@ -45,6 +45,7 @@ struct GemmByteArgs {
   int read_c;              // beta != 0
   int a_vec16, b_vec16;    // base and row pitch multiples of 16 bytes
   int tiles_m, tiles_n, group_m;
+  int pingpong;  // whole 256x256 NT tiles: the two-group kernel
 };
 enum ByteKind : int { BYTE_I8 = 0, BYTE_F8E4M3 = 1, BYTE_F8E5M2 = 2 };
 
@@ -118,6 +119,7 @@ hipError_t launch_fma(int dtype, bool transA, bool transB, const GemmArgs& a,
 hipError_t launch_byte(int kind, bool ta, bool tb, const GemmByteArgs& a, hipStream_t s);
 int byte_tile_m();
 int byte_tile_n();
+int byte_pp_tile();
 hipError_t launch_scale_c(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace dgt

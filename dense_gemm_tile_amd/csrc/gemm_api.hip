@@ -91,6 +91,23 @@ int choose_tile(int64_t M, int64_t N) {
   return TILE_64x64;
 }
 
+// Whole 256x256 NT tiles of a 1-byte-operand call take the two-group kernel
+// (K a multiple of its 128-byte slices, 16-byte rows, 32-bit load offsets).
+bool byte_pingpong(const GemmByteArgs& b, int transA, int transB) {
+  const int t = byte_pp_tile();
+  const int64_t ldmax = b.lda > b.ldb ? b.lda : b.ldb;
+  return !transA && transB && b.M % t == 0 && b.N % t == 0 && b.K > 0 && b.K % 128 == 0 &&
+         b.a_vec16 && b.b_vec16 && ldmax * t + 4096 < (int64_t{1} << 31);
+}
+
+void set_byte_tiles(GemmByteArgs& b, int transA, int transB) {
+  b.pingpong = byte_pingpong(b, transA, transB) ? 1 : 0;
+  const int tm = b.pingpong ? byte_pp_tile() : byte_tile_m();
+  const int tn = b.pingpong ? byte_pp_tile() : byte_tile_n();
+  b.tiles_m = (int)((b.M + tm - 1) / tm);
+  b.tiles_n = (int)((b.N + tn - 1) / tn);
+}
+
 int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB, float alpha,
               float beta, const void* A, int64_t lda, const void* B, int64_t ldb, const float* C,
               int64_t ldc, const float* D, int64_t ldd, Plan& plan) {
@@ -228,17 +245,18 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     b.read_c = reads_c ? 1 : 0;
     b.a_vec16 = ((uintptr_t)A % 16 == 0 && lda % 16 == 0) ? 1 : 0;
     b.b_vec16 = ((uintptr_t)B % 16 == 0 && ldb % 16 == 0) ? 1 : 0;
-    b.tiles_m = (int)((M + byte_tile_m() - 1) / byte_tile_m());
-    b.tiles_n = (int)((N + byte_tile_n() - 1) / byte_tile_n());
+    set_byte_tiles(b, transA, transB);
     b.group_m = 8;
     if ((int64_t)b.tiles_m * b.tiles_n > 0x7fffffff)
       return fail(GEMM_ERR_UNSUPPORTED, "too many output tiles for one launch");
     plan.byte8 = true;
     plan.byte_kind = dtype == GEMM_DTYPE_F8_E4M3 ? BYTE_F8E4M3 : BYTE_F8E5M2;
     const char* ops8 = transA ? (transB ? "TT" : "TN") : (transB ? "NT" : "NN");
-    std::snprintf(buf, sizeof buf, "fp8 %s mfma t%dx%dx128 w2x2 a32x32x64 %s epi=%s%s",
-                  dtype == GEMM_DTYPE_F8_E4M3 ? "e4m3" : "e5m2", byte_tile_m(), byte_tile_n(),
-                  ops8, epi_name, (!b.a_vec16 || !b.b_vec16) ? " bytewise staging" : "");
+    const int t8 = b.pingpong ? byte_pp_tile() : byte_tile_m();
+    std::snprintf(buf, sizeof buf, "fp8 %s mfma t%dx%dx128 %s a32x32x64 %s epi=%s%s%s",
+                  dtype == GEMM_DTYPE_F8_E4M3 ? "e4m3" : "e5m2", t8, t8,
+                  b.pingpong ? "w2x4" : "w2x2", ops8, epi_name, b.pingpong ? " pingpong" : "",
+                  (!b.a_vec16 || !b.b_vec16) ? " bytewise staging" : "");
     g_path = buf;
     return GEMM_OK;
   }
@@ -386,14 +404,15 @@ int plan_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alp
   a.read_c = reads_c ? 1 : 0;
   a.a_vec16 = ((uintptr_t)A % 16 == 0 && lda % 16 == 0) ? 1 : 0;
   a.b_vec16 = ((uintptr_t)B % 16 == 0 && ldb % 16 == 0) ? 1 : 0;
-  a.tiles_m = (int)((M + byte_tile_m() - 1) / byte_tile_m());
-  a.tiles_n = (int)((N + byte_tile_n() - 1) / byte_tile_n());
+  set_byte_tiles(a, transA, transB);
   a.group_m = 8;
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7fffffff)
     return fail(GEMM_ERR_UNSUPPORTED, "too many output tiles for one launch");
   const char* ops = transA ? (transB ? "TT" : "TN") : (transB ? "NT" : "NN");
-  std::snprintf(buf, sizeof buf, "i8 mfma t%dx%dx128 w2x2 a32x32x32 %s epi=%s%s%s", byte_tile_m(),
-                byte_tile_n(), ops, reads_c ? "general" : "beta0",
+  const int t8 = a.pingpong ? byte_pp_tile() : byte_tile_m();
+  std::snprintf(buf, sizeof buf, "i8 mfma t%dx%dx128 %s a32x32x32 %s epi=%s%s%s%s", t8, t8,
+                a.pingpong ? "w2x4" : "w2x2", ops, reads_c ? "general" : "beta0",
+                a.pingpong ? " pingpong" : "",
                 reads_ab ? "" : " (K == 0 or alpha == 0: D = beta*C)",
                 (reads_ab && (!a.a_vec16 || !a.b_vec16)) ? " bytewise staging" : "");
   g_path = buf;

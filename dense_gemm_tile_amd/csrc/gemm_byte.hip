@@ -29,7 +29,7 @@
 //    into their K-contiguous LDS rows byte by byte;
 //  * out-of-range elements are staged as zeros (their products are zero), C
 //    loads and D stores are predicated.
-#include "common.h"
+#include "gemm_mfma_pingpong.h"
 
 #include <cstdint>
 
@@ -55,6 +55,12 @@ struct KindI8 {
   __device__ static inline frag_t read(const char* base, int row, int ks, int half) {
     return *reinterpret_cast<const i32x4*>(base + lds_off_b(row, 2 * ks + half));
   }
+  // Same read from a precomputed offset: off = lds_off_b(row, CHUNK0 * half);
+  // the chunk of sub-step ks differs by bits the swizzle leaves alone.
+  static constexpr int CHUNK0 = 1;
+  __device__ static inline frag_t read_off(const char* base, int off, int ks) {
+    return *reinterpret_cast<const i32x4*>(base + (off ^ (ks << 5)));
+  }
   __device__ static inline acc_t mma(frag_t a, frag_t b, acc_t c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
   }
@@ -76,6 +82,12 @@ struct KindF8 {
   __device__ static inline frag_t read(const char* base, int row, int ks, int half) {
     const i32x4 lo = *reinterpret_cast<const i32x4*>(base + lds_off_b(row, 4 * ks + 2 * half));
     const i32x4 hi = *reinterpret_cast<const i32x4*>(base + lds_off_b(row, 4 * ks + 2 * half + 1));
+    return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  }
+  static constexpr int CHUNK0 = 2;
+  __device__ static inline frag_t read_off(const char* base, int off, int ks) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(base + (off ^ ((4 * ks) << 4)));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(base + (off ^ ((4 * ks + 1) << 4)));
     return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   }
   __device__ static inline acc_t mma(frag_t a, frag_t b, acc_t c) {
@@ -235,8 +247,139 @@ __global__ void __launch_bounds__(kThreads) gemm_byte_kernel(const GemmByteArgs 
       }
 }
 
+// Whole 256x256 tiles of the NT layout on the two-group ping-pong design of
+// the 16-bit kernels (gemm_mfma_pingpong.h): a K slice is 128 bytes of each
+// row, the same bytes per slice and the same LDS ring, loads and phases; only
+// the atom (int8 or 8-bit float), the fragment reads and the epilogue differ.
+// A slice is 4 int8 or 2 fp8 sub-steps of 8 MFMAs per wave, each MFMA twice
+// the 16-bit one's work at twice its rate, so a compute phase stays about
+// 1024 cycles.
+template <class Kind>
+struct PpByteFrags {
+  typename Kind::frag_t a[4], b[2];
+};
+
+template <class Kind>
+__global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(const GemmByteArgs p) {
+  using C = PingPongCfg;
+  using acc_t = typename Kind::acc_t;
+  constexpr int KS = 128 / Kind::KATOM;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2, lw = wave & 3;
+  const int wm = group, wn = lw;
+  int tm, tn;
+  schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+
+  PpOperand<false, C::TM> a;
+  PpOperand<false, C::TN> b;
+  a.init_load(p.A, p.lda, m0, lw, lane, 1);
+  b.init_load(p.B, p.ldb, n0, lw, lane, 1);
+  const int half = lane >> 5;
+  int offA[C::TM], offB[C::TN];  // fragment offsets within a slot, sub-step 0
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+    offA[i] = lds_off_b(wm * C::WTM + 32 * i + (lane & 31), Kind::CHUNK0 * half);
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j)
+    offB[j] = lds_off_b(wn * C::WTN + 32 * j + (lane & 31), Kind::CHUNK0 * half);
+
+  acc_t acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+
+  auto issue = [&](const PpOperand<false, C::TM>& x, int slice, int slot) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) x.issue(smem + slot * C::SLOT_BYTES, lw, i, slice);
+  };
+  auto issue_b = [&](int slice, int slot) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) b.issue(smem + slot * C::SLOT_BYTES, lw, i, slice);
+  };
+
+  // Phases as in pp_mainloop: group 0 reads slice s in phase 2s+1 and
+  // multiplies it in 2s+2, group 1 one phase later; A of slice t in slot
+  // 2t % 5 (loaded by group 1), B in slot (2t+1) % 5 (loaded by group 0).
+  const int KT = p.K / 128;
+  if (group == 1) {
+    issue(a, 0, 0);
+    if (KT > 1) {
+      issue(a, 1, 2);
+      pp_wait_vm<C::LOADS>();
+    } else {
+      pp_wait_vm<0>();
+    }
+  } else {
+    issue_b(0, 1);
+    pp_wait_vm<0>();
+  }
+  pp_barrier();
+  if (group == 1) {
+    pp_wait_vm<0>();
+    pp_barrier();
+  }
+  PpByteFrags<Kind> f[KS];
+  int h = 0;
+  for (int s = 0; s < KT; ++s) {
+    asm volatile("" : "+v"(a.row), "+v"(a.c0), "+v"(b.row), "+v"(b.c0));
+    asm volatile("" : "+v"(offA[0]), "+v"(offA[1]), "+v"(offA[2]), "+v"(offA[3]),
+                 "+v"(offB[0]), "+v"(offB[1]));
+    const int sa = h, sb = h == 4 ? 0 : h + 1;
+    const char* pa = smem + sa * C::SLOT_BYTES;
+    const char* pb = smem + sb * C::SLOT_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) f[ks].a[i] = Kind::read_off(pa, offA[i], ks);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) f[ks].b[j] = Kind::read_off(pb, offB[j], ks);
+    }
+    if (group == 0) {
+      if (s + 1 < KT) issue_b(s + 1, h >= 2 ? h - 2 : h + 3);
+      pp_wait_lgkm0();
+    } else {
+      const bool ld = s + 2 < KT;
+      if (ld) issue(a, s + 2, h >= 1 ? h - 1 : h + 4);
+      if (ld) pp_wait_vm_lgkm0<C::LOADS>();
+      else pp_wait_vm_lgkm0<0>();
+    }
+    pp_barrier();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = Kind::mma(f[ks].a[i], f[ks].b[j], acc[i][j]);
+    if (group == 0) pp_wait_vm<0>();
+    pp_barrier();
+    h = h >= 3 ? h - 3 : h + 2;
+  }
+  if (group == 0) pp_barrier();
+
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = m0 + wm * C::WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int c = n0 + wn * C::WTN + 32 * j + (lane & 31);
+        Kind::store(p, r, c, acc[i][j], v);
+      }
+}
+
 template <class Kind>
 void launch_kind(bool ta, bool tb, const GemmByteArgs& a, hipStream_t s) {
+  if (a.pingpong) {
+    gemm_pp_byte_kernel<Kind><<<dim3(a.tiles_m * a.tiles_n), dim3(PingPongCfg::THREADS), 0, s>>>(a);
+    return;
+  }
   const dim3 grid(a.tiles_m * a.tiles_n), block(kThreads);
   if (!ta && tb) gemm_byte_kernel<Kind, false, true><<<grid, block, 0, s>>>(a);
   else if (!ta && !tb) gemm_byte_kernel<Kind, false, false><<<grid, block, 0, s>>>(a);
@@ -255,5 +398,6 @@ hipError_t launch_byte(int kind, bool ta, bool tb, const GemmByteArgs& a, hipStr
 
 int byte_tile_m() { return kBM; }
 int byte_tile_n() { return kBN; }
+int byte_pp_tile() { return PingPongCfg::BM; }
 
 }  // namespace dgt

@@ -103,17 +103,20 @@ template <int NFRAG>
 struct PpOperand<false, NFRAG> {
   using C = PingPongCfg;
   // Load side: this lane's byte offset for instruction 0 and its chunk.
-  const uint16_t* base;  // tile's first row (M or N index), K = 0
-  int ld2, row, c0;
+  const char* base;  // tile's first row (M or N index), K = 0
+  int ld2, row, c0;  // ld2: row pitch in bytes
   // Read side: byte offset of each atom's fragment within a slot, sub-step 0.
   int off[NFRAG];
 
   __device__ static inline int lds_off(int r, int chunk) {
     return r * 128 + ((chunk ^ ((r ^ (r >> 3)) & 7)) << 4);
   }
-  __device__ inline void init_load(const uint16_t* X, int64_t ld, int r0, int lw, int lane) {
-    base = X + (int64_t)r0 * ld;
-    ld2 = (int)(ld * 2);
+  // esz: bytes per element (2 for f16/bf16; 1 for the 1-byte-operand
+  // kernels, whose 128-byte rows hold 128 K-values).
+  __device__ inline void init_load(const void* X, int64_t ld, int r0, int lw, int lane,
+                                   int esz = 2) {
+    base = static_cast<const char*>(X) + (int64_t)r0 * ld * esz;
+    ld2 = (int)(ld * esz);
     // Instruction i of wave lw covers rows 64*lw + 8i .. +7. Lane l fills
     // chunk slot l%8 of row 64*lw + 8i + l/8, whose swizzle is (l/8) ^ i, so
     // it fetches chunk (l%8) ^ (l/8) ^ i of that row.
@@ -122,7 +125,7 @@ struct PpOperand<false, NFRAG> {
   }
   __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
     const int voff = row + ((c0 ^ i) << 4);
-    const int soff = slice * (C::BK * 2) + i * 8 * ld2;
+    const int soff = slice * 128 + i * 8 * ld2;  // a slice is 128 bytes of each row
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
                                              16, voff, soff, 0, 0);
   }

@@ -114,3 +114,33 @@ def test_fp8_full_size_sampled_rows():
     D_ref, bound = oracle.gemm_reference(M, N, K, 4, 0, 1, 1.0, 0.0, A.numpy().reshape(-1), K,
                                          B.numpy().reshape(-1), K, rows=rows)
     assert oracle.check(D[rows].cpu().numpy().astype(np.float64), D_ref, bound)["ok"]
+
+
+@pytest.mark.parametrize("dt", ["f8e4m3", "f8e5m2"])
+def test_fp8_pingpong_whole_tiles_slice_counts(dt):
+    """Whole 256x256 NT tiles take the two-group kernel: K from one 128-byte
+    slice to several turns of the five-slot ring, padded leading dimensions."""
+    seed = 950
+    for K in (128, 256, 384, 640, 1152):
+        seed += 1
+        M, N = 512, 768
+        lda, ldb = K + (16 if seed % 2 else 0), K + 32
+        D, D_ref, bound, path = run_fp8(dt, M, N, K, 0, 1, 0.5, -1.0, seed=seed, lda=lda,
+                                        ldb=ldb, ldd=N + 4)
+        assert "pingpong" in path, path
+        assert oracle.check(D[:M, :N].astype(np.float64), D_ref, bound)["ok"], (dt, K)
+        assert np.all(D[:M, N:].view(np.uint32) == D_SENTINEL)
+
+
+def test_fp8_pingpong_exact_small_integers():
+    rng = np.random.default_rng(8)
+    M, N, K = 256, 512, 384
+    table = {-2: 0xC0, -1: 0xB8, 0: 0x00, 1: 0x38, 2: 0x40}
+    av = rng.integers(-2, 3, (M, K))
+    bv = rng.integers(-2, 3, (N, K))
+    enc = np.vectorize(lambda v: table[int(v)])
+    A = torch.from_numpy(enc(av).astype(np.uint8))
+    B = torch.from_numpy(enc(bv).astype(np.uint8))
+    D, _, _, path = run_fp8("f8e4m3", M, N, K, 0, 1, 1.0, 0.0, A=A, B=B)
+    assert "pingpong" in path, path
+    assert np.array_equal(D[:M, :N], (av @ bv.T).astype(np.float32))

@@ -120,3 +120,20 @@ def test_i8_full_size_sampled_rows():
     ref = oracle.gemm_reference_i8(M, N, K, 0, 1, 1, 0, A, K, B, K, rows=rows)
     got = Dd.cpu().numpy().reshape(M, N)[rows]
     assert np.array_equal(got, ref)
+
+
+def test_i8_pingpong_whole_tiles_slice_counts():
+    """Whole 256x256 NT tiles take the two-group kernel: K from one 128-byte
+    slice (prologue only) to several turns of the five-slot ring, padded
+    leading dimensions, both epilogues; bit-exact."""
+    seed = 900
+    for K in (128, 256, 384, 512, 640, 1152):
+        for alpha, beta in [(1, 0), (-7, 3)]:
+            seed += 1
+            M, N = 512, 768
+            lda, ldb = K + (16 if seed % 2 else 0), K + (32 if seed % 3 == 0 else 0)
+            got, ref, path = run_i8(M, N, K, 0, 1, alpha, beta, seed=seed, lda=lda, ldb=ldb,
+                                    ldd=N + 4)
+            assert "pingpong" in path, path
+            assert np.array_equal(got[:M, :N], ref), (K, alpha, beta)
+            assert np.all(got[:M, N:] == SENTINEL)
