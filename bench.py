@@ -243,6 +243,41 @@ def bench_fp8(args):
     }), flush=True)
 
 
+# Workloads whose operands fit in the 256 MB MALL: their hot time (operands left in
+# L2/MALL by the previous call) and cold time (a 1 GiB buffer written between calls)
+# differ, so both are reported.
+PER_CALL_DEFAULT = ("atom16x8x16", "gemm512", "ragged4097x1000x1032_tn")
+
+
+def per_call_timing(step, stream, n):
+    """Median and minimum of n individually timed calls, hot and cold.
+
+    Each call sits between its own pair of HIP events on the launch stream. Hot:
+    calls back to back. Cold: a 1 GiB fill between calls (outside the event pair)
+    evicts L2 and the MALL, so the operands come from HBM."""
+    import torch
+
+    def run(scrub):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i, (e0, e1) in enumerate(evs):
+            if scrub is not None:
+                scrub.fill_(float(i & 7))
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+        return {"median_us": round(ts[n // 2], 3), "min_us": round(ts[0], 3)}
+
+    hot = run(None)
+    with torch.cuda.stream(stream):
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device=stream.device)
+        cold = run(scrub)
+    del scrub
+    return {"samples": n, "hot": hot, "cold": cold}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,6 +288,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--per-call", type=int, default=None,
+                    help="samples of per-call hot and cold timing (default: 200 for the "
+                         "workloads that fit in the MALL, 0 otherwise)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -311,6 +349,11 @@ def main():
     wall = time.perf_counter() - w0
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = gpu_ms / args.steps
+
+    n_per_call = args.per_call
+    if n_per_call is None:
+        n_per_call = 200 if cfg.name in PER_CALL_DEFAULT else 0
+    per_call = per_call_timing(step, stream, n_per_call) if n_per_call > 0 else None
 
     # Parity of what was timed: a fresh call, then sampled rows against the oracle.
     max_rel = None
@@ -376,6 +419,10 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "roofline": roofline,
     }
+    if per_call is not None:
+        for k in ("hot", "cold"):
+            per_call[k]["gbs_at_median"] = round(alg_bytes / (per_call[k]["median_us"] * 1e-6) / 1e9, 1)
+        out["per_call"] = per_call
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

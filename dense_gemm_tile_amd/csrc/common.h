@@ -102,11 +102,12 @@ struct MfmaTileInfo {
   int bm, bn, bk;
   int waves_m, waves_n;
   int atom_m, atom_n, atom_k;
+  int kg;  // K groups: waves split K kg ways within one workgroup
 };
 
 // Matrix-core tile configurations, largest first.
 enum MfmaTile : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x64 = 2, TILE_16x16 = 3,
-                      NUM_MFMA_TILES = 4 };
+                      TILE_32x32K4 = 4, NUM_MFMA_TILES = 5 };
 const MfmaTileInfo& mfma_tile_info(int tile);
 
 hipError_t launch_mfma(int tile, int dtype, bool transA, bool transB, bool masked,

@@ -80,7 +80,10 @@ std::string pitch_reason(const char* name, const void* ptr, int64_t ld, int vw, 
   return buf;
 }
 
-int choose_tile(int64_t M, int64_t N) {
+// Largest tile that still gives every CU work; grids that even 64x64 tiles
+// leave under-filled (fewer than 256 tiles) take 32x32 tiles with K split
+// over four wave groups once K holds a step of 64 for each group.
+int choose_tile(int64_t M, int64_t N, int64_t K) {
   auto count = [&](int t) {
     const MfmaTileInfo& ti = mfma_tile_info(t);
     return ((M + ti.bm - 1) / ti.bm) * ((N + ti.bn - 1) / ti.bn);
@@ -88,6 +91,8 @@ int choose_tile(int64_t M, int64_t N) {
   if (count(TILE_256x256) >= 256) return TILE_256x256;
   if (count(TILE_128x128) >= 128) return TILE_128x128;
   if (M <= 16 && N <= 16) return TILE_16x16;
+  const MfmaTileInfo& k4 = mfma_tile_info(TILE_32x32K4);
+  if (count(TILE_64x64) < 256 && K >= (int64_t)k4.bk * k4.kg) return TILE_32x32K4;
   return TILE_64x64;
 }
 
@@ -291,7 +296,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     return GEMM_OK;
   }
 
-  int tile = choose_tile(M, N);
+  int tile = choose_tile(M, N, K);
   if (const char* ft = env("GEMM_FORCE_TILE")) {
     int found = -1;
     for (int t = 0; t < NUM_MFMA_TILES; ++t)
@@ -303,7 +308,8 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   const MfmaTileInfo& ti = mfma_tile_info(tile);
   plan.mfma = true;
   plan.tile = tile;
-  plan.masked = (M % ti.bm) || (N % ti.bn) || (K % ti.bk);
+  // With K groups, the unmasked kernel needs every group's every step whole.
+  plan.masked = (M % ti.bm) || (N % ti.bn) || (K % ((int64_t)ti.bk * ti.kg));
   // The unmasked kernels address an operand box through a buffer resource
   // with 32-bit byte offsets spanning up to max(bm, bn, bk) rows of the
   // operand; larger pitches take the masked kernels' 64-bit addressing.
@@ -327,9 +333,11 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   // A last K step whose valid part ends within the first half of a 16x16x32
   // sub-step finishes with v_mfma_f32_16x16x16 (no product of staged zeros).
   const bool k16_tail = ti.atom_k == 32 && K % 32 >= 1 && K % 32 <= 16;
-  std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s%s", ti.name,
+  char ksplit[32] = "";
+  if (ti.kg > 1) std::snprintf(ksplit, sizeof ksplit, " ksplit%d", ti.kg);
+  std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s%s%s", ti.name,
                 ti.waves_m, pingpong ? 4 : ti.waves_n, ti.atom_m, ti.atom_n, ti.atom_k, ops,
-                epi_name, pingpong ? " pingpong" : "", plan.masked ? " masked" : "",
+                epi_name, ksplit, pingpong ? " pingpong" : "", plan.masked ? " masked" : "",
                 k16_tail ? " k16-tail" : "",
                 !src32 ? "" : dtype == GEMM_DTYPE_F32_BF16 ? " f32->bf16" : " f32->f16",
                 elem_reason.empty() ? "" : " narrow staging (", elem_reason.c_str(),

@@ -6,13 +6,14 @@ namespace dgt {
 namespace {
 template <class C>
 constexpr MfmaTileInfo info(const char* name) {
-  return MfmaTileInfo{name, C::BM, C::BN, C::BK, C::WM, C::WN, C::At::M, C::At::N, C::At::K};
+  return MfmaTileInfo{name, C::BM, C::BN, C::BK, C::WM, C::WN, C::At::M, C::At::N, C::At::K, C::KG};
 }
 const MfmaTileInfo kTiles[NUM_MFMA_TILES] = {
     info<Cfg256>("t256x256x64"),
     info<Cfg128>("t128x128x64"),
     info<Cfg64>("t64x64x64"),
     info<Cfg16>("t16x16x64"),
+    info<Cfg32k4>("t32x32x64k4"),
 };
 }  // namespace
 
@@ -25,6 +26,7 @@ hipError_t launch_mfma(int tile, int dtype, bool ta, bool tb, bool masked, const
     case TILE_128x128: return launch_mfma_128(dtype, ta, tb, masked, a, s);
     case TILE_64x64: return launch_mfma_64(dtype, ta, tb, masked, a, s);
     case TILE_16x16: return launch_mfma_16(dtype, ta, tb, masked, a, s);
+    case TILE_32x32K4: return launch_mfma_32k4(dtype, ta, tb, masked, a, s);
     default: return hipErrorInvalidValue;
   }
 }

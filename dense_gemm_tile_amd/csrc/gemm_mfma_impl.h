@@ -100,20 +100,30 @@ struct Atom<16> {  // v_mfma_f32_16x16x32_*: 4 f32 accumulators per lane
 };
 
 // --------------------------------------------------------- configuration ----
-template <int BM_, int BN_, int WM_, int WN_, int ATOM_>
+// KG > 1 splits K over KG groups of WM x WN waves: group g takes K steps
+// g, g + KG, g + 2KG, ... of the same output tile into its own pair of LDS
+// stages, and the groups' accumulators are summed through LDS in group order
+// at the end (a fixed order, so results do not vary from run to run).
+template <int BM_, int BN_, int WM_, int WN_, int ATOM_, int KG_ = 1>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = 64;
-  static constexpr int WM = WM_, WN = WN_;
-  static constexpr int THREADS = WM * WN * 64;
+  static constexpr int WM = WM_, WN = WN_, KG = KG_;
+  static constexpr int GROUP_THREADS = WM * WN * 64;  // one K group
+  static constexpr int THREADS = GROUP_THREADS * KG;
   using At = Atom<ATOM_>;
   static constexpr int WTM = BM / WM, WTN = BN / WN;     // one wave's sub-tile
   static constexpr int TM = WTM / At::M, TN = WTN / At::N;  // atoms per wave
   static constexpr int KSTEPS = BK / At::K;
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int GROUP_LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int LDS_BYTES = KG * GROUP_LDS_BYTES;
+  // Accumulators that groups 1..KG-1 hand to group 0 (f32, lane-major).
+  static constexpr int XFER_BYTES = (KG - 1) * WM * WN * TM * TN * At::NACC * 64 * 4;
   static_assert(WTM % At::M == 0 && WTN % At::N == 0, "wave tile must hold whole atoms");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+  static_assert(XFER_BYTES <= LDS_BYTES, "the K-group sum is staged in the operand LDS");
+  static_assert(THREADS <= 1024, "at most 1024 threads per workgroup");
 };
 
 // Byte offset of 16-byte chunk `chunk` (0..7) of LDS row `row` (128 bytes).
@@ -477,18 +487,24 @@ __device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::T
 //     fragments of step kt+1 from nb, and only then run the MFMAs of the last
 //     sub-step of kt, which hide that LDS latency.
 // Global loads therefore have almost two K steps of MFMA work to land.
+// With K groups (Cfg::KG > 1) every group runs this pipeline on its own K
+// steps; all groups run the same number of steps (a group's steps past the
+// end of K stage zeros, which the host guarantees by masking such shapes).
 template <class Cfg, class Tag, bool TA, bool TB, bool MASK, int EPI>
 __global__ void __launch_bounds__(Cfg::THREADS)
 gemm_mfma_kernel(const GemmArgs p) {
   using At = typename Cfg::At;
   using acc_t = typename At::acc_t;
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / Cfg::WN;
-  const int wn = wave % Cfg::WN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int grp = wave / (Cfg::WM * Cfg::WN);        // K group
+  const int gwave = wave % (Cfg::WM * Cfg::WN);      // wave within its group
+  const int tid = threadIdx.x % Cfg::GROUP_THREADS;  // thread within its group
+  const int wm = gwave / Cfg::WN;
+  const int wn = gwave % Cfg::WN;
+  char* const smem = lds + grp * Cfg::GROUP_LDS_BYTES;
 
   int tm, tn;
   schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
@@ -497,8 +513,8 @@ gemm_mfma_kernel(const GemmArgs p) {
 
   // A box rows are M indices; B box rows are N indices. A is K-contiguous
   // unless transposed; B is K-contiguous only when transposed.
-  Stager<Cfg::BM, Cfg::THREADS, !TA, MASK> sa;
-  Stager<Cfg::BN, Cfg::THREADS, TB, MASK> sb;
+  Stager<Cfg::BM, Cfg::GROUP_THREADS, !TA, MASK> sa;
+  Stager<Cfg::BN, Cfg::GROUP_THREADS, TB, MASK> sb;
 
   acc_t acc[Cfg::TM][Cfg::TN];
 #pragma unroll
@@ -508,21 +524,23 @@ gemm_mfma_kernel(const GemmArgs p) {
 #pragma unroll
       for (int v = 0; v < At::NACC; ++v) acc[i][j][v] = 0.0f;
 
-  const int KT = (p.K + Cfg::BK - 1) / Cfg::BK;
+  // This group's K steps: kstep(kt) is the first K index of its kt-th step.
+  const int KT = ((p.K + Cfg::BK - 1) / Cfg::BK + Cfg::KG - 1) / Cfg::KG;
+  auto kstep = [&](int kt) { return (kt * Cfg::KG + grp) * Cfg::BK; };
   const int a_row0 = wm * Cfg::WTM + At::frag_row(lane);
   const int b_row0 = wn * Cfg::WTN + At::frag_row(lane);
   const int koct = At::frag_koct(lane);
   constexpr int CPS = At::K / 8;  // 16-byte chunks per K sub-step
 
   // Prologue: step 0 into buffer 0, step 1 into registers, first fragments.
-  sa.load(p.A, p.lda, m0, p.M, 0, p.K, tid, p.a_vw, p.src32);
-  sb.load(p.B, p.ldb, n0, p.N, 0, p.K, tid, p.b_vw, p.src32);
+  sa.load(p.A, p.lda, m0, p.M, kstep(0), p.K, tid, p.a_vw, p.src32);
+  sb.load(p.B, p.ldb, n0, p.N, kstep(0), p.K, tid, p.b_vw, p.src32);
   sa.store(smem, tid);
   sb.store(smem + Cfg::A_BYTES, tid);
   __syncthreads();
   if (KT > 1) {
-    sa.load(p.A, p.lda, m0, p.M, Cfg::BK, p.K, tid, p.a_vw, p.src32);
-    sb.load(p.B, p.ldb, n0, p.N, Cfg::BK, p.K, tid, p.b_vw, p.src32);
+    sa.load(p.A, p.lda, m0, p.M, kstep(1), p.K, tid, p.a_vw, p.src32);
+    sb.load(p.B, p.ldb, n0, p.N, kstep(1), p.K, tid, p.b_vw, p.src32);
   }
   Frags<Cfg> cur, nxt;
   read_frags<Cfg>(cur, smem, smem + Cfg::A_BYTES, a_row0, b_row0, koct);
@@ -532,10 +550,11 @@ gemm_mfma_kernel(const GemmArgs p) {
     const char* Bs = As + Cfg::A_BYTES;
     // K tails on the 16x16x32 atom only: on the 32x32 atoms the tail saves
     // little and the extra control flow around 256 accumulators makes the
-    // compiler spill them.
+    // compiler spill them. A group's last step may lie wholly past K
+    // (krem <= 0: nothing runs) or be whole (krem >= BK: every sub-step runs).
     if constexpr (MASK && At::K == 32) {
       if (kt == KT - 1) {
-        k_tail<Cfg, Tag>(acc, cur, As, Bs, a_row0, b_row0, lane, p.K - kt * Cfg::BK);
+        k_tail<Cfg, Tag>(acc, cur, As, Bs, a_row0, b_row0, lane, p.K - kstep(kt));
         break;
       }
     }
@@ -551,7 +570,7 @@ gemm_mfma_kernel(const GemmArgs p) {
       sb.store(nA + Cfg::A_BYTES, tid);
       __syncthreads();
       if (kt + 2 < KT) {
-        const int k0 = (kt + 2) * Cfg::BK;
+        const int k0 = kstep(kt + 2);
         sa.load(p.A, p.lda, m0, p.M, k0, p.K, tid, p.a_vw, p.src32);
         sb.load(p.B, p.ldb, n0, p.N, k0, p.K, tid, p.b_vw, p.src32);
       }
@@ -559,6 +578,38 @@ gemm_mfma_kernel(const GemmArgs p) {
     }
     mma_step<Cfg, Tag>(acc, cur);
     cur = nxt;
+  }
+
+  if constexpr (Cfg::KG > 1) {
+    // Groups 1..KG-1 hand their accumulators to group 0 through LDS (lane-
+    // major, so each store and load is one contiguous 256-byte row per
+    // register); group 0 adds them in group order and runs the epilogue.
+    constexpr int NREG = Cfg::TM * Cfg::TN * At::NACC;
+    float* xfer = reinterpret_cast<float*>(lds);
+    __syncthreads();  // every group is done reading its operand stages
+    if (grp > 0) {
+      float* dst = xfer + ((grp - 1) * (Cfg::WM * Cfg::WN) + gwave) * NREG * 64 + lane;
+#pragma unroll
+      for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+          for (int v = 0; v < At::NACC; ++v)
+            dst[((i * Cfg::TN + j) * At::NACC + v) * 64] = acc[i][j][v];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < Cfg::KG; ++g) {
+      const float* src = xfer + ((g - 1) * (Cfg::WM * Cfg::WN) + gwave) * NREG * 64 + lane;
+#pragma unroll
+      for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+          for (int v = 0; v < At::NACC; ++v)
+            acc[i][j][v] += src[((i * Cfg::TN + j) * At::NACC + v) * 64];
+    }
   }
 
   store_tile<Cfg, EPI, MASK>(acc, p, m0 + wm * Cfg::WTM, n0 + wn * Cfg::WTN, lane);
@@ -604,10 +655,13 @@ using Cfg256 = TileCfg<256, 256, 2, 2, 32>;
 using Cfg128 = TileCfg<128, 128, 2, 2, 32>;
 using Cfg64 = TileCfg<64, 64, 2, 2, 16>;
 using Cfg16 = TileCfg<16, 16, 1, 1, 16>;
+// Under-filled grids: 32x32 tiles, K split over four one-wave groups.
+using Cfg32k4 = TileCfg<32, 32, 1, 1, 32, 4>;
 
 hipError_t launch_mfma_256(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mfma_128(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mfma_64(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mfma_16(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_32k4(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 
 }  // namespace dgt

@@ -247,7 +247,25 @@ def test_tile_and_epilogue_choice(lib):
     assert _v(lib, M=4096, N=4096, K=4096, dtype=1, beta=1.0, C=D0) == lib.GEMM_OK
     assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 NN epi=acc+c pingpong"
     assert _v(lib, M=512, N=512, K=512, alpha=1.5, beta=0.5) == lib.GEMM_OK
-    assert "epi=general" in lib.gemm_last_path()
+    assert lib.gemm_last_path() == "mfma t32x32x64k4 w1x1 a32x32x16 NN epi=general ksplit4"
+
+
+def test_k_split_tile_choice(lib):
+    # 64x64 tiles would leave CUs idle: 32x32 tiles, K split over 4 wave groups
+    assert _v(lib, M=1000, N=500, K=256) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma t32x32x64k4 ")
+    assert " ksplit4 masked" in lib.gemm_last_path()
+    # too little K for four groups of 64
+    assert _v(lib, M=512, N=512, K=255) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma t64x64x64 ")
+    # 256 tiles of 64x64 already fill the chip
+    assert _v(lib, M=1024, N=1024, K=4096) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma t64x64x64 ")
+    # whole tiles, but K not a multiple of 4 x 64: the groups' last steps are masked
+    assert _v(lib, M=512, N=512, K=512 + 64) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith("ksplit4 masked"), lib.gemm_last_path()
+    assert _v(lib, M=512, N=512, K=1024) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith("ksplit4"), lib.gemm_last_path()
 
 
 def test_force_path_and_tile(lib, monkeypatch):
