@@ -30,6 +30,7 @@ struct Plan {
   bool mfma = false;
   int tile = 0;
   bool masked = false;
+  bool pp_f32 = false;  // float32 operands on the two-group kernel
   int epi = EPI_BETA0;
   GemmArgs args{};
   bool byte8 = false;  // 8-bit float operands: the 1-byte-operand kernel
@@ -313,23 +314,32 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   // The unmasked kernels address an operand box through a buffer resource
   // with 32-bit byte offsets spanning up to max(bm, bn, bk) rows of the
   // operand; larger pitches take the masked kernels' 64-bit addressing.
+  bool big_pitch;
   {
     const int64_t rows = ti.bm > ti.bn ? (ti.bm > ti.bk ? ti.bm : ti.bk)
                                        : (ti.bn > ti.bk ? ti.bn : ti.bk);
     const int64_t ldmax = lda > ldb ? lda : ldb;
-    if (ldmax * esz * rows + 4096 >= (int64_t{1} << 31)) plan.masked = true;
+    big_pitch = ldmax * esz * rows + 4096 >= (int64_t{1} << 31);
+    if (big_pitch) plan.masked = true;
   }
   a.a_vw = a_vw;
   a.b_vw = b_vw;
   a.src32 = src32 ? (dtype == GEMM_DTYPE_F32_BF16 ? 2 : 1) : 0;
-  if (a_elem || b_elem || src32) plan.masked = true;
+  // Float32 operands, both K-contiguous, 16-byte rows, whole 256x256 tiles
+  // and K a multiple of its 32-deep slices: the two-group kernel rounds them
+  // as it reads fragments. Every other float32 call is rounded while the
+  // masked kernel stages it.
+  plan.pp_f32 = src32 && tile == TILE_256x256 && !transA && transB && !a_elem && !b_elem &&
+                !big_pitch && M % ti.bm == 0 && N % ti.bn == 0 && K % pp_f32_slice() == 0;
+  if (plan.pp_f32) plan.masked = false;
+  else if (a_elem || b_elem || src32) plan.masked = true;
   a.tiles_m = (int)((M + ti.bm - 1) / ti.bm);
   a.tiles_n = (int)((N + ti.bn - 1) / ti.bn);
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7fffffff)
     return fail(GEMM_ERR_UNSUPPORTED, "too many output tiles for one launch");
   // Whole 256x256 tiles (any operand layout) take the kernel with two wave
   // groups (2x4 waves) and direct global->LDS loads.
-  const bool pingpong = tile == TILE_256x256 && !plan.masked;
+  const bool pingpong = tile == TILE_256x256 && !plan.masked;  // includes plan.pp_f32
   // A last K step whose valid part ends within the first half of a 16x16x32
   // sub-step finishes with v_mfma_f32_16x16x16 (no product of staged zeros).
   const bool k16_tail = ti.atom_k == 32 && K % 32 >= 1 && K % 32 <= 16;
@@ -456,6 +466,8 @@ int gemm(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB, flo
     if (plan.scale_only) e = launch_scale_c(plan.args, s);
     else if (plan.byte8)
       e = launch_byte(plan.byte_kind, transA != 0, transB != 0, plan.bargs, s);
+    else if (plan.pp_f32)
+      e = launch_pp_f32(dtype & 1, plan.args, s);
     else if (plan.mfma)
       e = launch_mfma(plan.tile, dtype & 1, transA != 0, transB != 0, plan.masked, plan.args, s);
     else e = launch_fma(dtype, transA != 0, transB != 0, plan.args, s);

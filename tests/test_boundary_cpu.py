@@ -162,10 +162,21 @@ def test_k16_tail_is_named(lib):
 
 
 def test_f32_operand_dtypes(lib, monkeypatch):
-    # float32 A/B rounded while staged: always the masked matrix-core kernel
+    # whole 256x256 NT tiles, K a multiple of 32: the two-group kernel rounds
+    # fragments as it reads them
     assert _v(lib, M=8192, N=8192, K=8192, tB=1, dtype=lib.GEMM_DTYPE_F32_BF16) == lib.GEMM_OK
-    path = lib.gemm_last_path()
-    assert path.startswith("mfma t256x256x64 w2x2") and path.endswith("masked f32->bf16"), path
+    assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 pingpong f32->bf16"
+    assert _v(lib, M=4096, N=4096, K=4096 + 32, tB=1, dtype=2, beta=1.0, C=D0) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 NT epi=acc+c pingpong f32->f16"
+    # otherwise rounded while staged on the masked kernel: other layouts, K not
+    # a multiple of 32, rows not 16-byte aligned
+    for kw in (dict(tB=0), dict(tA=1, tB=1), dict(tB=1, K=8192 + 16),
+               dict(tB=1, lda=8192 + 2)):
+        args = dict(M=8192, N=8192, K=8192, dtype=lib.GEMM_DTYPE_F32_BF16)
+        args.update(kw)
+        assert _v(lib, **args) == lib.GEMM_OK
+        path = lib.gemm_last_path()
+        assert path.startswith("mfma t256x256x64 w2x2") and " masked f32->bf16" in path, (kw, path)
     assert _v(lib, dtype=lib.GEMM_DTYPE_F32_F16) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith("masked f32->f16"), lib.gemm_last_path()
     # pitches count 4-byte elements: 66 floats = 264 B is 8-byte aligned only

@@ -151,8 +151,8 @@ def test_tiled_shapes_narrow_staging(tile, dtype, monkeypatch):
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("dtype", ["f32_f16", "f32_bf16"])
 def test_tiled_shapes_f32_operands(tile, dtype, monkeypatch):
-    """float32 A and B rounded to f16/bf16 while staged (always the masked
-    kernel): every layout, general epilogue, aligned and 8-/4-byte pitches,
+    """float32 A and B rounded to f16/bf16 (while staged on the masked
+    kernel; as read from LDS on whole NT tiles): every layout, general epilogue, aligned and 8-/4-byte pitches,
     bases 4 bytes past a 16-byte boundary; NaN in the padding is never read."""
     monkeypatch.setenv("GEMM_FORCE_TILE", tile)
     seed = 6000
@@ -183,6 +183,86 @@ def test_f32_operands_equal_prerounded_16bit_bitwise(dtype):
     r16 = run(cfg16, workloads.make_inputs(cfg16, A_src=inp32.A_src, B_src=inp32.B_src))
     assert r32.path.replace(" f32->" + dtype, "") == r16.path, (r32.path, r16.path)
     assert torch.equal(r32.D, r16.D)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_f32_operands_pingpong(dtype, monkeypatch):
+    """Whole 256x256 NT tiles of float32 operands take the two-group kernel,
+    which rounds each fragment as it reads it from LDS: one slice of 32, two,
+    an odd count, and many; every epilogue; against the oracle."""
+    monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
+    seed = 6500
+    for K in (32, 64, 96, 1056):
+        for alpha, beta in [(1.0, 0.0), (1.0, 1.0), (1.5, -0.5)]:
+            seed += 1
+            cfg = workloads.Config(f"f32pp{seed}", 512, 256, K, "f32_" + dtype, 0, 1, alpha,
+                                   beta, "uniform", seed, ldd=256 + 4 * (seed % 2))
+            r = run(cfg)
+            assert "pingpong f32->" + dtype in r.path and "masked" not in r.path, r.path
+            r.check()
+            r.check_padding_untouched()
+    # other layouts, K not a multiple of 32, or 8-byte rows: the masked kernel
+    for (tA, tB, K, ldb) in [(0, 0, 64, None), (1, 1, 64, None), (0, 1, 48, None),
+                             (0, 1, 64, 66)]:
+        seed += 1
+        cfg = workloads.Config(f"f32pp{seed}", 512, 256, K, "f32_" + dtype, tA, tB, 1.0, 0.0,
+                               "uniform", seed, ldb=ldb)
+        r = run(cfg)
+        assert " masked" in r.path and "pingpong" not in r.path, r.path
+        r.check()
+
+
+def _tie_heavy_f32(shape, dtype, rng):
+    """float32 values that stress rounding to the 16-bit format: exact ties
+    between two neighbours (both parities), one float32 ulp either side of a
+    tie, subnormals of the 16-bit format, and plain random values."""
+    n = int(np.prod(shape))
+    if dtype == "bf16":
+        hi = rng.integers(0x3C00, 0x4080, n, dtype=np.uint32)   # |x| about 2^-7 .. 4
+        hi |= rng.integers(0, 2, n, dtype=np.uint32) << 15       # sign
+        low = np.choose(rng.integers(0, 4, n), [np.full(n, 0x8000), np.full(n, 0x8001),
+                                                 np.full(n, 0x7FFF), rng.integers(0, 0x10000, n)])
+        bits = (hi << 16) | low.astype(np.uint32)
+        sub = rng.random(n) < 0.1  # bf16 subnormals: float32 exponent field 0
+        bits[sub] = (bits[sub] & 0x8000FFFF) | (rng.integers(1, 0x80, sub.sum()).astype(np.uint32) << 16)
+        x = bits.view(np.float32)
+    else:
+        h = (rng.standard_normal(n) * 2.0).astype(np.float16)
+        nxt = np.nextafter(h, np.float16(np.inf))
+        mid = (h.astype(np.float32) + nxt.astype(np.float32)) / 2  # exact in float32
+        x = np.choose(rng.integers(0, 4, n),
+                      [mid, np.nextafter(mid, np.float32(np.inf)), np.nextafter(mid, np.float32(-np.inf)),
+                       rng.standard_normal(n).astype(np.float32)])
+        sub = rng.random(n) < 0.1  # f16 subnormals and ties between them
+        x[sub] = (rng.integers(-1023, 1024, sub.sum()) * 2.0 ** -25).astype(np.float32)
+    return torch.tensor(x.astype(np.float32).reshape(shape))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_f32_pingpong_rounding_bitwise(dtype, monkeypatch):
+    """In-register rounding of the two-group kernel against the oracle's
+    rounding: D from float32 operands must equal, bitwise, D of the 16-bit
+    kernel fed the operands the oracle rounds (same tile, same sum order)."""
+    monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
+    rng = np.random.default_rng(44)
+    M, N, K = 256, 512, 192  # K whole 64-slices: both sides on the two-group design
+    A32 = _tie_heavy_f32((M, K), dtype, rng)
+    B32 = _tie_heavy_f32((N, K), dtype, rng)
+    code = 0 if dtype == "f16" else 1
+
+    def oracle_rounded(x):
+        bits = oracle.round_f32_bits(x.numpy().reshape(-1), code)
+        return torch.tensor(oracle.decode_bits(bits, code).astype(np.float32).reshape(x.shape))
+
+    cfg32 = workloads.Config("f32tie", M, N, K, "f32_" + dtype, 0, 1, 1.0, 0.0, "uniform", 1)
+    r32 = run(cfg32, workloads.make_inputs(cfg32, A_src=A32, B_src=B32))
+    assert "pingpong f32->" + dtype in r32.path, r32.path
+    cfg16 = workloads.Config("f32tie16", M, N, K, dtype, 0, 1, 1.0, 0.0, "uniform", 1)
+    r16 = run(cfg16, workloads.make_inputs(cfg16, A_src=oracle_rounded(A32),
+                                           B_src=oracle_rounded(B32)))
+    assert r32.path.replace(" f32->" + dtype, "") == r16.path, (r32.path, r16.path)
+    assert torch.equal(r32.D, r16.D)
+    r32.check()
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
