@@ -120,6 +120,10 @@ struct TileCfg {
   static constexpr int LDS_BYTES = KG * GROUP_LDS_BYTES;
   // Accumulators that groups 1..KG-1 hand to group 0 (f32, lane-major).
   static constexpr int XFER_BYTES = (KG - 1) * WM * WN * TM * TN * At::NACC * 64 * 4;
+  // The masked kernel's interior-tile paths (whole-step unmasked loads, 16-byte
+  // stores) are compiled in only where the accumulators leave registers for
+  // both loaders: with 256 accumulators per lane they would spill.
+  static constexpr bool INNER_PATHS = TM * TN * At::NACC <= 64;
   static_assert(WTM % At::M == 0 && WTN % At::N == 0, "wave tile must hold whole atoms");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
   static_assert(XFER_BYTES <= LDS_BYTES, "the K-group sum is staged in the operand LDS");
@@ -219,15 +223,20 @@ struct Stager {
 
   // Issue the global loads of the box at (r0, k0). rlim / klim: number of
   // valid rows / K-values of the whole operand (used only when MASK). vw
-  // (MASK only): the operand's staging vector width in elements; below 16
-  // bytes its pieces are not 16-byte aligned and are read in narrower loads.
-  // src32 (MASK only): 0 for 16-bit operands; 1 / 2 for float32 operands
-  // rounded to f16 / bf16 here.
-  __device__ inline void load(const void* __restrict__ Xv, int64_t ld, int r0, int rlim, int k0,
-                              int klim, int tid, int vw = 8, int src32 = 0) {
+  // (MASK only): the operand's staging vector width in elements; below 8
+  // (16 bytes) its pieces are not 16-byte aligned and are read in narrower
+  // loads. src32 (MASK only): 0 for 16-bit operands; 1 / 2 for float32
+  // operands rounded to f16 / bf16 here. whole (MASK only, uniform over the
+  // workgroup): the box lies inside the operand, so a 16-byte-aligned
+  // operand takes the unmasked kernel's buffer loads, which need no bounds
+  // checks and no waits; the masked kernel's interior tiles do so on every
+  // whole K step.
+  __device__ __forceinline__ void load(const void* __restrict__ Xv, int64_t ld, int r0, int rlim,
+                                       int k0, int klim, int tid, int vw = 8, int src32 = 0,
+                                       bool whole = false) {
     const uint16_t* __restrict__ X = static_cast<const uint16_t*>(Xv);
     const float* __restrict__ X32 = static_cast<const float*>(Xv);
-    if constexpr (!MASK) {
+    if (!MASK || (whole && vw == 8)) {
       if constexpr (KCONTIG) {
         const auto rs = make_rsrc(X + (int64_t)r0 * ld + k0);
         const int voff = (int)(((tid >> 3) * ld + ((tid & 7) << 3)) * 2);
@@ -498,7 +507,9 @@ gemm_mfma_kernel(const GemmArgs p) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Uniform within a wave: the K group, and with it each step's K offset and
+  // the buffer resources built from it, stay scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = wave / (Cfg::WM * Cfg::WN);        // K group
   const int gwave = wave % (Cfg::WM * Cfg::WN);      // wave within its group
   const int tid = threadIdx.x % Cfg::GROUP_THREADS;  // thread within its group
@@ -532,16 +543,23 @@ gemm_mfma_kernel(const GemmArgs p) {
   const int koct = At::frag_koct(lane);
   constexpr int CPS = At::K / 8;  // 16-byte chunks per K sub-step
 
+  // Masked kernel: tiles wholly inside M (N) read the whole K steps of A (B)
+  // with the unmasked loads when the operand allows them.
+  const bool inner_m = Cfg::INNER_PATHS && m0 + Cfg::BM <= p.M;
+  const bool inner_n = Cfg::INNER_PATHS && n0 + Cfg::BN <= p.N;
+  const bool a_whole = MASK && p.a_fast && inner_m, b_whole = MASK && p.b_fast && inner_n;
+  auto load_step = [&](int k0) {
+    const bool kin = k0 + Cfg::BK <= p.K;
+    sa.load(p.A, p.lda, m0, p.M, k0, p.K, tid, p.a_vw, p.src32, a_whole && kin);
+    sb.load(p.B, p.ldb, n0, p.N, k0, p.K, tid, p.b_vw, p.src32, b_whole && kin);
+  };
+
   // Prologue: step 0 into buffer 0, step 1 into registers, first fragments.
-  sa.load(p.A, p.lda, m0, p.M, kstep(0), p.K, tid, p.a_vw, p.src32);
-  sb.load(p.B, p.ldb, n0, p.N, kstep(0), p.K, tid, p.b_vw, p.src32);
+  load_step(kstep(0));
   sa.store(smem, tid);
   sb.store(smem + Cfg::A_BYTES, tid);
   __syncthreads();
-  if (KT > 1) {
-    sa.load(p.A, p.lda, m0, p.M, kstep(1), p.K, tid, p.a_vw, p.src32);
-    sb.load(p.B, p.ldb, n0, p.N, kstep(1), p.K, tid, p.b_vw, p.src32);
-  }
+  if (KT > 1) load_step(kstep(1));
   Frags<Cfg> cur, nxt;
   read_frags<Cfg>(cur, smem, smem + Cfg::A_BYTES, a_row0, b_row0, koct);
 
@@ -569,11 +587,7 @@ gemm_mfma_kernel(const GemmArgs p) {
       sa.store(nA, tid);
       sb.store(nA + Cfg::A_BYTES, tid);
       __syncthreads();
-      if (kt + 2 < KT) {
-        const int k0 = kstep(kt + 2);
-        sa.load(p.A, p.lda, m0, p.M, k0, p.K, tid, p.a_vw, p.src32);
-        sb.load(p.B, p.ldb, n0, p.N, k0, p.K, tid, p.b_vw, p.src32);
-      }
+      if (kt + 2 < KT) load_step(kstep(kt + 2));
       read_frags<Cfg>(nxt, nA, nA + Cfg::A_BYTES, a_row0, b_row0, koct);
     }
     mma_step<Cfg, Tag>(acc, cur);
@@ -612,7 +626,11 @@ gemm_mfma_kernel(const GemmArgs p) {
     }
   }
 
-  store_tile<Cfg, EPI, MASK>(acc, p, m0 + wm * Cfg::WTM, n0 + wn * Cfg::WTN, lane);
+  // Tiles wholly inside M x N need no masked stores, even in the masked kernel.
+  if (!MASK || (inner_m && inner_n))
+    store_tile<Cfg, EPI, false>(acc, p, m0 + wm * Cfg::WTM, n0 + wn * Cfg::WTN, lane);
+  else
+    store_tile<Cfg, EPI, true>(acc, p, m0 + wm * Cfg::WTM, n0 + wn * Cfg::WTN, lane);
 }
 
 template <class Cfg, class Tag, bool TA, bool TB, bool MASK>
