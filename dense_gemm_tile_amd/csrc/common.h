@@ -28,10 +28,10 @@ struct GemmArgs {
                  //    values, rounded to f16 / bf16 (nearest, ties to even) as
                  //    they are staged (masked kernel only); a_vw, b_vw then
                  //    count float32 elements (4, 2 or 1)
-  int a_fast;    // 1: whole boxes of A may be read with 16-byte buffer loads
-  int b_fast;    //    (16-bit values, 16-byte rows, 32-bit byte offsets reach
-                 //    every box); the masked kernel then reads the whole K
-                 //    steps of its interior tiles that way (same for B)
+  int a_fast;    // 1: whole boxes of A may be read without bounds checks
+  int b_fast;    //    (16-bit values; 32-bit byte offsets reach every box):
+                 //    the masked kernel then reads the whole K steps of its
+                 //    interior tiles that way (same for B)
 };
 
 // Arguments of the 1-byte-operand kernels (see gemm_byte.hip): int8 ->

@@ -333,8 +333,8 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
                 !big_pitch && M % ti.bm == 0 && N % ti.bn == 0 && K % pp_f32_slice() == 0;
   if (plan.pp_f32) plan.masked = false;
   else if (a_elem || b_elem || src32) plan.masked = true;
-  a.a_fast = !src32 && !a_elem && !big_pitch;
-  a.b_fast = !src32 && !b_elem && !big_pitch;
+  a.a_fast = !src32 && !big_pitch;
+  a.b_fast = !src32 && !big_pitch;
   a.tiles_m = (int)((M + ti.bm - 1) / ti.bm);
   a.tiles_n = (int)((N + ti.bn - 1) / ti.bn);
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7fffffff)

@@ -227,10 +227,10 @@ struct Stager {
   // (16 bytes) its pieces are not 16-byte aligned and are read in narrower
   // loads. src32 (MASK only): 0 for 16-bit operands; 1 / 2 for float32
   // operands rounded to f16 / bf16 here. whole (MASK only, uniform over the
-  // workgroup): the box lies inside the operand, so a 16-byte-aligned
-  // operand takes the unmasked kernel's buffer loads, which need no bounds
-  // checks and no waits; the masked kernel's interior tiles do so on every
-  // whole K step.
+  // workgroup): the box lies inside the operand, so its pieces need no
+  // bounds checks: a 16-byte-aligned operand takes the unmasked kernel's
+  // buffer loads, a 16-bit operand with narrower rows one 16-byte global load
+  // per piece; the masked kernel's interior tiles do so on every whole K step.
   __device__ __forceinline__ void load(const void* __restrict__ Xv, int64_t ld, int r0, int rlim,
                                        int k0, int klim, int tid, int vw = 8, int src32 = 0,
                                        bool whole = false) {
@@ -252,6 +252,23 @@ struct Stager {
 #pragma unroll
         for (int j = 0; j < NL; ++j)
           v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * step, 0);
+      }
+    } else if (whole && !src32) {
+      // Whole box of an operand whose rows are not 16-byte aligned: the same
+      // pieces as 16-byte global loads at their own (2-byte aligned)
+      // addresses, which this target serves unaligned (the compiler itself
+      // merges eight 16-bit loads into one such load); no bounds checks.
+      typedef u32x4 u32x4_a2 __attribute__((aligned(2)));
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        int64_t off;
+        if constexpr (KCONTIG) {
+          const int id = tid + i * THREADS;
+          off = (int64_t)(r0 + (id >> 3)) * ld + k0 + ((id & 7) << 3);
+        } else {
+          off = (int64_t)(k0 + (tid / (R / 8)) * NL + i) * ld + r0 + (tid % (R / 8)) * 8;
+        }
+        v[i] = *reinterpret_cast<const u32x4_a2*>(X + off);
       }
     } else if constexpr (KCONTIG) {
 #pragma unroll
