@@ -398,6 +398,35 @@ def test_k_split_is_deterministic_and_exact():
         assert np.array_equal(r.D[:, :N].numpy(), (A @ B).astype(np.float32)), (tA, tB)
 
 
+def test_huge_pitch_64bit_addressing():
+    """A row pitch whose byte offsets across one tile pass 2^31 (A with
+    2^24 + 8 elements per row: an 8 GiB extent, of which only the M x K
+    elements are written and read) takes the masked kernel's 64-bit
+    addressing; D must match the oracle on the packed operand."""
+    import dense_gemm_tile_amd as dgt
+    dev = torch.device("cuda:0")
+    M, N, K = 256, 192, 256
+    lda = (1 << 24) + 8
+    cfg = workloads.Config("hugepitch", M, N, K, "bf16", 0, 0, 1.0, 0.0, "uniform", 97)
+    inp = workloads.make_inputs(cfg)
+    say(f"huge pitch M={M} N={N} K={K} lda={lda}")
+    Abig = torch.empty((M - 1) * lda + K, dtype=torch.bfloat16, device=dev)
+    Abig.as_strided((M, K), (lda, 1)).copy_(inp.A.to(dev))
+    B = inp.B.to(dev)
+    D = torch.full((M, N), float("nan"), device=dev)
+    dgt.gemm(M, N, K, "bf16", 0, 0, 1.0, 0.0, Abig, lda, B, N, None, N, D, N)
+    path = dgt.gemm_last_path()
+    torch.cuda.synchronize()
+    assert " masked" in path, path
+    D_ref, bound = oracle.gemm_reference(M, N, K, 1, 0, 0, 1.0, 0.0,
+                                         workloads.bits_u16(inp.A).reshape(-1), K,
+                                         workloads.bits_u16(inp.B).reshape(-1), N)
+    rep = oracle.check(D.cpu().numpy().astype(np.float64), D_ref, bound)
+    del Abig
+    torch.cuda.empty_cache()
+    assert rep["ok"], rep
+
+
 # ----------------------------------------------- epilogue and aliasing ------
 
 def test_inplace_equals_separate_buffers_bitwise():
