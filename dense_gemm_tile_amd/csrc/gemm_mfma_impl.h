@@ -231,9 +231,14 @@ struct Stager {
   // bounds checks: a 16-byte-aligned operand takes the unmasked kernel's
   // buffer loads, a 16-bit operand with narrower rows one 16-byte global load
   // per piece; the masked kernel's interior tiles do so on every whole K step.
+  // pieces (MASK only, uniform; the operand is 16-byte aligned, 16-bit, and
+  // its offsets fit 32 bits): every piece of this box is wholly inside or
+  // wholly outside the operand, so the buffer loads serve it too, with an
+  // out-of-range offset for the outside pieces, which the hardware answers
+  // with zeros.
   __device__ __forceinline__ void load(const void* __restrict__ Xv, int64_t ld, int r0, int rlim,
                                        int k0, int klim, int tid, int vw = 8, int src32 = 0,
-                                       bool whole = false) {
+                                       bool whole = false, bool pieces = false) {
     const uint16_t* __restrict__ X = static_cast<const uint16_t*>(Xv);
     const float* __restrict__ X32 = static_cast<const float*>(Xv);
     if (!MASK || (whole && vw == 8)) {
@@ -252,6 +257,32 @@ struct Stager {
 #pragma unroll
         for (int j = 0; j < NL; ++j)
           v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * step, 0);
+      }
+    } else if (pieces) {
+      // Offset 2^31: every dword of the 16-byte access lies at or past the
+      // resource's 0x7FFFFFFF records, so nothing is read and zeros return.
+      // Inside pieces stay below 2^31 - 4096 (the host's 32-bit offset rule).
+      constexpr int kOut = (int)0x80000000u;
+      if constexpr (KCONTIG) {
+        const auto rs = make_rsrc(X + (int64_t)r0 * ld + k0);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const int id = tid + i * THREADS;
+          const int rr = id >> 3, kk = (id & 7) << 3;
+          const bool in = r0 + rr < rlim && k0 + kk < klim;
+          v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, in ? (int)((rr * ld + kk) * 2) : kOut,
+                                                       0, 0);
+        }
+      } else {
+        const int rc = tid % (R / 8), kb = tid / (R / 8);
+        const auto rs = make_rsrc(X + (int64_t)k0 * ld + r0);
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          const int kk = kb * NL + j, rr = rc * 8;
+          const bool in = k0 + kk < klim && r0 + rr < rlim;
+          v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, in ? (int)((kk * ld + rr) * 2) : kOut,
+                                                       0, 0);
+        }
       }
     } else if (whole && !src32) {
       // Whole box of an operand whose rows are not 16-byte aligned: the same
@@ -454,32 +485,55 @@ __device__ inline float epi_one(float x, float c, float alpha, float beta) {
 // that into 4 consecutive columns of one row per lane, so C is read and D is
 // written with 16-byte accesses; otherwise elements are written one by one
 // with bounds checks.
+//
+// C may be D itself (the in-place form; any other overlap is rejected on the
+// host), so the compiler may not move a C load above an earlier D store. The
+// C values of a whole row of atoms (wide form) or of one atom (element form)
+// are therefore loaded before any of their D stores: one memory round trip
+// per batch instead of one per store. Each element is still read before it is
+// written, by the lane that writes it.
 template <class Cfg, int EPI, bool MASK>
 __device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::TN],
                                   const GemmArgs& p, int r0, int c0, int lane) {
   using At = typename Cfg::At;
+  constexpr int NG = At::NACC / 4;  // groups of 4 rows per atom and lane
   const float alpha = p.alpha, beta = p.beta;
   const int col_l = At::acc_col(lane);
   if (!MASK && p.wide_epi) {
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
+      f32x4 cv[Cfg::TN][NG];
+      if constexpr (EPI != EPI_BETA0) {
+#pragma unroll
+        for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const int c = c0 + j * At::N + (col_l & ~3);
+            const int r = r0 + i * At::M + At::acc_row(lane, 4 * g) + (lane & 3);
+            cv[j][g] = *reinterpret_cast<const f32x4*>(p.C + (int64_t)r * p.ldc + c);
+          }
+      }
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j) {
         const int c = c0 + j * At::N + (col_l & ~3);
 #pragma unroll
-        for (int g = 0; g < At::NACC / 4; ++g) {
+        for (int g = 0; g < NG; ++g) {
           float x[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                         acc[i][j][4 * g + 3]};
           quad_transpose(x, lane);
           const int r = r0 + i * At::M + At::acc_row(lane, 4 * g) + (lane & 3);
-          f32x4 cv = {0.0f, 0.0f, 0.0f, 0.0f};
-          if constexpr (EPI != EPI_BETA0)
-            cv = *reinterpret_cast<const f32x4*>(p.C + (int64_t)r * p.ldc + c);
           f32x4 o;
-          o[0] = epi_one<EPI>(x[0], cv[0], alpha, beta);
-          o[1] = epi_one<EPI>(x[1], cv[1], alpha, beta);
-          o[2] = epi_one<EPI>(x[2], cv[2], alpha, beta);
-          o[3] = epi_one<EPI>(x[3], cv[3], alpha, beta);
+          if constexpr (EPI != EPI_BETA0) {
+            o[0] = epi_one<EPI>(x[0], cv[j][g][0], alpha, beta);
+            o[1] = epi_one<EPI>(x[1], cv[j][g][1], alpha, beta);
+            o[2] = epi_one<EPI>(x[2], cv[j][g][2], alpha, beta);
+            o[3] = epi_one<EPI>(x[3], cv[j][g][3], alpha, beta);
+          } else {
+            o[0] = epi_one<EPI>(x[0], 0.0f, alpha, beta);
+            o[1] = epi_one<EPI>(x[1], 0.0f, alpha, beta);
+            o[2] = epi_one<EPI>(x[2], 0.0f, alpha, beta);
+            o[3] = epi_one<EPI>(x[3], 0.0f, alpha, beta);
+          }
           // D is written once and not read back here: stream it past the caches.
           __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(p.D + (int64_t)r * p.ldd + c));
         }
@@ -492,13 +546,20 @@ __device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::T
 #pragma unroll
     for (int j = 0; j < Cfg::TN; ++j) {
       const int c = c0 + j * At::N + col_l;
+      float cv[At::NACC];
+      if constexpr (EPI != EPI_BETA0) {
+#pragma unroll
+        for (int v = 0; v < At::NACC; ++v) {
+          const int r = r0 + i * At::M + At::acc_row(lane, v);
+          cv[v] = (!MASK || (r < p.M && c < p.N)) ? p.C[(int64_t)r * p.ldc + c] : 0.0f;
+        }
+      }
 #pragma unroll
       for (int v = 0; v < At::NACC; ++v) {
         const int r = r0 + i * At::M + At::acc_row(lane, v);
         if (MASK && (r >= p.M || c >= p.N)) continue;
-        float cv = 0.0f;
-        if constexpr (EPI != EPI_BETA0) cv = p.C[(int64_t)r * p.ldc + c];
-        p.D[(int64_t)r * p.ldd + c] = epi_one<EPI>(acc[i][j][v], cv, alpha, beta);
+        p.D[(int64_t)r * p.ldd + c] =
+            epi_one<EPI>(acc[i][j][v], EPI != EPI_BETA0 ? cv[v] : 0.0f, alpha, beta);
       }
     }
   }
@@ -565,10 +626,17 @@ gemm_mfma_kernel(const GemmArgs p) {
   const bool inner_m = Cfg::INNER_PATHS && m0 + Cfg::BM <= p.M;
   const bool inner_n = Cfg::INNER_PATHS && n0 + Cfg::BN <= p.N;
   const bool a_whole = MASK && p.a_fast && inner_m, b_whole = MASK && p.b_fast && inner_n;
+  // A box's pieces (8 K-values of one row for a K-contiguous operand, else 8
+  // row-values of one K row) are wholly inside or outside the operand when
+  // the edge that crosses them falls on a multiple of 8.
+  const bool a_pieces = MASK && p.a_fast && p.a_vw == 8 &&
+                        (TA ? (inner_m || p.M % 8 == 0) : p.K % 8 == 0);
+  const bool b_pieces = MASK && p.b_fast && p.b_vw == 8 &&
+                        (TB ? p.K % 8 == 0 : (inner_n || p.N % 8 == 0));
   auto load_step = [&](int k0) {
     const bool kin = k0 + Cfg::BK <= p.K;
-    sa.load(p.A, p.lda, m0, p.M, k0, p.K, tid, p.a_vw, p.src32, a_whole && kin);
-    sb.load(p.B, p.ldb, n0, p.N, k0, p.K, tid, p.b_vw, p.src32, b_whole && kin);
+    sa.load(p.A, p.lda, m0, p.M, k0, p.K, tid, p.a_vw, p.src32, a_whole && kin, a_pieces);
+    sb.load(p.B, p.ldb, n0, p.N, k0, p.K, tid, p.b_vw, p.src32, b_whole && kin, b_pieces);
   };
 
   // Prologue: step 0 into buffer 0, step 1 into registers, first fragments.
