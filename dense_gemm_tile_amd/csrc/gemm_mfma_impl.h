@@ -168,18 +168,13 @@ struct Stager {
     return r;
   }
 
-  // A whole piece read with vw-element (2*vw-byte) loads, vw in {4, 2, 1}.
-  __device__ static inline u32x4 load_narrow(const uint16_t* p, int vw) {
-    if (vw == 4) {
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 4);
-      return u32x4{lo.x, lo.y, hi.x, hi.y};
-    }
-    if (vw == 2) {
-      const unsigned* q = reinterpret_cast<const unsigned*>(p);
-      return u32x4{q[0], q[1], q[2], q[3]};
-    }
-    return load_partial(p, 8);
+  // A whole piece of an operand whose rows are not 16-byte aligned (vw in
+  // {4, 2, 1}): one 16-byte global load at the piece's own 2-byte-aligned
+  // address, which this target serves unaligned, so nothing has to be packed
+  // (and waited for) here.
+  __device__ static inline u32x4 load_narrow(const uint16_t* p, int) {
+    typedef u32x4 u32x4_a2 __attribute__((aligned(2)));
+    return *reinterpret_cast<const u32x4_a2*>(p);
   }
 
   // Rounding of one float32 value to a 16-bit pattern, to nearest with ties
