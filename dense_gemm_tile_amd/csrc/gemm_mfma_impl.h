@@ -487,9 +487,32 @@ __device__ inline float epi_one(float x, float c, float alpha, float beta) {
 // are therefore loaded before any of their D stores: one memory round trip
 // per batch instead of one per store. Each element is still read before it is
 // written, by the lane that writes it.
+// The C values of the wide form, in the layout store_tile uses, for callers
+// that read them early (the K-split kernel, before its main loop).
+template <class Cfg>
+struct WideC {
+  f32x4 v[Cfg::TM][Cfg::TN][Cfg::At::NACC / 4];
+};
+template <class Cfg>
+__device__ inline void load_wide_c(WideC<Cfg>& w, const GemmArgs& p, int r0, int c0, int lane) {
+  using At = typename Cfg::At;
+  const int col_l = At::acc_col(lane);
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int g = 0; g < At::NACC / 4; ++g) {
+        const int c = c0 + j * At::N + (col_l & ~3);
+        const int r = r0 + i * At::M + At::acc_row(lane, 4 * g) + (lane & 3);
+        w.v[i][j][g] = *reinterpret_cast<const f32x4*>(p.C + (int64_t)r * p.ldc + c);
+      }
+}
+
 template <class Cfg, int EPI, bool MASK>
 __device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::TN],
-                                  const GemmArgs& p, int r0, int c0, int lane) {
+                                  const GemmArgs& p, int r0, int c0, int lane,
+                                  const WideC<Cfg>& pre = WideC<Cfg>{}, bool use_pre = false) {
   using At = typename Cfg::At;
   constexpr int NG = At::NACC / 4;  // groups of 4 rows per atom and lane
   const float alpha = p.alpha, beta = p.beta;
@@ -498,7 +521,12 @@ __device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::T
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
       f32x4 cv[Cfg::TN][NG];
-      if constexpr (EPI != EPI_BETA0) {
+      if (EPI != EPI_BETA0 && use_pre) {
+#pragma unroll
+        for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+          for (int g = 0; g < NG; ++g) cv[j][g] = pre.v[i][j][g];
+      } else if constexpr (EPI != EPI_BETA0) {
 #pragma unroll
         for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
@@ -628,6 +656,14 @@ gemm_mfma_kernel(const GemmArgs p) {
                         (TA ? (inner_m || p.M % 8 == 0) : p.K % 8 == 0);
   const bool b_pieces = MASK && p.b_fast && p.b_vw == 8 &&
                         (TB ? p.K % 8 == 0 : (inner_n || p.N % 8 == 0));
+  // K-split tiles: group 0 reads the C it will need before the main loop,
+  // so that latency overlaps the K steps instead of following the group sum.
+  constexpr bool PRE_C = Cfg::KG > 1 && EPI != EPI_BETA0;
+  WideC<Cfg> cpre;
+  const bool pre_c = PRE_C && grp == 0 && p.wide_epi && (!MASK || (inner_m && inner_n));
+  if constexpr (PRE_C) {
+    if (pre_c) load_wide_c<Cfg>(cpre, p, m0 + wm * Cfg::WTM, n0 + wn * Cfg::WTN, lane);
+  }
   auto load_step = [&](int k0) {
     const bool kin = k0 + Cfg::BK <= p.K;
     sa.load(p.A, p.lda, m0, p.M, k0, p.K, tid, p.a_vw, p.src32, a_whole && kin, a_pieces);
@@ -708,7 +744,8 @@ gemm_mfma_kernel(const GemmArgs p) {
 
   // Tiles wholly inside M x N need no masked stores, even in the masked kernel.
   if (!MASK || (inner_m && inner_n))
-    store_tile<Cfg, EPI, false>(acc, p, m0 + wm * Cfg::WTM, n0 + wn * Cfg::WTN, lane);
+    store_tile<Cfg, EPI, false>(acc, p, m0 + wm * Cfg::WTM, n0 + wn * Cfg::WTN, lane, cpre,
+                                pre_c);
   else
     store_tile<Cfg, EPI, true>(acc, p, m0 + wm * Cfg::WTM, n0 + wn * Cfg::WTN, lane);
 }
