@@ -127,8 +127,13 @@ GEMM_API const char* gemm_last_error(void);
 
 /* Path of the last gemm()/gemm_validate() on this thread, e.g.
  * "mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 pingpong",
+ * "mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 pingpong f32->bf16" (float32
+ * operands rounded as their fragments are read),
+ * "mfma t32x32x64k4 w1x1 a32x32x16 NN epi=general ksplit4" (K split over four
+ * wave groups of one workgroup, for grids with few output tiles),
  * "mfma t128x128x64 w2x2 a32x32x16 TN epi=general masked narrow staging
- * (A: 2-byte loads, row pitch 8194 B is not a multiple of 16 B)" or
+ * (A: 2-byte loads, row pitch 8194 B is not a multiple of 16 B)",
+ * "fp8 e4m3 mfma t256x256x128 w2x4 a32x32x64 NT epi=beta0 pingpong" or
  * "fma t64x64x16 NN epi=beta0: forced by GEMM_FORCE_PATH=fma". Same lifetime
  * as above. */
 GEMM_API const char* gemm_last_path(void);
