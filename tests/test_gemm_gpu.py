@@ -53,6 +53,17 @@ def test_workload_parity_full_size_sampled(name):
     assert np.all(np.isfinite(r.D.numpy()))
 
 
+def test_f32_operand_workload_full_size_sampled():
+    """The float32-operand workload (4096^3 NT, rounded to bf16 on the GPU) in
+    the launch configuration the benchmark times, against the oracle's own
+    rounding on rows that touch every 256-row tile band."""
+    cfg = workloads.EXTRA_CONFIGS["gemm4096_f32in_nt"]
+    r = run(cfg)
+    assert r.path == "mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 pingpong f32->bf16", r.path
+    r.check(rows=sample_rows(cfg.M, 256, 1))
+    assert np.all(np.isfinite(r.D.numpy()))
+
+
 def test_ragged_workload_on_mfma_with_aligned_pitch():
     """Same ragged shape with A's rows padded to a 16-byte pitch: the masked
     matrix-core path must agree with the oracle too."""
