@@ -64,10 +64,11 @@ struct KindI8 {
   __device__ static inline acc_t mma(frag_t a, frag_t b, acc_t c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
   }
-  __device__ static inline void store(const GemmByteArgs& p, int64_t r, int c, acc_t v, int e) {
-    const int32_t* C = static_cast<const int32_t*>(p.C);
+  // cbits: C[r][c] as read by epilogue() (when p.read_c).
+  __device__ static inline void store(const GemmByteArgs& p, int64_t r, int c, acc_t v, int e,
+                                      unsigned cbits) {
     unsigned d = (unsigned)p.alpha_i * (unsigned)v[e];
-    if (p.read_c) d += (unsigned)p.beta_i * (unsigned)C[r * p.ldc + c];
+    if (p.read_c) d += (unsigned)p.beta_i * cbits;
     static_cast<int32_t*>(p.D)[r * p.ldd + c] = (int32_t)d;
   }
 };
@@ -93,13 +94,40 @@ struct KindF8 {
   __device__ static inline acc_t mma(frag_t a, frag_t b, acc_t c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, 127, 0, 127);
   }
-  __device__ static inline void store(const GemmByteArgs& p, int64_t r, int c, acc_t v, int e) {
+  // cbits: C[r][c] as read by epilogue() (when p.read_c).
+  __device__ static inline void store(const GemmByteArgs& p, int64_t r, int c, acc_t v, int e,
+                                      unsigned cbits) {
     float d = p.alpha_f * v[e];
-    if (p.read_c) d = __builtin_fmaf(p.beta_f, static_cast<const float*>(p.C)[r * p.ldc + c], d);
+    if (p.read_c) d = __builtin_fmaf(p.beta_f, __builtin_bit_cast(float, cbits), d);
     static_cast<float*>(p.D)[r * p.ldd + c] = d;
   }
 };
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Epilogue of one 32x32 atom whose top-left output element is (r0, c0): lane
+// l's accumulator v is row 8*(v/4) + 4*(l/32) + v%4, column l%32. C (32-bit
+// int or float, read as raw bits) may be D itself, so the compiler may not
+// move a C load above an earlier D store: all of the atom's C values are read
+// before its first store, one memory round trip per atom instead of per
+// element. Each element is read before it is written, by the lane that
+// writes it.
+template <class Kind, bool MASK>
+__device__ inline void epilogue(const GemmByteArgs& p, int r0, int c0,
+                                const typename Kind::acc_t& acc, int lane) {
+  unsigned cb[16];
+  const int c = c0 + (lane & 31);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r = r0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    const bool in = !MASK || (r < p.M && c < p.N);
+    cb[v] = (p.read_c && in) ? static_cast<const unsigned*>(p.C)[(int64_t)r * p.ldc + c] : 0u;
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r = r0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    if (!MASK || (r < p.M && c < p.N)) Kind::store(p, r, c, acc, v, cb[v]);
+  }
+}
 
 constexpr int kBM = 128, kBN = 128, kBK = 128, kThreads = 256;
 constexpr int kTM = 2, kTN = 2;           // atoms per wave
@@ -233,18 +261,12 @@ __global__ void __launch_bounds__(kThreads) gemm_byte_kernel(const GemmByteArgs 
     __syncthreads();
   }
 
-  // Epilogue: accumulator v of lane l in atom (i, j) is row 8*(v/4) + 4*(l/32)
-  // + v%4, column l%32 of the atom.
+  // Epilogue, atom by atom (masked at the edges).
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int c = n0 + wn * 64 + 32 * j + (lane & 31);
-        if (r < p.M && c < p.N) Kind::store(p, r, c, acc[i][j], v);
-      }
+      epilogue<Kind, true>(p, m0 + wm * 64 + 32 * i, n0 + wn * 64 + 32 * j, acc[i][j], lane);
 }
 
 // Whole 256x256 tiles of the NT layout on the two-group ping-pong design of
@@ -366,12 +388,8 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = m0 + wm * C::WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int c = n0 + wn * C::WTN + 32 * j + (lane & 31);
-        Kind::store(p, r, c, acc[i][j], v);
-      }
+      epilogue<Kind, false>(p, m0 + wm * C::WTM + 32 * i, n0 + wn * C::WTN + 32 * j, acc[i][j],
+                            lane);
 }
 
 template <class Kind>
