@@ -15,11 +15,70 @@
 #include "dense_gemm_tile.h"
 #include "common.h"
 
+extern char** environ;  // POSIX: the process environment (read by read_env)
+
 namespace dgt {
 namespace {
 
 thread_local std::string g_err;
 thread_local std::string g_path;
+
+// The matrix-core path description of the last call, formatted into g_path
+// only when it is asked for (gemm_last_path(), GEMM_LOG=debug): tiny GEMMs
+// are launch-bound, and formatting it on every call cost about as much host
+// time as the rest of the checks.
+struct MfmaPath {
+  const MfmaTileInfo* ti;
+  const char* ops;
+  const char* epi;
+  bool pingpong, masked, k16_tail;
+  const char* src32;  // "", " f32->f16" or " f32->bf16"
+  std::string elem_reason;
+};
+thread_local MfmaPath g_mpath;
+thread_local bool g_path_lazy = false;
+
+const std::string& current_path() {
+  if (g_path_lazy) {
+    const MfmaPath& m = g_mpath;
+    char buf[512], ksplit[32] = "";
+    if (m.ti->kg > 1) std::snprintf(ksplit, sizeof ksplit, " ksplit%d", m.ti->kg);
+    std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s%s%s",
+                  m.ti->name, m.ti->waves_m, m.pingpong ? 4 : m.ti->waves_n, m.ti->atom_m,
+                  m.ti->atom_n, m.ti->atom_k, m.ops, m.epi, ksplit,
+                  m.pingpong ? " pingpong" : "", m.masked ? " masked" : "",
+                  m.k16_tail ? " k16-tail" : "", m.src32,
+                  m.elem_reason.empty() ? "" : " narrow staging (", m.elem_reason.c_str(),
+                  m.elem_reason.empty() ? "" : ")");
+    g_path = buf;
+    g_path_lazy = false;
+  }
+  return g_path;
+}
+
+// The library's environment switches, read in one pass over the environment
+// at the start of each call (three getenv scans cost more than the checks).
+struct EnvSwitches {
+  const char* force_path = nullptr;  // GEMM_FORCE_PATH
+  const char* force_tile = nullptr;  // GEMM_FORCE_TILE
+  const char* log = nullptr;         // GEMM_LOG
+};
+thread_local EnvSwitches g_env;
+
+void read_env() {
+  g_env = EnvSwitches{};
+  for (char** e = environ; e && *e; ++e) {
+    const char* v = *e;
+    if (v[0] != 'G' || std::strncmp(v, "GEMM_", 5) != 0) continue;
+    v += 5;
+    if (std::strncmp(v, "FORCE_PATH=", 11) == 0) g_env.force_path = v + 11;
+    else if (std::strncmp(v, "FORCE_TILE=", 11) == 0) g_env.force_tile = v + 11;
+    else if (std::strncmp(v, "LOG=", 4) == 0) g_env.log = v + 4;
+  }
+  if (g_env.force_path && !*g_env.force_path) g_env.force_path = nullptr;
+  if (g_env.force_tile && !*g_env.force_tile) g_env.force_tile = nullptr;
+  if (g_env.log && !*g_env.log) g_env.log = nullptr;
+}
 
 // Largest dimension the int32 index arithmetic in the kernels supports.
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1024;
@@ -41,11 +100,6 @@ struct Plan {
 int fail(int code, const std::string& msg) {
   g_err = msg;
   return code;
-}
-
-const char* env(const char* name) {
-  const char* v = std::getenv(name);
-  return (v && *v) ? v : nullptr;
 }
 
 // Byte extent of a row-major [rows, cols] matrix with leading dimension ld.
@@ -119,6 +173,8 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
               int64_t ldc, const float* D, int64_t ldd, Plan& plan) {
   g_err.clear();
   g_path.clear();
+  g_path_lazy = false;
+  read_env();
   char buf[256];
   transA = transA != 0;
   transB = transB != 0;
@@ -227,7 +283,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   }
 
   if (fp8) {
-    if (const char* force = env("GEMM_FORCE_PATH")) {
+    if (const char* force = g_env.force_path) {
       if (std::strcmp(force, "fma") == 0)
         return fail(GEMM_ERR_UNSUPPORTED, "GEMM_FORCE_PATH=fma has no 8-bit float form");
       if (std::strcmp(force, "mfma") != 0)
@@ -277,7 +333,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   if (a_elem) elem_reason = pitch_reason("A", A, lda, a_vw, esz);
   if (b_elem) elem_reason += (a_elem ? "; " : "") + pitch_reason("B", B, ldb, b_vw, esz);
   std::string decline;
-  const char* force = env("GEMM_FORCE_PATH");
+  const char* force = g_env.force_path;
   if (force && std::strcmp(force, "fma") == 0) {
     if (src32)
       return fail(GEMM_ERR_UNSUPPORTED, "GEMM_FORCE_PATH=fma has no f32-operand form");
@@ -298,7 +354,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   }
 
   int tile = choose_tile(M, N, K);
-  if (const char* ft = env("GEMM_FORCE_TILE")) {
+  if (const char* ft = g_env.force_tile) {
     int found = -1;
     for (int t = 0; t < NUM_MFMA_TILES; ++t)
       if (std::strcmp(ft, mfma_tile_info(t).name) == 0) found = t;
@@ -345,16 +401,15 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   // A last K step whose valid part ends within the first half of a 16x16x32
   // sub-step finishes with v_mfma_f32_16x16x16 (no product of staged zeros).
   const bool k16_tail = ti.atom_k == 32 && K % 32 >= 1 && K % 32 <= 16;
-  char ksplit[32] = "";
-  if (ti.kg > 1) std::snprintf(ksplit, sizeof ksplit, " ksplit%d", ti.kg);
-  std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s%s%s", ti.name,
-                ti.waves_m, pingpong ? 4 : ti.waves_n, ti.atom_m, ti.atom_n, ti.atom_k, ops,
-                epi_name, ksplit, pingpong ? " pingpong" : "", plan.masked ? " masked" : "",
-                k16_tail ? " k16-tail" : "",
-                !src32 ? "" : dtype == GEMM_DTYPE_F32_BF16 ? " f32->bf16" : " f32->f16",
-                elem_reason.empty() ? "" : " narrow staging (", elem_reason.c_str(),
-                elem_reason.empty() ? "" : ")");
-  g_path = buf;
+  g_mpath.ti = &ti;
+  g_mpath.ops = ops;
+  g_mpath.epi = epi_name;
+  g_mpath.pingpong = pingpong;
+  g_mpath.masked = plan.masked;
+  g_mpath.k16_tail = k16_tail;
+  g_mpath.src32 = !src32 ? "" : dtype == GEMM_DTYPE_F32_BF16 ? " f32->bf16" : " f32->f16";
+  g_mpath.elem_reason.swap(elem_reason);
+  g_path_lazy = true;
   return GEMM_OK;
 }
 
@@ -365,6 +420,8 @@ int plan_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alp
             int64_t ldc, const int32_t* D, int64_t ldd, GemmByteArgs& a, bool& noop) {
   g_err.clear();
   g_path.clear();
+  g_path_lazy = false;
+  read_env();
   noop = false;
   char buf[256];
   transA = transA != 0;
@@ -440,11 +497,11 @@ int plan_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alp
 }
 
 void log_call(int64_t M, int64_t N, int64_t K, int status) {
-  const char* lv = env("GEMM_LOG");
+  const char* lv = g_env.log;
   if (!lv || std::strcmp(lv, "debug") != 0) return;
   if (status == GEMM_OK)
     std::fprintf(stderr, "[gemm] M=%lld N=%lld K=%lld -> %s\n", (long long)M, (long long)N,
-                 (long long)K, g_path.c_str());
+                 (long long)K, current_path().c_str());
   else
     std::fprintf(stderr, "[gemm] M=%lld N=%lld K=%lld -> error %d: %s\n", (long long)M,
                  (long long)N, (long long)K, status, g_err.c_str());
@@ -520,7 +577,7 @@ int gemm_i8_validate(int64_t M, int64_t N, int64_t K, int transA, int transB, in
 
 const char* gemm_last_error(void) { return dgt::g_err.c_str(); }
 
-const char* gemm_last_path(void) { return dgt::g_path.c_str(); }
+const char* gemm_last_path(void) { return dgt::current_path().c_str(); }
 
 int gemm_tile_order(int64_t tiles_m, int64_t tiles_n, int group_m, int32_t* tm, int32_t* tn) {
   if (tiles_m <= 0 || tiles_n <= 0 || group_m < 1 || !tm || !tn ||
