@@ -86,11 +86,14 @@ def _stream(s):
     return int(s.cuda_stream)
 
 
+_DTYPE_CODES = {"f16": GEMM_DTYPE_F16, "bf16": GEMM_DTYPE_BF16, "f32_f16": GEMM_DTYPE_F32_F16,
+                "f32_bf16": GEMM_DTYPE_F32_BF16, "f8e4m3": GEMM_DTYPE_F8_E4M3,
+                "f8e5m2": GEMM_DTYPE_F8_E5M2}
+
+
 def _dtype(d):
     if isinstance(d, str):
-        return {"f16": GEMM_DTYPE_F16, "bf16": GEMM_DTYPE_BF16, "f32_f16": GEMM_DTYPE_F32_F16,
-                "f32_bf16": GEMM_DTYPE_F32_BF16, "f8e4m3": GEMM_DTYPE_F8_E4M3,
-                "f8e5m2": GEMM_DTYPE_F8_E5M2}[d]
+        return _DTYPE_CODES[d]
     return int(d)
 
 
