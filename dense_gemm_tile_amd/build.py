@@ -1,6 +1,7 @@
 """Build libdense_gemm_tile_amd.so in-tree with hipcc for gfx950.
 
-Usage: python dense_gemm_tile_amd/build.py   (or __graft_entry__.build()). It is
+Usage: python dense_gemm_tile_amd/build.py [--incremental]
+(or __graft_entry__.build(), which always compiles everything). It is
 run as a script, not imported through the package, because importing the
 package requires the library this script builds.
 Objects go to _build/ at the repository root; the shared library lands next to
@@ -44,8 +45,22 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src: str, extra) -> str:
+def _headers():
+    return (glob.glob(os.path.join(CSRC, "*.h")) +
+            glob.glob(os.path.join(ROOT, "include", "*.h")))
+
+
+def _up_to_date(src: str, obj: str) -> bool:
+    if not os.path.exists(obj):
+        return False
+    t = os.path.getmtime(obj)
+    return all(os.path.getmtime(f) <= t for f in [src, *_headers()])
+
+
+def _compile(src: str, extra, incremental: bool = False) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    if incremental and _up_to_date(src, obj):
+        return obj
     cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -53,12 +68,15 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None, extra_flags=()) -> str:
+def build(verbose: bool = False, jobs: int | None = None, extra_flags=(),
+          incremental: bool = False) -> str:
+    """Compile every source (or, with incremental, those whose object is older
+    than the source or any header) and link the library."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags), incremental), srcs))
     tmp = LIB_PATH + ".tmp"
     # -z defs: an undefined symbol (e.g. a kernel stub the compiler did not
     # emit) fails the link instead of the first dlopen.
@@ -73,4 +91,4 @@ def build(verbose: bool = False, jobs: int | None = None, extra_flags=()) -> str
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv[1:])

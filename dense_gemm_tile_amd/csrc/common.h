@@ -99,6 +99,20 @@ __host__ __device__ inline void schedule_tile(int bid, int tiles_m, int tiles_n,
   grouped_tile(lid, tiles_m, tiles_n, group_m, tm, tn);
 }
 
+// Enqueue kernel `k` on `s` with the given arguments. The status returned is
+// that of this launch alone (hipLaunchKernel), so an error left behind by an
+// earlier, unrelated HIP call on the thread is neither reported nor cleared.
+template <class T>
+struct same_type {
+  using type = T;
+};
+template <class... P>
+inline hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s,
+                                typename same_type<P>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, 0, s);
+}
+
 // Launchers (defined next to their kernels). They return the HIP status of
 // the launch.
 struct MfmaTileInfo {

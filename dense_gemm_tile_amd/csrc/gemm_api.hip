@@ -362,33 +362,44 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
       return fail(GEMM_ERR_INVALID_ARG, std::string("GEMM_FORCE_TILE names no tile: ") + ft);
     tile = found;
   }
-  const MfmaTileInfo& ti = mfma_tile_info(tile);
-  plan.mfma = true;
-  plan.tile = tile;
-  // With K groups, the unmasked kernel needs every group's every step whole.
-  plan.masked = (M % ti.bm) || (N % ti.bn) || (K % ((int64_t)ti.bk * ti.kg));
-  // The unmasked kernels address an operand box through a buffer resource
-  // with 32-bit byte offsets spanning up to max(bm, bn, bk) rows of the
-  // operand; larger pitches take the masked kernels' 64-bit addressing.
-  bool big_pitch;
-  {
+  a.a_vw = a_vw;
+  a.b_vw = b_vw;
+  a.src32 = src32 ? (dtype == GEMM_DTYPE_F32_BF16 ? 2 : 1) : 0;
+  // Whether tile t needs the masked kernel (edges, a K tail, narrow staging,
+  // float32 operands off the two-group kernel) and whether its operand boxes
+  // need 64-bit addressing: the unmasked kernels address a box through a
+  // buffer resource with 32-bit byte offsets spanning up to max(bm, bn, bk)
+  // rows of the operand; larger pitches take the masked kernel's 64-bit
+  // addressing. With K groups, the unmasked kernel needs every group's every
+  // step whole.
+  bool big_pitch = false;
+  auto plan_tile = [&](int t) {
+    const MfmaTileInfo& ti = mfma_tile_info(t);
+    plan.masked = (M % ti.bm) || (N % ti.bn) || (K % ((int64_t)ti.bk * ti.kg));
     const int64_t rows = ti.bm > ti.bn ? (ti.bm > ti.bk ? ti.bm : ti.bk)
                                        : (ti.bn > ti.bk ? ti.bn : ti.bk);
     const int64_t ldmax = lda > ldb ? lda : ldb;
     big_pitch = ldmax * esz * rows + 4096 >= (int64_t{1} << 31);
     if (big_pitch) plan.masked = true;
+    // Float32 operands, both K-contiguous, 16-byte rows, whole 256x256 tiles
+    // and K a multiple of its 32-deep slices: the two-group kernel rounds them
+    // as it reads fragments. Every other float32 call is rounded while the
+    // masked kernel stages it.
+    plan.pp_f32 = src32 && t == TILE_256x256 && !transA && transB && !a_elem && !b_elem &&
+                  !big_pitch && M % ti.bm == 0 && N % ti.bn == 0 && K % pp_f32_slice() == 0;
+    if (plan.pp_f32) plan.masked = false;
+    else if (a_elem || b_elem || src32) plan.masked = true;
+  };
+  plan_tile(tile);
+  // The 256x256 tile runs only whole tiles (the two-group kernel); a call
+  // that needs masking at that size takes the 128x128 masked kernel.
+  if (tile == TILE_256x256 && plan.masked) {
+    tile = TILE_128x128;
+    plan_tile(tile);
   }
-  a.a_vw = a_vw;
-  a.b_vw = b_vw;
-  a.src32 = src32 ? (dtype == GEMM_DTYPE_F32_BF16 ? 2 : 1) : 0;
-  // Float32 operands, both K-contiguous, 16-byte rows, whole 256x256 tiles
-  // and K a multiple of its 32-deep slices: the two-group kernel rounds them
-  // as it reads fragments. Every other float32 call is rounded while the
-  // masked kernel stages it.
-  plan.pp_f32 = src32 && tile == TILE_256x256 && !transA && transB && !a_elem && !b_elem &&
-                !big_pitch && M % ti.bm == 0 && N % ti.bn == 0 && K % pp_f32_slice() == 0;
-  if (plan.pp_f32) plan.masked = false;
-  else if (a_elem || b_elem || src32) plan.masked = true;
+  const MfmaTileInfo& ti = mfma_tile_info(tile);
+  plan.mfma = true;
+  plan.tile = tile;
   a.a_fast = !src32 && !big_pitch;
   a.b_fast = !src32 && !big_pitch;
   a.tiles_m = (int)((M + ti.bm - 1) / ti.bm);

@@ -393,25 +393,23 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
 }
 
 template <class Kind>
-void launch_kind(bool ta, bool tb, const GemmByteArgs& a, hipStream_t s) {
-  if (a.pingpong) {
-    gemm_pp_byte_kernel<Kind><<<dim3(a.tiles_m * a.tiles_n), dim3(PingPongCfg::THREADS), 0, s>>>(a);
-    return;
-  }
-  const dim3 grid(a.tiles_m * a.tiles_n), block(kThreads);
-  if (!ta && tb) gemm_byte_kernel<Kind, false, true><<<grid, block, 0, s>>>(a);
-  else if (!ta && !tb) gemm_byte_kernel<Kind, false, false><<<grid, block, 0, s>>>(a);
-  else if (ta && tb) gemm_byte_kernel<Kind, true, true><<<grid, block, 0, s>>>(a);
-  else gemm_byte_kernel<Kind, true, false><<<grid, block, 0, s>>>(a);
+hipError_t launch_kind(bool ta, bool tb, const GemmByteArgs& a, hipStream_t s) {
+  const dim3 grid(a.tiles_m * a.tiles_n);
+  if (a.pingpong)
+    return launch_kernel(gemm_pp_byte_kernel<Kind>, grid, dim3(PingPongCfg::THREADS), s, a);
+  const dim3 block(kThreads);
+  if (!ta && tb) return launch_kernel(gemm_byte_kernel<Kind, false, true>, grid, block, s, a);
+  if (!ta && !tb) return launch_kernel(gemm_byte_kernel<Kind, false, false>, grid, block, s, a);
+  if (ta && tb) return launch_kernel(gemm_byte_kernel<Kind, true, true>, grid, block, s, a);
+  return launch_kernel(gemm_byte_kernel<Kind, true, false>, grid, block, s, a);
 }
 
 }  // namespace
 
 hipError_t launch_byte(int kind, bool ta, bool tb, const GemmByteArgs& a, hipStream_t s) {
-  if (kind == BYTE_I8) launch_kind<KindI8>(ta, tb, a, s);
-  else if (kind == BYTE_F8E4M3) launch_kind<KindF8<0>>(ta, tb, a, s);
-  else launch_kind<KindF8<1>>(ta, tb, a, s);
-  return hipGetLastError();
+  if (kind == BYTE_I8) return launch_kind<KindI8>(ta, tb, a, s);
+  if (kind == BYTE_F8E4M3) return launch_kind<KindF8<0>>(ta, tb, a, s);
+  return launch_kind<KindF8<1>>(ta, tb, a, s);
 }
 
 int byte_tile_m() { return kBM; }

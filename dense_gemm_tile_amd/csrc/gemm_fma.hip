@@ -115,19 +115,17 @@ __global__ void __launch_bounds__(256) scale_c_kernel(const GemmArgs p) {
 
 hipError_t launch_fma(int dtype, bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.tiles_m * a.tiles_n), block(FB_THREADS);
-  if (!ta && !tb) gemm_fma_kernel<false, false><<<grid, block, 0, s>>>(a, dtype);
-  else if (!ta && tb) gemm_fma_kernel<false, true><<<grid, block, 0, s>>>(a, dtype);
-  else if (ta && !tb) gemm_fma_kernel<true, false><<<grid, block, 0, s>>>(a, dtype);
-  else gemm_fma_kernel<true, true><<<grid, block, 0, s>>>(a, dtype);
-  return hipGetLastError();
+  if (!ta && !tb) return launch_kernel(gemm_fma_kernel<false, false>, grid, block, s, a, dtype);
+  if (!ta && tb) return launch_kernel(gemm_fma_kernel<false, true>, grid, block, s, a, dtype);
+  if (ta && !tb) return launch_kernel(gemm_fma_kernel<true, false>, grid, block, s, a, dtype);
+  return launch_kernel(gemm_fma_kernel<true, true>, grid, block, s, a, dtype);
 }
 
 hipError_t launch_scale_c(const GemmArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.M * a.N;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  scale_c_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(scale_c_kernel, dim3((unsigned)blocks), dim3(256), s, a);
 }
 
 }  // namespace dgt

@@ -153,19 +153,19 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_f32_kernel(const
 }
 
 template <class Tag>
-void launch_tag(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_tag(const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.tiles_m * a.tiles_n), block(PingPongCfg::THREADS);
-  if (a.epi == EPI_BETA0) gemm_pp_f32_kernel<Tag, EPI_BETA0><<<grid, block, 0, s>>>(a);
-  else if (a.epi == EPI_ACC_PLUS_C) gemm_pp_f32_kernel<Tag, EPI_ACC_PLUS_C><<<grid, block, 0, s>>>(a);
-  else gemm_pp_f32_kernel<Tag, EPI_GENERAL><<<grid, block, 0, s>>>(a);
+  if (a.epi == EPI_BETA0) return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_BETA0>, grid, block, s, a);
+  if (a.epi == EPI_ACC_PLUS_C)
+    return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_ACC_PLUS_C>, grid, block, s, a);
+  return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_GENERAL>, grid, block, s, a);
 }
 
 }  // namespace
 
 hipError_t launch_pp_f32(int dtype16, const GemmArgs& a, hipStream_t s) {
-  if (dtype16 == 0) launch_tag<TagF16>(a, s);
-  else launch_tag<TagBF16>(a, s);
-  return hipGetLastError();
+  if (dtype16 == 0) return launch_tag<TagF16>(a, s);
+  return launch_tag<TagBF16>(a, s);
 }
 
 int pp_f32_slice() { return 32; }

@@ -755,16 +755,14 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.tiles_m * a.tiles_n), block(Cfg::THREADS);
   switch (a.epi) {
     case EPI_BETA0:
-      gemm_mfma_kernel<Cfg, Tag, TA, TB, MASK, EPI_BETA0><<<grid, block, 0, s>>>(a);
-      break;
+      return launch_kernel(gemm_mfma_kernel<Cfg, Tag, TA, TB, MASK, EPI_BETA0>, grid, block, s, a);
     case EPI_ACC_PLUS_C:
-      gemm_mfma_kernel<Cfg, Tag, TA, TB, MASK, EPI_ACC_PLUS_C><<<grid, block, 0, s>>>(a);
-      break;
+      return launch_kernel(gemm_mfma_kernel<Cfg, Tag, TA, TB, MASK, EPI_ACC_PLUS_C>, grid, block,
+                           s, a);
     default:
-      gemm_mfma_kernel<Cfg, Tag, TA, TB, MASK, EPI_GENERAL><<<grid, block, 0, s>>>(a);
-      break;
+      return launch_kernel(gemm_mfma_kernel<Cfg, Tag, TA, TB, MASK, EPI_GENERAL>, grid, block, s,
+                           a);
   }
-  return hipGetLastError();
 }
 
 template <class Cfg>

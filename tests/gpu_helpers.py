@@ -77,6 +77,23 @@ class Run:
         assert rep["ok"], (self.cfg, self.path, rep)
         return rep
 
+    def check_elements(self, block: int = 64, seed: int = 0):
+        """One element at a random position inside every block x block region
+        of D, each against its own dot product in the oracle."""
+        c = self.cfg
+        rng = np.random.default_rng(seed)
+        I, J = [], []
+        for i0 in range(0, c.M, block):
+            for j0 in range(0, c.N, block):
+                I.append(rng.integers(i0, min(c.M, i0 + block)))
+                J.append(rng.integers(j0, min(c.N, j0 + block)))
+        I, J = np.array(I, dtype=np.int64), np.array(J, dtype=np.int64)
+        D_ref, bound = oracle.gemm_reference_elements(*self.oracle_args(), I, J)
+        got = self.D.numpy()[I, J].astype(np.float64)
+        rep = oracle.check(got, D_ref, bound)
+        assert rep["ok"], (self.cfg, self.path, rep)
+        return rep
+
     def check_padding_untouched(self):
         _, _, _, ldd = self.cfg.lds()
         if ldd > self.cfg.N and not self.cfg.inplace:

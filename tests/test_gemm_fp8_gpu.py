@@ -20,7 +20,7 @@ def _gpu():
 
 
 def run_fp8(dt, M, N, K, tA, tB, alpha, beta, *, seed=0, lda=None, ldb=None, ldd=None,
-            a_off=0, A=None, B=None):
+            a_off=0, A=None, B=None, inplace=False):
     import dense_gemm_tile_amd as dgt
     fmt = FMT[dt]
     lda = lda or (M if tA else K) or 1
@@ -36,10 +36,13 @@ def run_fp8(dt, M, N, K, tA, tB, alpha, beta, *, seed=0, lda=None, ldb=None, ldd
     Ad = a_buf.to(dev)[a_off:]
     Bd = B.reshape(-1).to(dev)
     Cd = C.to(dev)
-    Dd = torch.empty((max(M, 1), ldd), dtype=torch.float32, device=dev)
-    Dd.view(torch.int32).fill_(int(np.uint32(D_SENTINEL).view(np.int32)))
+    if inplace:  # D is C itself (same pointer and leading dimension)
+        Dd = Cd
+    else:
+        Dd = torch.empty((max(M, 1), ldd), dtype=torch.float32, device=dev)
+        Dd.view(torch.int32).fill_(int(np.uint32(D_SENTINEL).view(np.int32)))
     say(f"{dt} M={M} N={N} K={K} tA={tA} tB={tB} a={alpha} b={beta} lds={lda},{ldb},{ldd} "
-        f"off={a_off}")
+        f"off={a_off} inplace={inplace}")
     dgt.gemm(M, N, K, dt, tA, tB, alpha, beta, Ad, lda, Bd, ldb, Cd if beta != 0 else None,
              ldd, Dd, ldd)
     path = dgt.gemm_last_path()
@@ -144,3 +147,20 @@ def test_fp8_pingpong_exact_small_integers():
     D, _, _, path = run_fp8("f8e4m3", M, N, K, 0, 1, 1.0, 0.0, A=A, B=B)
     assert "pingpong" in path, path
     assert np.array_equal(D[:M, :N], (av @ bv.T).astype(np.float32))
+
+
+@pytest.mark.parametrize("dt", ["f8e4m3", "f8e5m2"])
+def test_fp8_inplace_c_is_d(dt):
+    """D may be C itself: each element of C is read before the same lane
+    writes D there. Both the 128x128 kernel (a ragged shape) and the
+    two-group kernel (whole 256x256 NT tiles) are run with C == D and a
+    general epilogue, against the oracle on the original C."""
+    for (M, N, K, tA, tB) in [(300, 129, 520, 1, 0), (512, 768, 384, 0, 1)]:
+        D, D_ref, bound, path = run_fp8(dt, M, N, K, tA, tB, 1.5, -0.75, seed=970 + M,
+                                        inplace=True)
+        if (tA, tB) == (0, 1):
+            assert "pingpong" in path, path
+        else:
+            assert "pingpong" not in path, path
+        rep = oracle.check(D[:M, :N].astype(np.float64), D_ref, bound)
+        assert rep["ok"], (dt, M, N, K, rep)

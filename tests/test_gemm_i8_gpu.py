@@ -137,3 +137,14 @@ def test_i8_pingpong_whole_tiles_slice_counts():
             assert "pingpong" in path, path
             assert np.array_equal(got[:M, :N], ref), (K, alpha, beta)
             assert np.all(got[:M, N:] == SENTINEL)
+
+
+def test_i8_inplace_c_is_d_on_both_kernels():
+    """C == D with a general epilogue on the two-group kernel (whole 256x256
+    NT tiles) and on the 128x128 kernel (other layouts), bit-exact."""
+    got, ref, path = run_i8(512, 768, 640, 0, 1, -3, 2, seed=930, inplace=True)
+    assert "pingpong" in path, path
+    assert np.array_equal(got[:512, :768], ref)
+    got, ref, path = run_i8(512, 768, 640, 1, 0, 5, -1, seed=931, inplace=True)
+    assert "pingpong" not in path, path
+    assert np.array_equal(got[:512, :768], ref)
