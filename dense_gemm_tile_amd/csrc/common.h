@@ -32,6 +32,18 @@ struct GemmArgs {
   int b_fast;    //    (16-bit values; 32-bit byte offsets reach every box):
                  //    the masked kernel then reads the whole K steps of its
                  //    interior tiles that way (same for B)
+  int a_direct;  // 128x128 ring kernel: 1 if A is loaded straight into LDS
+  int b_direct;  //    (16-byte rows, edges of its contiguous dimension on
+                 //    multiples of 8 elements), 0 if staged through registers
+  int ring_mode; // 128x128 ring kernel: RingMode below
+};
+
+// Forms of the 128x128 ring kernel.
+enum RingMode : int {
+  RING_SHARED = 0,   // five half-slots (80 KiB): two workgroups share a CU
+  RING_KSPLIT2 = 1,  // two K groups of 4 waves per workgroup, a ring each
+  RING_DEEP = 2,     // ten half-slots (160 KiB), slices requested four ahead;
+                     //    both operands loaded straight into LDS
 };
 
 // Arguments of the 1-byte-operand kernels (see gemm_byte.hip): int8 ->
@@ -130,6 +142,10 @@ const MfmaTileInfo& mfma_tile_info(int tile);
 
 hipError_t launch_mfma(int tile, int dtype, bool transA, bool transB, bool masked,
                        const GemmArgs& a, hipStream_t stream);
+// 128x128 tiles on the direct-to-LDS ring kernel: f16 (dtype 0) or bf16 (1)
+// operands, any layout, any M/N/K, row pitches up to the 32-bit offset rule.
+hipError_t launch_ring128(int dtype, bool transA, bool transB, const GemmArgs& a,
+                          hipStream_t stream);
 // Output tile of the VALU-FMA fallback.
 constexpr int kFmaTileM = 64, kFmaTileN = 64;
 

@@ -31,9 +31,11 @@ struct MfmaPath {
   const MfmaTileInfo* ti;
   const char* ops;
   const char* epi;
-  bool pingpong, masked, k16_tail;
+  bool pingpong, masked, k16_tail, ring;
+  int ring_mode;
   const char* src32;  // "", " f32->f16" or " f32->bf16"
-  std::string elem_reason;
+  std::string elem_reason;  // operands read in narrow pieces (general kernel)
+  std::string staged;       // operands staged through registers (ring kernel)
 };
 thread_local MfmaPath g_mpath;
 thread_local bool g_path_lazy = false;
@@ -43,13 +45,18 @@ const std::string& current_path() {
     const MfmaPath& m = g_mpath;
     char buf[512], ksplit[32] = "";
     if (m.ti->kg > 1) std::snprintf(ksplit, sizeof ksplit, " ksplit%d", m.ti->kg);
-    std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s%s%s",
+    std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s%s%s%s%s%s%s",
                   m.ti->name, m.ti->waves_m, m.pingpong ? 4 : m.ti->waves_n, m.ti->atom_m,
                   m.ti->atom_n, m.ti->atom_k, m.ops, m.epi, ksplit,
-                  m.pingpong ? " pingpong" : "", m.masked ? " masked" : "",
-                  m.k16_tail ? " k16-tail" : "", m.src32,
+                  m.pingpong ? " pingpong" : "",
+                  !m.ring ? ""
+                  : m.ring_mode == RING_KSPLIT2 ? " ring ksplit2"
+                  : m.ring_mode == RING_DEEP ? " ring deep" : " ring",
+                  m.masked ? " masked" : "", m.k16_tail ? " k16-tail" : "", m.src32,
                   m.elem_reason.empty() ? "" : " narrow staging (", m.elem_reason.c_str(),
-                  m.elem_reason.empty() ? "" : ")");
+                  m.elem_reason.empty() ? "" : ")",
+                  m.staged.empty() ? "" : " staged (", m.staged.c_str(),
+                  m.staged.empty() ? "" : ")");
     g_path = buf;
     g_path_lazy = false;
   }
@@ -62,6 +69,7 @@ struct EnvSwitches {
   const char* force_path = nullptr;  // GEMM_FORCE_PATH
   const char* force_tile = nullptr;  // GEMM_FORCE_TILE
   const char* log = nullptr;         // GEMM_LOG
+  const char* ring_mode = nullptr;   // GEMM_RING_MODE: form of the 128x128 ring kernel
 };
 thread_local EnvSwitches g_env;
 
@@ -74,10 +82,12 @@ void read_env() {
     if (std::strncmp(v, "FORCE_PATH=", 11) == 0) g_env.force_path = v + 11;
     else if (std::strncmp(v, "FORCE_TILE=", 11) == 0) g_env.force_tile = v + 11;
     else if (std::strncmp(v, "LOG=", 4) == 0) g_env.log = v + 4;
+    else if (std::strncmp(v, "RING_MODE=", 10) == 0) g_env.ring_mode = v + 10;
   }
   if (g_env.force_path && !*g_env.force_path) g_env.force_path = nullptr;
   if (g_env.force_tile && !*g_env.force_tile) g_env.force_tile = nullptr;
   if (g_env.log && !*g_env.log) g_env.log = nullptr;
+  if (g_env.ring_mode && !*g_env.ring_mode) g_env.ring_mode = nullptr;
 }
 
 // Largest dimension the int32 index arithmetic in the kernels supports.
@@ -90,6 +100,7 @@ struct Plan {
   int tile = 0;
   bool masked = false;
   bool pp_f32 = false;  // float32 operands on the two-group kernel
+  bool ring = false;    // 16-bit operands on the 128x128 direct-to-LDS ring kernel
   int epi = EPI_BETA0;
   GemmArgs args{};
   bool byte8 = false;  // 8-bit float operands: the 1-byte-operand kernel
@@ -409,6 +420,58 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   // Whole 256x256 tiles (any operand layout) take the kernel with two wave
   // groups (2x4 waves) and direct global->LDS loads.
   const bool pingpong = tile == TILE_256x256 && !plan.masked;  // includes plan.pp_f32
+  // 128x128 tiles of 16-bit operands take the direct-to-LDS ring kernel,
+  // edges, K tails and unaligned rows included; each operand is loaded
+  // straight into LDS when its base and row pitch are multiples of 16 bytes
+  // and the edges cutting its contiguous dimension fall on multiples of 8
+  // elements, else staged through registers.
+  std::string staged;
+  plan.ring = tile == TILE_128x128 && !src32 && !big_pitch;
+  if (plan.ring) {
+    auto direct = [&](int vw, bool mn_contig, int64_t mn) {
+      return vw == 8 && (mn_contig ? mn % 8 == 0 : K % 8 == 0);
+    };
+    a.a_direct = direct(a_vw, transA != 0, M) ? 1 : 0;
+    a.b_direct = direct(b_vw, transB == 0, N) ? 1 : 0;
+    auto why = [&](const char* name, const void* ptr, int64_t ld, int vw, bool mn_contig) {
+      char w[160];
+      if (vw != 8) {
+        if ((uintptr_t)ptr % 16 != 0)
+          std::snprintf(w, sizeof w, "%s: base address is not 16-byte aligned", name);
+        else
+          std::snprintf(w, sizeof w, "%s: row pitch %lld B is not a multiple of 16 B", name,
+                        (long long)(ld * 2));
+      } else {
+        std::snprintf(w, sizeof w, "%s: %s %% 8 != 0", name,
+                      mn_contig ? (name[0] == 'A' ? "M" : "N") : "K");
+      }
+      return std::string(w);
+    };
+    if (!a.a_direct) staged = why("A", A, lda, a_vw, transA != 0);
+    if (!a.b_direct) staged += (staged.empty() ? "" : "; ") + why("B", B, ldb, b_vw, transB == 0);
+    elem_reason.clear();
+    // "masked": edge tiles or a K tail (the ring kernel masks in place)
+    plan.masked = (M % ti.bm) || (N % ti.bn) || (K % ti.bk);
+    // Grids of at most one tile per CU: the deep ring (every slice requested
+    // four slices ahead from 160 KiB of LDS) when both operands go straight
+    // into LDS, else K split over two wave groups per workgroup (8 waves,
+    // two rings), so that each SIMD still alternates between two waves.
+    // Larger grids: one group per workgroup, two workgroups per CU.
+    const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
+    a.ring_mode = ntiles > 256 ? RING_SHARED
+                  : (a.a_direct && a.b_direct) ? RING_DEEP : RING_KSPLIT2;
+    if (const char* rm = g_env.ring_mode) {
+      if (std::strcmp(rm, "shared") == 0) a.ring_mode = RING_SHARED;
+      else if (std::strcmp(rm, "ksplit2") == 0) a.ring_mode = RING_KSPLIT2;
+      else if (std::strcmp(rm, "deep") == 0 && a.a_direct && a.b_direct) a.ring_mode = RING_DEEP;
+      else if (std::strcmp(rm, "deep") == 0)
+        return fail(GEMM_ERR_UNSUPPORTED,
+                    "GEMM_RING_MODE=deep needs both operands loaded straight into LDS");
+      else
+        return fail(GEMM_ERR_INVALID_ARG,
+                    std::string("GEMM_RING_MODE must be shared, ksplit2 or deep, got ") + rm);
+    }
+  }
   // A last K step whose valid part ends within the first half of a 16x16x32
   // sub-step finishes with v_mfma_f32_16x16x16 (no product of staged zeros).
   const bool k16_tail = ti.atom_k == 32 && K % 32 >= 1 && K % 32 <= 16;
@@ -416,6 +479,9 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   g_mpath.ops = ops;
   g_mpath.epi = epi_name;
   g_mpath.pingpong = pingpong;
+  g_mpath.ring = plan.ring;
+  g_mpath.ring_mode = a.ring_mode;
+  g_mpath.staged.swap(staged);
   g_mpath.masked = plan.masked;
   g_mpath.k16_tail = k16_tail;
   g_mpath.src32 = !src32 ? "" : dtype == GEMM_DTYPE_F32_BF16 ? " f32->bf16" : " f32->f16";
@@ -507,6 +573,18 @@ int plan_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alp
   return GEMM_OK;
 }
 
+// Launch a planned call.
+hipError_t launch_plan(const Plan& plan, int dtype, int transA, int transB, hipStream_t s) {
+  if (plan.noop) return hipSuccess;
+  if (plan.scale_only) return launch_scale_c(plan.args, s);
+  if (plan.byte8) return launch_byte(plan.byte_kind, transA != 0, transB != 0, plan.bargs, s);
+  if (plan.pp_f32) return launch_pp_f32(dtype & 1, plan.args, s);
+  if (plan.ring) return launch_ring128(dtype & 1, transA != 0, transB != 0, plan.args, s);
+  if (plan.mfma)
+    return launch_mfma(plan.tile, dtype & 1, transA != 0, transB != 0, plan.masked, plan.args, s);
+  return launch_fma(dtype, transA != 0, transB != 0, plan.args, s);
+}
+
 void log_call(int64_t M, int64_t N, int64_t K, int status) {
   const char* lv = g_env.log;
   if (!lv || std::strcmp(lv, "debug") != 0) return;
@@ -530,17 +608,8 @@ int gemm(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB, flo
   Plan plan;
   int st = plan_call(M, N, K, dtype, transA, transB, alpha, beta, A, lda, B, ldb, C, ldc, D, ldd,
                      plan);
-  if (st == GEMM_OK && !plan.noop) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (plan.scale_only) e = launch_scale_c(plan.args, s);
-    else if (plan.byte8)
-      e = launch_byte(plan.byte_kind, transA != 0, transB != 0, plan.bargs, s);
-    else if (plan.pp_f32)
-      e = launch_pp_f32(dtype & 1, plan.args, s);
-    else if (plan.mfma)
-      e = launch_mfma(plan.tile, dtype & 1, transA != 0, transB != 0, plan.masked, plan.args, s);
-    else e = launch_fma(dtype, transA != 0, transB != 0, plan.args, s);
+  if (st == GEMM_OK) {
+    const hipError_t e = launch_plan(plan, dtype, transA, transB, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
       st = fail(GEMM_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   }

@@ -476,10 +476,11 @@ __device__ inline float epi_one(float x, float c, float alpha, float beta) {
 // is (r0, c0); C is read only for the epilogue kinds that need it.
 //
 // Each accumulator register group holds 4 consecutive rows of one column per
-// lane. On whole tiles with 16-byte aligned D (and C), a quad transpose turns
-// that into 4 consecutive columns of one row per lane, so C is read and D is
-// written with 16-byte accesses; otherwise elements are written one by one
-// with bounds checks.
+// lane. With 16-byte aligned D (and C), a quad transpose turns that into 4
+// consecutive columns of one row per lane, so C is read and D is written with
+// 16-byte accesses (on edge tiles too when N is a multiple of 4, each lane
+// checking its row and quad); otherwise elements are written one by one with
+// bounds checks.
 //
 // C may be D itself (the in-place form; any other overlap is rejected on the
 // host), so the compiler may not move a C load above an earlier D store. The
@@ -517,7 +518,10 @@ __device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::T
   constexpr int NG = At::NACC / 4;  // groups of 4 rows per atom and lane
   const float alpha = p.alpha, beta = p.beta;
   const int col_l = At::acc_col(lane);
-  if (!MASK && p.wide_epi) {
+  // The 16-byte form also serves masked tiles when N is a multiple of 4:
+  // every quad of columns a lane stores then lies wholly inside or outside
+  // N, so one predicate per lane and row decides it.
+  if (p.wide_epi && (!MASK || p.N % 4 == 0)) {
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
       f32x4 cv[Cfg::TN][NG];
@@ -533,7 +537,9 @@ __device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::T
           for (int g = 0; g < NG; ++g) {
             const int c = c0 + j * At::N + (col_l & ~3);
             const int r = r0 + i * At::M + At::acc_row(lane, 4 * g) + (lane & 3);
-            cv[j][g] = *reinterpret_cast<const f32x4*>(p.C + (int64_t)r * p.ldc + c);
+            cv[j][g] = (!MASK || (r < p.M && c < p.N))
+                           ? *reinterpret_cast<const f32x4*>(p.C + (int64_t)r * p.ldc + c)
+                           : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
           }
       }
 #pragma unroll
@@ -558,7 +564,8 @@ __device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::T
             o[3] = epi_one<EPI>(x[3], 0.0f, alpha, beta);
           }
           // D is written once and not read back here: stream it past the caches.
-          __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(p.D + (int64_t)r * p.ldd + c));
+          if (!MASK || (r < p.M && c < p.N))
+            __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(p.D + (int64_t)r * p.ldd + c));
         }
       }
     }
@@ -765,12 +772,16 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
   }
 }
 
-template <class Cfg>
+// MASKED_ONLY: only the masked kernels are compiled (the configuration's
+// unmasked calls run elsewhere); an unmasked launch request then fails.
+template <class Cfg, bool MASKED_ONLY = false>
 hipError_t launch_mfma_cfg(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a,
                            hipStream_t s) {
-#define DGT_LAUNCH_MASK(TAG, TA_, TB_)                               \
-  return masked ? launch_epi<Cfg, TAG, TA_, TB_, true>(a, s)         \
-                : launch_epi<Cfg, TAG, TA_, TB_, false>(a, s)
+  if (MASKED_ONLY && !masked) return hipErrorInvalidValue;
+#define DGT_LAUNCH_MASK(TAG, TA_, TB_)                                                \
+  if constexpr (MASKED_ONLY) return launch_epi<Cfg, TAG, TA_, TB_, true>(a, s);       \
+  else return masked ? launch_epi<Cfg, TAG, TA_, TB_, true>(a, s)                     \
+                     : launch_epi<Cfg, TAG, TA_, TB_, false>(a, s)
 #define DGT_LAUNCH_T(TAG)                          \
   do {                                             \
     if (!ta && !tb) DGT_LAUNCH_MASK(TAG, false, false); \

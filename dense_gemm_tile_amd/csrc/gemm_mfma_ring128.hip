@@ -1,0 +1,165 @@
+// 128x128 tiles on the ring design (gemm_ring.h): the kernel for mid-size
+// shapes (too few 256x256 tiles to fill the chip), ragged shapes and operands
+// whose rows are not 16-byte aligned, for f16/bf16 operands in any of the
+// four layouts. Three forms: two workgroups per CU (five half-slots each),
+// two K groups per workgroup, and the deep ring below for grids of at most
+// one tile per CU.
+#include "gemm_ring.h"
+
+namespace dgt {
+
+namespace {
+
+// Deep ring: both operands loaded straight into LDS, one workgroup of 4
+// waves per CU with all 160 KiB as ten half-slots, so that every half-slice
+// is requested four slices before it is multiplied (slot 2t % 10 for A of
+// slice t, 2t+1 for B). For grids of at most one tile per CU, where no second
+// workgroup shares the CU and the loads' latency has to be covered by
+// requests in flight alone.
+template <class Tag, int EPI, bool AMN, bool BMN>
+__global__ void __launch_bounds__(Ring128Cfg::THREADS, 1)
+gemm_ring128_deep_kernel(const GemmArgs p) {
+  using C = Ring128Cfg;
+  using At = typename C::At;
+  using acc_t = typename At::acc_t;
+  constexpr int SLOTS = 10, AHEAD = SLOTS / 2 - 1;  // slices requested ahead
+  __shared__ __attribute__((aligned(1024))) char smem[SLOTS * C::HALF_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  int tm, tn;
+  schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+
+  RingOperand<AMN, 128> a;
+  RingOperand<BMN, 128> b;
+  a.init(p.A, p.lda, m0, p.M, p.K, wm, lane);
+  b.init(p.B, p.ldb, n0, p.N, p.K, wn, lane);
+
+  acc_t acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < At::NACC; ++v) acc[i][j][v] = 0.0f;
+
+  const int KT = (p.K + C::BK - 1) / C::BK;
+  auto slot = [&](int h) { return smem + (h % SLOTS) * C::HALF_BYTES; };
+  auto request = [&](int t) {
+    a.issue_direct(slot(2 * t), t, w, lane);
+    b.issue_direct(slot(2 * t + 1), t, w, lane);
+  };
+  // Wait until slice t is in LDS: the slices requested after it may stay in
+  // flight (each is 2 x LOADS instructions of this wave).
+  auto wait_for = [&](int t) {
+    int after = KT - 1 - t;
+    after = after < 0 ? 0 : (after > AHEAD - 1 ? AHEAD - 1 : after);
+    if (after >= 3) pp_wait_vm_lgkm0<6 * C::LOADS>();
+    else if (after == 2) pp_wait_vm_lgkm0<4 * C::LOADS>();
+    else if (after == 1) pp_wait_vm_lgkm0<2 * C::LOADS>();
+    else pp_wait_vm_lgkm0<0>();
+  };
+  static_assert(AHEAD == 4, "wait_for counts at most three slices in flight behind the next");
+
+  // Interior tiles that read C request it right after the prologue's loads
+  // (64 registers per lane; one wave per SIMD leaves room), so it arrives
+  // while the K loop runs.
+  constexpr bool PRE_C = EPI != EPI_BETA0;
+  const bool inner = m0 + C::BM <= p.M && n0 + C::BN <= p.N;
+  const bool pre_c = PRE_C && p.wide_epi && inner;
+  WideC<C> cpre;
+  constexpr int NC = PRE_C ? C::TM * C::TN * At::NACC / 4 : 0;  // C loads per lane
+
+  // Prologue: slices 0 .. AHEAD-1, then C; wait for slice 0.
+  for (int t = 0; t < AHEAD && t < KT; ++t) request(t);
+  if constexpr (PRE_C) {
+    if (pre_c) load_wide_c<C>(cpre, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane);
+    if (pre_c) {
+      const int after = KT - 1 < AHEAD - 1 ? KT - 1 : AHEAD - 1;
+      if (after >= 3) pp_wait_vm_lgkm0<6 * C::LOADS + NC>();
+      else if (after == 2) pp_wait_vm_lgkm0<4 * C::LOADS + NC>();
+      else if (after == 1) pp_wait_vm_lgkm0<2 * C::LOADS + NC>();
+      else pp_wait_vm_lgkm0<NC>();
+    } else {
+      wait_for(0);
+    }
+  } else {
+    wait_for(0);
+  }
+  pp_barrier();
+
+  for (int s = 0; s < KT; ++s) {
+    // The slots of slice s-1 are free (all waves passed the barrier after
+    // their last read of it): request slice s+AHEAD into them.
+    if (s + AHEAD < KT) request(s + AHEAD);
+    const char* sa = slot(2 * s);
+    const char* sb = slot(2 * s + 1);
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      u32x4 fa[C::TM], fb[C::TN];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) fa[i] = a.read(sa, i, ks);
+#pragma unroll
+      for (int jj = 0; jj < C::TN; ++jj) fb[jj] = b.read(sb, jj, ks);
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < C::TN; ++jj) acc[i][jj] = At::mma(Tag{}, fa[i], fb[jj], acc[i][jj]);
+    }
+    if (s + 1 < KT) wait_for(s + 1);
+    else pp_wait_lgkm0();
+    pp_barrier();
+  }
+
+  if (inner) store_tile<C, EPI, false>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane, cpre, pre_c);
+  else store_tile<C, EPI, true>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane);
+}
+
+template <class Tag, bool AMN, bool BMN>
+hipError_t launch_ring_deep(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid(a.tiles_m * a.tiles_n), block(Ring128Cfg::THREADS);
+  if (a.epi == EPI_BETA0)
+    return launch_kernel(gemm_ring128_deep_kernel<Tag, EPI_BETA0, AMN, BMN>, grid, block, s, a);
+  if (a.epi == EPI_ACC_PLUS_C)
+    return launch_kernel(gemm_ring128_deep_kernel<Tag, EPI_ACC_PLUS_C, AMN, BMN>, grid, block, s,
+                         a);
+  return launch_kernel(gemm_ring128_deep_kernel<Tag, EPI_GENERAL, AMN, BMN>, grid, block, s, a);
+}
+
+template <class Tag, bool AMN, bool BMN, int KG>
+hipError_t launch_ring_kg(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid(a.tiles_m * a.tiles_n), block(Ring128Cfg::THREADS * KG);
+  if (a.epi == EPI_BETA0)
+    return launch_kernel(gemm_ring_kernel<128, Tag, EPI_BETA0, AMN, BMN, KG, true>, grid, block, s, a);
+  if (a.epi == EPI_ACC_PLUS_C)
+    return launch_kernel(gemm_ring_kernel<128, Tag, EPI_ACC_PLUS_C, AMN, BMN, KG, true>, grid, block, s,
+                         a);
+  return launch_kernel(gemm_ring_kernel<128, Tag, EPI_GENERAL, AMN, BMN, KG, true>, grid, block, s, a);
+}
+
+template <class Tag, bool AMN, bool BMN>
+hipError_t launch_ring(const GemmArgs& a, hipStream_t s) {
+  if (a.ring_mode == RING_DEEP) return launch_ring_deep<Tag, AMN, BMN>(a, s);
+  if (a.ring_mode == RING_KSPLIT2) return launch_ring_kg<Tag, AMN, BMN, 2>(a, s);
+  return launch_ring_kg<Tag, AMN, BMN, 1>(a, s);
+}
+
+template <class Tag>
+hipError_t launch_ring_layout(bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
+  // A is M-contiguous when stored transposed; B is N-contiguous when not.
+  if (!ta && tb) return launch_ring<Tag, false, false>(a, s);
+  if (!ta && !tb) return launch_ring<Tag, false, true>(a, s);
+  if (ta && tb) return launch_ring<Tag, true, false>(a, s);
+  return launch_ring<Tag, true, true>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_ring128(int dtype, bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
+  if (dtype == 0) return launch_ring_layout<TagF16>(ta, tb, a, s);
+  return launch_ring_layout<TagBF16>(ta, tb, a, s);
+}
+
+}  // namespace dgt

@@ -1,0 +1,468 @@
+// The ring design of the 128x128 direct-to-LDS kernel
+// (gemm_mfma_ring128.hip), written for a square tile of side ROWS.
+//
+// Same contraction and atom nest as the other matrix-core kernels (TVM TIRx
+// `gemm`: "Algorithm" steps 1-3), with asynchronous operand staging in the
+// spirit of Phobos `@pipeline`, laid out for CDNA4:
+//
+//  * 4 waves (2 x 2) per K group; each wave computes a (ROWS/2)x(ROWS/2)
+//    block of the tile with v_mfma_f32_32x32x16 atoms. At ROWS = 128 that is
+//    64 accumulator registers per lane and 80 KiB of LDS, so two workgroups
+//    share a CU (or, with two K groups, one workgroup of 8 waves uses the
+//    whole 160 KiB).
+//  * LDS is a ring of five half-slots, each one operand of one K slice of
+//    64; A of slice t lives in slot 2t % 5 and B in slot (2t+1) % 5.
+//    Iteration s multiplies slice s; right after its barrier the slots of
+//    slice s-1 are free and take B of slice s+1 and A of slice s+2, so every
+//    load has one or two iterations to land.
+//  * Operands are read in the layout they are stored in: a K-contiguous
+//    operand (A stored [M][K], B stored [N][K]) fills a slot as ROWS rows of
+//    128 bytes with chunk c of row r at c ^ ((r ^ r>>3) & 7), one
+//    ds_read_b128 per fragment; an M/N-contiguous one (A stored [K][M], B
+//    stored [K][N]) as 64 K-rows of 2*ROWS bytes with chunk c of row r at
+//    c ^ (4 (r & 3)), two ds_read_b64_tr_b16 (transposed reads) per fragment.
+//    No operand is transposed in registers.
+//  * Staging, per operand and per call: direct, when the operand's base and
+//    row pitch are multiples of 16 bytes and every edge that cuts its
+//    contiguous dimension falls on a multiple of 8 elements: each lane's
+//    buffer_load_dwordx4 writes its 16 bytes straight into LDS, and pieces
+//    wholly outside the operand get an out-of-range offset, which the
+//    hardware answers with zeros. Otherwise staged: the same 16-byte pieces
+//    go through registers (read as the dword-aligned dwords that cover them
+//    and shifted into place, so any 2-byte alignment works; the buffer's
+//    record count ends at the dword holding the operand's last element),
+//    elements past an edge are zeroed, and one ds_write_b128 per piece puts
+//    them where the direct load would have.
+//  * Edge tiles store D element by element with bounds checks; interior
+//    tiles with 16-byte accesses.
+#pragma once
+
+#include "gemm_mfma_pingpong.h"
+
+namespace dgt {
+
+template <int ROWS>
+struct RingCfg {
+  static constexpr int BM = ROWS, BN = ROWS, BK = 64;
+  static constexpr int WM = 2, WN = 2, THREADS = WM * WN * 64;
+  using At = Atom<32>;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int TM = WTM / At::M, TN = WTN / At::N;
+  static constexpr int KSTEPS = BK / At::K;
+  static constexpr int HALF_BYTES = ROWS * BK * 2;  // one operand of one slice
+  static constexpr int SLOTS = 5;
+  static constexpr int LDS_BYTES = SLOTS * HALF_BYTES;
+  static constexpr int LOADS = HALF_BYTES / 1024 / (THREADS / 64);  // per wave per half
+  static constexpr int MIN_WG = (160 * 1024) / LDS_BYTES;  // workgroups per CU (KG = 1)
+  // Only the 128x128 tile is built: a 256x256 four-wave form (128x128 per
+  // wave) measured 23 % slower at 8192^3 than the two-group kernel.
+  static_assert(ROWS == 128, "tile side 128");
+  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+};
+using Ring128Cfg = RingCfg<128>;
+
+constexpr int kOutOfRange = (int)0x80000000u;
+
+// A buffer resource over `base` whose record count is `nrec` bytes: offsets
+// at or past it read as zero.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, unsigned nrec) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nrec,
+                                           0x00020000);
+}
+
+// Record count for a resource based at `b` over an operand that starts at
+// `X` and whose stored extent is `ext` bytes: up to the end of the dword
+// (in memory, 4-byte aligned) that holds the operand's last byte, at most
+// 2^31 - 4 bytes.
+__device__ inline unsigned nrec_from(const char* X, int64_t ext, const char* b) {
+  const uintptr_t end = ((uintptr_t)X + (uintptr_t)ext + 3) & ~(uintptr_t)3;
+  const int64_t n = (int64_t)(end - (uintptr_t)b);
+  if (n <= 0) return 0u;
+  return n > 0x7FFFFFFC ? 0x7FFFFFFCu : (unsigned)n;
+}
+
+// Zero the 16-bit elements of a 16-byte piece from index nv (0..8) on.
+__device__ inline u32x4 keep_first(u32x4 v, int nv) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const unsigned lo = 2 * d < nv ? 0x0000FFFFu : 0u;
+    const unsigned hi = 2 * d + 1 < nv ? 0xFFFF0000u : 0u;
+    v[d] &= lo | hi;
+  }
+  return v;
+}
+
+// One operand: its loads into a half-slot (direct or staged through
+// registers) and its fragment reads. MN: stored with M (or N) contiguous.
+// Instruction i (0..3) of wave w writes LDS bytes [(4w + i) KiB, +1 KiB) of
+// the half-slot, lane l the 16 bytes at l * 16 of that.
+template <bool MN, int ROWS>
+struct RingOperand {
+  using Cfg = RingCfg<ROWS>;
+  static constexpr int LOADS = Cfg::LOADS;
+  static constexpr int NFRAG = Cfg::TM;   // atoms per wave along this operand
+  static constexpr int RB = ROWS * 2;     // bytes of one K-row of an M/N-contiguous slot
+  const char* X;  // operand base
+  int64_t ld2;    // row pitch in bytes
+  int64_t ext;    // bytes of the stored extent ((rows - 1) * ld + cols) * 2
+  int r0;         // tile origin along M (or N)
+  int rlim;       // M (or N)
+  int klim;       // K
+  int off[NFRAG];  // fragment read offsets of this lane's atoms, sub-step 0
+
+  // Logical position of the piece lane `lane` moves in instruction i of wave
+  // w: K-contiguous: tile row rr (0..ROWS-1) and K chunk cc (0..7) of the
+  // slice (an instruction covers 8 rows of 128 bytes); M/N-contiguous: slice
+  // K-row rr (0..63) and M/N chunk cc (0..ROWS/8-1) (an instruction covers
+  // 1024/RB K-rows of RB bytes).
+  __device__ static inline void piece(int w, int i, int lane, int& rr, int& cc) {
+    if constexpr (!MN) {
+      rr = (ROWS / 4) * w + 8 * i + (lane >> 3);
+      cc = (lane & 7) ^ ((rr ^ (rr >> 3)) & 7);
+    } else {
+      constexpr int CPR = ROWS / 8;  // 16-byte chunks per K-row
+      rr = 16 * w + (64 / CPR) * i + lane / CPR;
+      cc = (lane % CPR) ^ (4 * (rr & 3));
+    }
+  }
+
+  __device__ inline void init(const void* Xv, int64_t ld, int r0_, int rlim_, int klim_,
+                              int wsub, int lane) {
+    X = static_cast<const char*>(Xv);
+    ld2 = ld * 2;
+    r0 = r0_;
+    rlim = rlim_;
+    klim = klim_;
+    ext = MN ? ((int64_t)(klim - 1) * ld + rlim) * 2 : ((int64_t)(rlim - 1) * ld + klim) * 2;
+    if constexpr (!MN) {
+#pragma unroll
+      for (int t = 0; t < NFRAG; ++t)
+        off[t] = lds_off(wsub * (ROWS / 2) + t * 32 + (lane & 31), lane >> 5);
+    } else {
+      // Lane l (16-lane group g = l/16, s = l%16) of the first transposed
+      // read names K-row 8 (l/32) + s/4 and columns 16 (g & 1) + 4 (s % 4)
+      // .. +3 of its atom; the second read is 4 rows down, sub-step ks is 16
+      // ks rows down (both keep r & 3, so the swizzle is unchanged).
+      const int r = 8 * (lane >> 5) + ((lane & 15) >> 2);
+#pragma unroll
+      for (int t = 0; t < NFRAG; ++t) {
+        const int col = wsub * (ROWS / 2) + t * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        off[t] = r * RB + (((col >> 3) ^ (4 * (r & 3))) << 4) + ((col & 7) << 1);
+      }
+    }
+  }
+
+  // Resource base and record count for slice t, and the byte offset of the
+  // piece (rr, cc) from that base, or kOutOfRange if the piece lies wholly
+  // outside the operand. `start` is the piece's first index along the
+  // contiguous dimension and `lim` that dimension's size (for masking).
+  __device__ inline const char* slice_base(int t) const {
+    return MN ? X + (int64_t)t * Cfg::BK * ld2 + (int64_t)r0 * 2 : X + (int64_t)r0 * ld2;
+  }
+  __device__ inline int piece_off(int t, int rr, int cc, int& start, int& lim) const {
+    if constexpr (!MN) {
+      start = t * Cfg::BK + cc * 8;
+      lim = klim;
+      const bool in = r0 + rr < rlim && start < klim;
+      return in ? (int)(rr * ld2) + start * 2 : kOutOfRange;
+    } else {
+      start = r0 + cc * 8;
+      lim = rlim;
+      const bool in = t * Cfg::BK + rr < klim && start < rlim;
+      return in ? (int)(rr * ld2) + cc * 16 : kOutOfRange;
+    }
+  }
+
+  __device__ __forceinline__ void issue_direct(char* slot, int t, int w, int lane) const {
+    const char* b = slice_base(t);
+    const auto rs = make_rsrc_n(b, nrec_from(X, ext, b));
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      int rr, cc, start, lim;
+      piece(w, i, lane, rr, cc);
+      const int voff = piece_off(t, rr, cc, start, lim);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (pp_lds_ptr_t)(slot + (4 * w + i) * 1024), 16,
+                                               voff, 0, 0, 0);
+    }
+  }
+
+  // Staged loads of slice t: each 16-byte piece (2-byte aligned) is read as
+  // the dwords that cover it, with dword-aligned addresses only: four from
+  // the dword at or below its start and one more after them. The record
+  // count then cuts at a dword boundary (the extent rounded up to a dword),
+  // so no dword that holds part of an element is dropped and nothing past
+  // the operand's last dword is read.
+  __device__ __forceinline__ void load_staged(u32x4 (&v)[LOADS],
+                                              unsigned (&e)[LOADS],
+                                              unsigned (&sh)[LOADS], int t, int w,
+                                              int lane) const {
+    // The resource starts at the dword holding the slice's first byte, so
+    // every dword-aligned offset below a piece's start is still >= 0.
+    const char* b0 = slice_base(t);
+    const int bshift = (int)((uintptr_t)b0 & 3);  // 0 or 2
+    const char* b = b0 - bshift;
+    const auto rs = make_rsrc_n(b, nrec_from(X, ext, b));
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      int rr, cc, start, lim;
+      piece(w, i, lane, rr, cc);
+      const int off = piece_off(t, rr, cc, start, lim);
+      // the piece's byte offset from the aligned base, and its position
+      // within its first dword
+      const int rel = off == kOutOfRange ? 0 : off + bshift;
+      sh[i] = (unsigned)(rel & 3);
+      const int aoff = off == kOutOfRange ? kOutOfRange : rel - (rel & 3);
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, aoff, 0, 0);
+      e[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, aoff == kOutOfRange ? kOutOfRange : aoff + 16,
+                                                  0, 0);
+    }
+  }
+
+  // Shift each piece into place (the dwords were read from the dword at or
+  // below its start), zero the elements past the edge of the contiguous
+  // dimension (pieces that straddle it), then write the pieces where a
+  // direct load would have.
+  __device__ __forceinline__ void store_staged(char* slot, const u32x4 (&v)[LOADS],
+                                               const unsigned (&e)[LOADS],
+                                               const unsigned (&sh)[LOADS], int t,
+                                               int w, int lane, bool edge) const {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      u32x4 x;
+      x[0] = __builtin_amdgcn_alignbyte(v[i][1], v[i][0], sh[i]);
+      x[1] = __builtin_amdgcn_alignbyte(v[i][2], v[i][1], sh[i]);
+      x[2] = __builtin_amdgcn_alignbyte(v[i][3], v[i][2], sh[i]);
+      x[3] = __builtin_amdgcn_alignbyte(e[i], v[i][3], sh[i]);
+      if (edge) {
+        int rr, cc, start, lim;
+        piece(w, i, lane, rr, cc);
+        (void)piece_off(t, rr, cc, start, lim);
+        x = keep_first(x, lim - start < 8 ? (lim - start > 0 ? lim - start : 0) : 8);
+      }
+      *reinterpret_cast<u32x4*>(slot + (4 * w + i) * 1024 + lane * 16) = x;
+    }
+  }
+
+  __device__ __forceinline__ u32x4 read(const char* slot, int t, int ks) const {
+    if constexpr (!MN) {
+      return *reinterpret_cast<const u32x4*>(slot + (off[t] ^ (ks << 5)));
+    } else {
+      typedef __attribute__((address_space(3))) pp_i16x4 lds_i16x4;
+      const char* q = slot + off[t] + ks * 16 * RB;
+      const pp_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q));
+      const pp_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * RB));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{l2.x, l2.y, h2.x, h2.y};
+    }
+  }
+};
+
+// The epilogue of one atom row of a wave's 64x64 block (after the K groups'
+// exchange each group finishes one of the two rows).
+template <class C>
+struct RingRow : C {
+  static constexpr int TM = 1;
+};
+
+// KG K groups of 4 waves each: group g multiplies the tile's slices g, g+KG,
+// g+2KG, ... with a ring of its own; with KG = 2 a tile takes 160 KiB of LDS
+// and 8 waves, so grids of about one tile per CU still give every SIMD two
+// independent waves. The groups' accumulators are summed in group order.
+// ROWS: tile side (128: 64x64 per wave, two workgroups per CU with KG = 1).
+// STAGING: operands staged through registers are supported (otherwise both
+// must be direct).
+template <int ROWS, class Tag, int EPI, bool AMN, bool BMN, int KG, bool STAGING>
+__global__ void __launch_bounds__(RingCfg<ROWS>::THREADS * KG, RingCfg<ROWS>::MIN_WG / KG)
+gemm_ring_kernel(const GemmArgs p) {
+  using C = RingCfg<ROWS>;
+  using At = typename C::At;
+  using acc_t = typename At::acc_t;
+  __shared__ __attribute__((aligned(1024))) char lds[KG * C::LDS_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2;  // K group
+  const int w = wave & 3;     // wave within its group
+  const int wm = w >> 1, wn = w & 1;
+  char* const smem = lds + grp * C::LDS_BYTES;
+  int tm, tn;
+  schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+
+  RingOperand<AMN, ROWS> a;
+  RingOperand<BMN, ROWS> b;
+  a.init(p.A, p.lda, m0, p.M, p.K, wm, lane);
+  b.init(p.B, p.ldb, n0, p.N, p.K, wn, lane);
+  // Staging modes (uniform over the launch) and, for staged operands, whether
+  // this tile's pieces can straddle the edge of the contiguous dimension.
+  const bool a_dir = !STAGING || p.a_direct, b_dir = !STAGING || p.b_direct;
+  const bool a_edge = AMN ? (m0 + C::BM > p.M && p.M % 8 != 0) : (p.K % 8 != 0);
+  const bool b_edge = BMN ? (n0 + C::BN > p.N && p.N % 8 != 0) : (p.K % 8 != 0);
+  const bool staged = !a_dir || !b_dir;
+  // Atoms of this wave that hold outputs inside M x N (uniform per wave): on
+  // edge tiles the others are neither read nor multiplied.
+  auto nvalid = [](int lo, int lim, int n) {
+    const int v = (lim - lo + 31) / 32;
+    return v < 0 ? 0 : (v > n ? n : v);
+  };
+  const int nvi = nvalid(m0 + wm * C::WTM, p.M, C::TM);
+  const int nvj = nvalid(n0 + wn * C::WTN, p.N, C::TN);
+  const bool full_wave = nvi == C::TM && nvj == C::TN;
+
+  acc_t acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < At::NACC; ++v) acc[i][j][v] = 0.0f;
+
+  // This group's slices: local index j is the tile's slice j*KG + grp.
+  const int KT = (p.K + C::BK - 1) / C::BK;
+  const int JT = (KT + KG - 1) / KG;                  // iterations (all groups)
+  const int NJ = KT > grp ? (KT - grp + KG - 1) / KG : 0;  // this group's slices
+  auto gs = [&](int j) { return j * KG + grp; };
+  auto slot = [&](int h) { return smem + (h % C::SLOTS) * C::HALF_BYTES; };
+  // Staged operands: the covering dwords of each piece and its byte shift.
+  u32x4 va[C::LOADS], vb[C::LOADS];
+  unsigned ea[C::LOADS], eb[C::LOADS], sa_[C::LOADS], sb_[C::LOADS];
+
+  // With two K groups each group finishes one atom row of its waves' blocks
+  // (row grp). On interior tiles that read C it requests those C values
+  // right after the prologue's loads, so they arrive while the K loop runs
+  // instead of after it (32 registers per lane).
+  constexpr bool PRE_C = KG == 2 && EPI != EPI_BETA0;
+  const bool inner = m0 + C::BM <= p.M && n0 + C::BN <= p.N;
+  const bool pre_c = PRE_C && p.wide_epi && inner;
+  WideC<RingRow<C>> cpre;
+
+  // Prologue: local slice 0 into slots 0 and 1, then A of local slice 1
+  // (direct) into slot 2, or local slice 1 (staged) into registers.
+  if (NJ > 0) {
+    if (a_dir) a.issue_direct(slot(0), gs(0), w, lane);
+    else a.load_staged(va, ea, sa_, gs(0), w, lane);
+    if (b_dir) b.issue_direct(slot(1), gs(0), w, lane);
+    else b.load_staged(vb, eb, sb_, gs(0), w, lane);
+    if (a_dir && NJ > 1) a.issue_direct(slot(2), gs(1), w, lane);
+  }
+  if constexpr (PRE_C) {
+    if (pre_c)
+      load_wide_c<RingRow<C>>(cpre, p, m0 + wm * C::WTM + grp * At::M, n0 + wn * C::WTN, lane);
+  }
+  constexpr int NC = PRE_C ? C::TN * At::NACC / 4 : 0;  // C loads per lane
+  if (NJ > 0) {
+    if (staged) {
+      pp_wait_vm<0>();
+      if (!a_dir) a.store_staged(slot(0), va, ea, sa_, gs(0), w, lane, a_edge);
+      if (!b_dir) b.store_staged(slot(1), vb, eb, sb_, gs(0), w, lane, b_edge);
+      if (NJ > 1) {
+        if (!a_dir) a.load_staged(va, ea, sa_, gs(1), w, lane);
+        if (!b_dir) b.load_staged(vb, eb, sb_, gs(1), w, lane);
+      }
+      pp_wait_lgkm0();
+    } else if (NJ > 1) {
+      // A of local slice 1 (and the C requests) may stay in flight
+      if (pre_c) pp_wait_vm_lgkm0<C::LOADS + NC>();
+      else pp_wait_vm_lgkm0<C::LOADS>();
+    } else {
+      if (pre_c) pp_wait_vm_lgkm0<NC>();
+      else pp_wait_vm_lgkm0<0>();
+    }
+  }
+  pp_barrier();
+
+  for (int j = 0; j < JT; ++j) {
+    if (j < NJ) {
+      // Staged operands: local slice j+1 arrived in registers during the
+      // previous iteration (this waits for every older load); write it into
+      // its slots (A: 2j+2, left by B of j-2; B: 2j+3, left by A of j-1),
+      // then request local slice j+2 into the same registers.
+      if (staged && j + 1 < NJ) {
+        pp_wait_vm<0>();
+        if (!a_dir) a.store_staged(slot(2 * j + 2), va, ea, sa_, gs(j + 1), w, lane, a_edge);
+        if (!b_dir) b.store_staged(slot(2 * j + 3), vb, eb, sb_, gs(j + 1), w, lane, b_edge);
+      }
+      // Direct loads into the slots local slice j-1 has left: B of j+1
+      // first, then A of j+2 (slot 2j+4, left by B of j-1).
+      if (b_dir && j + 1 < NJ) b.issue_direct(slot(2 * j + 3), gs(j + 1), w, lane);
+      if (a_dir && j + 2 < NJ) a.issue_direct(slot(2 * j + 4), gs(j + 2), w, lane);
+      if (staged && j + 2 < NJ) {
+        if (!a_dir) a.load_staged(va, ea, sa_, gs(j + 2), w, lane);
+        if (!b_dir) b.load_staged(vb, eb, sb_, gs(j + 2), w, lane);
+      }
+
+      // Multiply local slice j (edge waves: only their atoms that hold
+      // outputs inside M x N; the branch is uniform per wave).
+      const char* sa = slot(2 * j);
+      const char* sb = slot(2 * j + 1);
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks) {
+        u32x4 fa[C::TM], fb[C::TN];
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) fa[i] = a.read(sa, i, ks);
+#pragma unroll
+        for (int jj = 0; jj < C::TN; ++jj) fb[jj] = b.read(sb, jj, ks);
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < C::TN; ++jj)
+            if (full_wave || (i < nvi && jj < nvj))
+              acc[i][jj] = At::mma(Tag{}, fa[i], fb[jj], acc[i][jj]);
+      }
+
+      // Local slice j+1 must be in LDS by the next barrier. A direct B of
+      // j+1 was issued first in this iteration, so at most the one
+      // half-slice request that followed it (A of j+2: 4 direct loads or 8
+      // staged ones) may stay in flight; a direct A of j+1 is older still.
+      // Without a direct B, the staged wait at the top of this iteration
+      // already covered every older load. LDS reads and staged writes must
+      // be complete.
+      if (b_dir) {
+        if (j + 2 < NJ && a_dir) pp_wait_vm_lgkm0<C::LOADS>();
+        else if (j + 2 < NJ) pp_wait_vm_lgkm0<2 * C::LOADS>();  // staged: two loads per piece
+        else pp_wait_vm_lgkm0<0>();
+      } else {
+        pp_wait_lgkm0();
+      }
+    }
+    pp_barrier();
+  }
+
+  if constexpr (KG == 1) {
+    if (inner) store_tile<C, EPI, false>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane);
+    else store_tile<C, EPI, true>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane);
+  } else {
+    static_assert(KG == 2 && C::TM == 2, "two K groups, each finishing one atom row");
+    // Group g hands atom row 1-g to the other group through LDS (every
+    // group is past its last read of the ring: the loop ended on a
+    // barrier), then finishes atom row g as (group 0's sum) + (group 1's).
+    constexpr int NV = C::TN * At::NACC;  // registers of one atom row
+    float* x = reinterpret_cast<float*>(lds);
+    {
+      float* dst = x + (grp * 4 + w) * NV * 64 + lane;
+#pragma unroll
+      for (int jj = 0; jj < C::TN; ++jj)
+#pragma unroll
+        for (int v = 0; v < At::NACC; ++v)  // (a select: no dynamic index into registers)
+          dst[(jj * At::NACC + v) * 64] = grp == 0 ? acc[1][jj][v] : acc[0][jj][v];
+    }
+    pp_wait_lgkm0();
+    pp_barrier();
+    acc_t fin[1][C::TN];
+    {
+      const float* src = x + ((1 - grp) * 4 + w) * NV * 64 + lane;
+#pragma unroll
+      for (int jj = 0; jj < C::TN; ++jj)
+#pragma unroll
+        for (int v = 0; v < At::NACC; ++v) {
+          const float other = src[(jj * At::NACC + v) * 64];
+          fin[0][jj][v] = grp == 0 ? acc[0][jj][v] + other : other + acc[1][jj][v];
+        }
+    }
+    const int r0 = m0 + wm * C::WTM + grp * At::M;
+    if (inner) store_tile<RingRow<C>, EPI, false>(fin, p, r0, n0 + wn * C::WTN, lane, cpre, pre_c);
+    else store_tile<RingRow<C>, EPI, true>(fin, p, r0, n0 + wn * C::WTN, lane);
+  }
+}
+
+}  // namespace dgt

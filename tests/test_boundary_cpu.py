@@ -113,13 +113,28 @@ def test_empty_and_degenerate_calls(lib):
 
 
 def test_unaligned_pitch_stays_on_mfma_with_narrow_staging(lib):
-    # transposed f16 A with lda = 4097: an 8194-byte row pitch
+    # transposed f16 A with lda = 4097: an 8194-byte row pitch. 128x128 tiles
+    # run on the ring kernel, which stages A through registers.
     st = _v(lib, M=4097, N=1000, K=1032, tA=1, lda=4097, alpha=2.0, beta=-1.0)
     assert st == lib.GEMM_OK
     path = lib.gemm_last_path()
-    assert path.startswith("mfma t128x128x64") and " masked " in path, path
-    assert path.endswith(
-        "narrow staging (A: 2-byte loads, row pitch 8194 B is not a multiple of 16 B)"), path
+    # (264 tiles: two workgroups per CU where needed)
+    assert path == ("mfma t128x128x64 w2x2 a32x32x16 TN epi=general ring masked staged "
+                    "(A: row pitch 8194 B is not a multiple of 16 B)"), path
+    # same shape with a 16-byte pitch: A is still staged (M = 4097 cuts its
+    # contiguous dimension off a multiple of 8), B is loaded straight into LDS
+    assert _v(lib, M=4097, N=1000, K=1032, tA=1, lda=4104) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" ring masked staged (A: M % 8 != 0)")
+    # (256 tiles, at most one per CU: the deep ring when both operands go
+    # straight into LDS, else K split over two wave groups)
+    assert _v(lib, M=4096, N=1000, K=1032, tA=1, lda=4104) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" TN epi=beta0 ring deep masked"), lib.gemm_last_path()
+    assert _v(lib, M=4096, N=1024, K=1028, tA=0, lda=1032) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" ring ksplit2 masked staged (A: K % 8 != 0)")
+    assert _v(lib, M=4096, N=1000, K=1024, tA=0, tB=0, ldb=1000) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" NN epi=beta0 ring deep masked"), lib.gemm_last_path()
+    assert _v(lib, M=4096, N=1004, K=1024, tA=0, tB=0, ldb=1008) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" ring ksplit2 masked staged (B: N % 8 != 0)")
     assert _v(lib, A=A0 + 2) == lib.GEMM_OK
     path = lib.gemm_last_path()
     assert path.startswith("mfma ") and "A: 2-byte loads, base address is not 16-byte aligned" in path
@@ -136,15 +151,43 @@ def test_unaligned_pitch_stays_on_mfma_with_narrow_staging(lib):
     assert _v(lib, lda=67, ldb=67, M=64, N=64, K=64) == lib.GEMM_OK
     assert ("(A: 2-byte loads, row pitch 134 B is not a multiple of 16 B; "
             "B: 2-byte loads, row pitch 134 B") in lib.gemm_last_path()
-    # whole tiles with an unaligned operand still take the masked kernel
+    # whole 256x256 tiles with an unaligned operand: 128x128 tiles on the ring
+    # kernel, B staged through registers
     assert _v(lib, M=8192, N=8192, K=8192, tB=1, dtype=1, ldb=8193) == lib.GEMM_OK
-    assert " masked narrow staging (B: 2-byte" in lib.gemm_last_path(), lib.gemm_last_path()
+    assert lib.gemm_last_path() == ("mfma t128x128x64 w2x2 a32x32x16 NT epi=beta0 ring staged "
+                                    "(B: row pitch 16386 B is not a multiple of 16 B)"), \
+        lib.gemm_last_path()
+
+
+def test_ring_modes(lib, monkeypatch):
+    # at most one 128x128 tile per CU: the deep ring (both operands direct)
+    assert _v(lib, M=2048, N=2048, K=2048, dtype=1) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "mfma t128x128x64 w2x2 a32x32x16 NN epi=beta0 ring deep"
+    # ... or two K groups when an operand is staged through registers
+    assert _v(lib, M=2048, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith(
+        "mfma t128x128x64 w2x2 a32x32x16 NN epi=beta0 ring ksplit2 staged (A: row pitch")
+    # more tiles than CUs: one group, two workgroups per CU
+    assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "mfma t128x128x64 w2x2 a32x32x16 NN epi=beta0 ring"
+    monkeypatch.setenv("GEMM_RING_MODE", "shared")
+    assert _v(lib, M=2048, N=2048, K=2048, dtype=1) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" ring")
+    monkeypatch.setenv("GEMM_RING_MODE", "ksplit2")
+    assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" ring ksplit2")
+    monkeypatch.setenv("GEMM_RING_MODE", "deep")
+    assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" ring deep")
+    assert _v(lib, M=2048, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_ERR_UNSUPPORTED
+    monkeypatch.setenv("GEMM_RING_MODE", "wide")
+    assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_ERR_INVALID_ARG
 
 
 def test_ragged_dims_stay_on_mfma_masked(lib):
     assert _v(lib, M=4097, N=1000, K=1032, tA=1, lda=4104) == lib.GEMM_OK
     path = lib.gemm_last_path()
-    assert path.startswith("mfma ") and path.endswith("masked"), path
+    assert path.startswith("mfma ") and " masked" in path, path
     assert _v(lib, M=16, N=8, K=16) == lib.GEMM_OK
     assert lib.gemm_last_path().startswith("mfma t16x16x64"), lib.gemm_last_path()
 

@@ -1,0 +1,140 @@
+"""GPU parity of the 128x128 direct-to-LDS ring kernel against the oracle.
+
+The kernel stages each operand either straight into LDS or through
+registers, for both stored orientations, with edge tiles, K tails and a ring
+of five half-slots whose schedule changes with the number of 64-deep K
+slices (one slice: prologue only; two: no third slice requested; more: the
+ring turns). Every combination is checked elementwise against the oracle,
+and the exact cases (permutation and integer inputs) bitwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_helpers import need_gpu, run
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu(monkeypatch):
+    need_gpu()
+    monkeypatch.delenv("GEMM_FORCE_PATH", raising=False)
+    monkeypatch.setenv("GEMM_FORCE_TILE", "t128x128x64")
+
+
+def _ld(cols, aligned):
+    """Leading dimension for a row of `cols` 16-bit values: padded to a 16-byte
+    pitch, or one element past it (2-byte pitch: staged through registers)."""
+    p = (cols + 7) // 8 * 8
+    return p if aligned else p + 1
+
+
+LAYOUTS = [(0, 1), (0, 0), (1, 1), (1, 0)]
+# (A direct-capable pitch, B direct-capable pitch)
+MODES = [(True, True), (False, True), (True, False), (False, False)]
+
+
+@pytest.mark.parametrize("kg", ["shared", "ksplit2", "deep"])
+@pytest.mark.parametrize("tA,tB", LAYOUTS)
+@pytest.mark.parametrize("mode", MODES)
+def test_ring_layouts_modes_and_slice_counts(tA, tB, mode, kg, monkeypatch):
+    """K from one slice of 64 (prologue only; with two K groups the second
+    group then has no slice at all) through two and three slices to several
+    turns of the ring, K tails that cut a 16-byte piece (K % 8 != 0) and ones
+    that do not; whole tiles and edge tiles on both M and N; one K group per
+    workgroup and two; the deep ring (ten half-slots, four slices ahead, both
+    operands loaded straight into LDS)."""
+    monkeypatch.setenv("GEMM_RING_MODE", kg)
+    a_al, b_al = mode
+    if kg == "deep" and mode != (True, True):
+        pytest.skip("the deep ring loads both operands straight into LDS")
+    seed = 7000 + 97 * LAYOUTS.index((tA, tB)) + 13 * MODES.index(mode) + 1000 * len(kg)
+    cases = [(256, 384, 64), (256, 128, 128), (384, 256, 192), (128, 128, 320),
+             (300, 260, 72), (136, 200, 1000), (264, 136, 1032), (129, 127, 17)]
+    for (M, N, K) in cases:
+        for alpha, beta in [(1.0, 0.0), (1.0, 1.0), (-1.5, 0.5)]:
+            seed += 1
+            lda = _ld(M if tA else K, a_al)
+            ldb = _ld(K if tB else N, b_al)
+            if kg == "deep" and ((M % 8 and tA) or (N % 8 and not tB) or K % 8):
+                continue  # an edge cuts a 16-byte piece: staged, not the deep ring
+            cfg = workloads.Config(f"ring{seed}", M, N, K, "bf16" if seed % 2 else "f16", tA, tB,
+                                   alpha, beta, "uniform", seed, lda=lda, ldb=ldb,
+                                   ldc=N + 3, ldd=N + 3)
+            r = run(cfg)
+            assert " ring" in r.path and (" ring deep" in r.path) == (kg == "deep") \
+                and (" ring ksplit2" in r.path) == (kg == "ksplit2"), r.path
+            r.check()
+            r.check_padding_untouched()
+
+
+@pytest.mark.parametrize("kg", ["shared", "ksplit2", "deep"])
+@pytest.mark.parametrize("tA,tB", LAYOUTS)
+@pytest.mark.parametrize("aligned", [True, False])
+def test_ring_permutations_pin_layouts_bitwise(tA, tB, aligned, kg, monkeypatch):
+    """P @ X and X @ Q move every element to a known place exactly: a wrong
+    swizzle, fragment lane or slot in either staging mode, or a wrong row in
+    the K groups' exchange, shows up."""
+    if kg == "deep" and not aligned:
+        pytest.skip("the deep ring loads both operands straight into LDS")
+    monkeypatch.setenv("GEMM_RING_MODE", kg)
+    rng = np.random.default_rng(300 + 2 * tA + tB + (8 if aligned else 0))
+    M, N, K = 256, 256, 256
+    X = torch.tensor(rng.uniform(-1, 1, (M, N)).astype(np.float32)).bfloat16().float().numpy()
+    P = np.eye(M, dtype=np.float32)[rng.permutation(M)]
+    Q = np.eye(N, dtype=np.float32)[:, rng.permutation(N)]
+    for A, B in [(P, X), (X, Q)]:
+        As = A.T if tA else A
+        Bs = B.T if tB else B
+        lda, ldb = _ld(As.shape[1], aligned), _ld(Bs.shape[1], aligned)
+        Ap = np.zeros((As.shape[0], lda), np.float32)
+        Ap[:, :As.shape[1]] = As
+        Bp = np.zeros((Bs.shape[0], ldb), np.float32)
+        Bp[:, :Bs.shape[1]] = Bs
+        cfg = workloads.Config("ringperm", M, N, K, "bf16", tA, tB, 1.0, 0.0, "uniform", 1,
+                               lda=lda, ldb=ldb)
+        inp = workloads.make_inputs(cfg, A_src=torch.tensor(Ap), B_src=torch.tensor(Bp))
+        r = run(cfg, inp)
+        assert " ring" in r.path and (("staged" in r.path) != aligned), r.path
+        assert np.array_equal(r.D[:, :N].numpy(), (A @ B).astype(np.float32))
+
+
+@pytest.mark.parametrize("kg", ["shared", "ksplit2"])
+def test_ring_integer_inputs_with_ragged_edges_bitwise(kg, monkeypatch):
+    """Integer-valued operands: every partial sum is exact, so D must equal
+    the exact product bitwise, here on the ragged shape of the transposed-A
+    workload (M = 4097 cuts a 16-byte piece of A's rows; K = 1032)."""
+    monkeypatch.setenv("GEMM_RING_MODE", kg)
+    rng = np.random.default_rng(5)
+    M, N, K = 4097, 1000, 1032
+    A = rng.integers(-2, 3, (M, K)).astype(np.float32)
+    B = rng.integers(-2, 3, (K, N)).astype(np.float32)
+    cfg = workloads.Config("ringint", M, N, K, "f16", 1, 0, 1.0, 0.0, "uniform", 1, lda=M)
+    inp = workloads.make_inputs(cfg, A_src=torch.tensor(np.ascontiguousarray(A.T)),
+                                B_src=torch.tensor(B))
+    r = run(cfg, inp)
+    assert " masked staged (A:" in r.path and " ring" in r.path, r.path
+    assert np.array_equal(r.D[:, :N].numpy(), (A @ B).astype(np.float32))
+
+
+@pytest.mark.parametrize("tA,tB", LAYOUTS)
+def test_ring_edge_waves_and_inplace(tA, tB, monkeypatch):
+    """Edge tiles whose waves hold no or few valid atoms (one row past a
+    multiple of 128, a column edge inside a wave's block), C == D, an
+    unaligned operand; D untouched outside M x N."""
+    seed = 9100 + 10 * LAYOUTS.index((tA, tB))
+    for (M, N, K, inplace, pad) in [(4097, 1000, 1032, False, 1), (1000, 4097, 520, True, 0),
+                                    (129, 1000, 256, False, 0), (1024, 4100, 200, False, 3)]:
+        seed += 1
+        lda = (M if tA else K) + pad
+        ldb = (K if tB else N) + (8 if seed % 2 else 0)
+        ld = N + (0 if inplace else 2)
+        cfg = workloads.Config(f"edge{seed}", M, N, K, "f16" if seed % 2 else "bf16", tA, tB,
+                               1.5, -0.5 if not inplace else 1.0, "uniform", seed, lda=lda,
+                               ldb=ldb, ldc=ld, ldd=ld, inplace=inplace)
+        r = run(cfg)
+        assert " ring" in r.path, r.path
+        r.check()
+        r.check_padding_untouched()
