@@ -12,6 +12,7 @@ max relative error on sampled rows, and the CPU oracle timed on a bounded
 sample of the same workload on this host's cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--shape M,N,K,dtype,tA,tB[,alpha,beta]]
                   [--no-cpu-baseline] [--cpu-seconds S]
   python bench.py --copy-calibration   # plain copy of known size (counter scale)
 """
@@ -37,19 +38,22 @@ DIST_TEXT = {"uniform": "uniform[-1, 1]", "normal": "normal(0, 1)",
              "normal_invsqrtk": "normal(0, 1/sqrt(K))"}
 
 
-def kernel_sources_digest() -> str:
-    """Digest of the kernel sources, to tell whether stored counters are stale."""
+def kernel_sources_digest(files) -> str:
+    """Digest of a kernel's source files (paths relative to the package's
+    csrc/), to tell whether counters stored for that kernel are stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_gemm_tile_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(files):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
 def stored_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, or None if the
-    summary is missing or was taken on different kernel sources."""
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed counter summary, or None if the summary is missing or was taken
+    on different sources of that kernel (the summary names its source files
+    and their digest)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -59,12 +63,79 @@ def stored_traffic(workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_sources_digest") != kernel_sources_digest():
-        return None
+    files = vals.get("kernel_source_files", "").split()
     try:
+        if not files or vals.get("kernel_sources_digest") != kernel_sources_digest(files):
+            return None
         return float(vals["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
+    except (KeyError, ValueError, OSError):
         return None
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock (the level the amdgpu driver's
+    pp_dpm_sclk marks current) and board power (hwmon power1_input) every
+    ~2 ms on a host thread while the timed steps run."""
+
+    def __init__(self):
+        import glob
+        import threading
+        self.sclk = next(iter(sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))), None)
+        dev = os.path.dirname(self.sclk) if self.sclk else None
+        hw = sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))) if dev else []
+        self.power = os.path.join(hw[0], "power1_input") if hw else None
+        self.cap = os.path.join(hw[0], "power1_cap") if hw else None
+        self.mhz, self.watts = [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read_mhz(self):
+        # One line per clock level ("1: 2400Mhz"); the current one is marked
+        # with "*" (an "S:" line when the chip is in a sleep state).
+        with open(self.sclk) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return float(line.split()[1].lower().replace("mhz", ""))
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                if self.sclk:
+                    m = self._read_mhz()
+                    if m:
+                        self.mhz.append(m)
+                if self.power:
+                    with open(self.power) as f:
+                        self.watts.append(float(f.read()) / 1e6)
+            except (OSError, ValueError):
+                pass
+            time.sleep(0.002)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self):
+        if not self.mhz:
+            return None
+        out = {"sclk_mhz_mean": round(sum(self.mhz) / len(self.mhz), 1),
+               "sclk_mhz_min": min(self.mhz), "sclk_mhz_max": max(self.mhz),
+               "samples": len(self.mhz),
+               "source": "amdgpu pp_dpm_sclk current level, sampled every ~2 ms during the "
+                         "timed steps"}
+        if self.watts:
+            out["power_w_mean"] = round(sum(self.watts) / len(self.watts), 1)
+        try:
+            with open(self.cap) as f:
+                out["power_cap_w"] = float(f.read()) / 1e6
+        except (OSError, TypeError, ValueError):
+            pass
+        return out
 
 
 def blas_threads() -> int:
@@ -284,6 +355,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gemm8192_nt")
+    ap.add_argument("--shape", default=None,
+                    help="an ad-hoc workload instead: M,N,K,dtype,transA,transB[,alpha,beta] "
+                         "(normal(0,1) inputs, seed 7; for tile-choice measurements)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-check", action="store_true")
@@ -314,7 +388,14 @@ def main():
     import dense_gemm_tile_amd as dgt
     import workloads
 
-    cfg = {**workloads.CONFIGS, **workloads.EXTRA_CONFIGS}[args.workload]
+    if args.shape:
+        f = args.shape.split(",")
+        alpha, beta = (float(f[6]), float(f[7])) if len(f) >= 8 else (1.0, 0.0)
+        cfg = workloads.Config(f"shape{f[0]}x{f[1]}x{f[2]}_{f[3]}_{f[4]}{f[5]}", int(f[0]),
+                               int(f[1]), int(f[2]), f[3], int(f[4]), int(f[5]), alpha, beta,
+                               "normal", 7)
+    else:
+        cfg = {**workloads.CONFIGS, **workloads.EXTRA_CONFIGS}[args.workload]
     lda, ldb, ldc, ldd = cfg.lds()
     inp = workloads.make_inputs(cfg)
     dev = torch.device("cuda:0")
@@ -337,18 +418,22 @@ def main():
     torch.cuda.synchronize()
     path = dgt.gemm_last_path()
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # The timed steps, back to back, with a HIP event on the launch stream
+    # before the first and after every step (events do not serialise the
+    # stream): whole-region time and each step's own time.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    gpu_ms = ev0.elapsed_time(ev1)
+    with ClockSampler() as clock:
+        w0 = time.perf_counter()
+        evs[0].record(stream)
+        for i in range(args.steps):
+            step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+    gpu_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = gpu_ms / args.steps
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
 
     n_per_call = args.per_call
     if n_per_call is None:
@@ -417,6 +502,9 @@ def main():
         "oracle_max_rel_err": max_rel,
         "path": path,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "step_ms": {"median": round(step_ms[len(step_ms) // 2], 5), "min": round(step_ms[0], 5),
+                    "max": round(step_ms[-1], 5)},
+        "clock": clock.summary(),
         "roofline": roofline,
     }
     if per_call is not None:
