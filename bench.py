@@ -12,9 +12,11 @@ max relative error on sampled rows, and the CPU oracle timed on a bounded
 sample of the same workload on this host's cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--shape M,N,K,dtype,tA,tB[,alpha,beta]]
+                  [--shape M,N,K,dtype,tA,tB[,alpha,beta[,lda[,ldb]]]]
                   [--no-cpu-baseline] [--cpu-seconds S]
   python bench.py --copy-calibration   # plain copy of known size (counter scale)
+  python bench.py --library-context    # the same workload on PyTorch's own GEMM
+                                       # (hipBLASLt on ROCm): context, not a result
 """
 from __future__ import annotations
 
@@ -73,69 +75,136 @@ def stored_traffic(workload: str):
 
 
 class ClockSampler:
-    """Samples the GPU's current shader clock (the level the amdgpu driver's
-    pp_dpm_sclk marks current) and board power (hwmon power1_input) every
-    ~2 ms on a host thread while the timed steps run."""
+    """Samples the GPU's shader clock and socket power on a host thread.
 
-    def __init__(self):
+    Source: the amdgpu metrics table through amdsmi (current gfx clock of each
+    XCD, socket power), else the driver's pp_dpm_sclk current level and hwmon
+    power1_input. The firmware refreshes these about once a second, so a
+    reading describes the second before it: only a sustained run of a second
+    or more gives a figure that belongs to the kernel."""
+
+    def __init__(self, period_s: float = 0.02):
         import glob
         import threading
+        self.period = period_s
+        self.samples = []  # (t, mean MHz over XCDs, per-XCD MHz or None, W or None)
+        self.source = None
+        self._smi = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = (amdsmi, amdsmi.amdsmi_get_processor_handles()[0])
+            self.source = "amdsmi gpu metrics (current_gfxclks per XCD, current_socket_power)"
+        except Exception:  # amdsmi missing or no device: the sysfs files below
+            self._smi = None
         self.sclk = next(iter(sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))), None)
         dev = os.path.dirname(self.sclk) if self.sclk else None
         hw = sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))) if dev else []
         self.power = os.path.join(hw[0], "power1_input") if hw else None
         self.cap = os.path.join(hw[0], "power1_cap") if hw else None
-        self.mhz, self.watts = [], []
+        if self._smi is None and self.sclk:
+            self.source = "amdgpu pp_dpm_sclk current level, hwmon power1_input"
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
+        self.t0 = None
 
-    def _read_mhz(self):
-        # One line per clock level ("1: 2400Mhz"); the current one is marked
-        # with "*" (an "S:" line when the chip is in a sleep state).
+    def _read_sysfs(self):
+        mhz = w = None
+        # One line per clock level ("1: 2400Mhz"); the current one ends in "*".
         with open(self.sclk) as f:
             for line in f:
                 if line.rstrip().endswith("*"):
-                    return float(line.split()[1].lower().replace("mhz", ""))
-        return None
+                    mhz = float(line.split()[1].lower().replace("mhz", ""))
+        if self.power:
+            with open(self.power) as f:
+                w = float(f.read()) / 1e6
+        return mhz, None, w
+
+    def _read_smi(self):
+        amdsmi, h = self._smi
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        per = [float(v) for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float))
+               and 0 < v < 10000]
+        if not per and isinstance(m.get("current_gfxclk"), (int, float)):
+            per = [float(m["current_gfxclk"])]
+        w = m.get("current_socket_power")
+        w = float(w) if isinstance(w, (int, float)) else None
+        return (sum(per) / len(per) if per else None), (per or None), w
 
     def _run(self):
         while not self._stop.is_set():
             try:
-                if self.sclk:
-                    m = self._read_mhz()
-                    if m:
-                        self.mhz.append(m)
-                if self.power:
-                    with open(self.power) as f:
-                        self.watts.append(float(f.read()) / 1e6)
-            except (OSError, ValueError):
+                mhz, per, w = self._read_smi() if self._smi else self._read_sysfs()
+                if mhz:
+                    self.samples.append((time.perf_counter() - self.t0, mhz, per, w))
+            except Exception:  # a sensor read that fails is skipped
                 pass
-            time.sleep(0.002)
+            time.sleep(self.period)
 
     def __enter__(self):
-        self._thread.start()
+        self.t0 = time.perf_counter()
+        if self._smi or self.sclk:
+            self._thread.start()
         return self
 
     def __exit__(self, *exc):
         self._stop.set()
-        self._thread.join()
+        if self._thread.is_alive():
+            self._thread.join()
 
-    def summary(self):
-        if not self.mhz:
+    def summary(self, after_s: float = 0.0):
+        ss = [x for x in self.samples if x[0] >= after_s]
+        if not ss:
             return None
-        out = {"sclk_mhz_mean": round(sum(self.mhz) / len(self.mhz), 1),
-               "sclk_mhz_min": min(self.mhz), "sclk_mhz_max": max(self.mhz),
-               "samples": len(self.mhz),
-               "source": "amdgpu pp_dpm_sclk current level, sampled every ~2 ms during the "
-                         "timed steps"}
-        if self.watts:
-            out["power_w_mean"] = round(sum(self.watts) / len(self.watts), 1)
+        mhz = [x[1] for x in ss]
+        out = {"sclk_mhz_mean": round(sum(mhz) / len(mhz), 1), "sclk_mhz_min": min(mhz),
+               "sclk_mhz_max": max(mhz), "samples": len(ss), "source": self.source}
+        per = [x[2] for x in ss if x[2]]
+        if per and all(len(p) == len(per[0]) for p in per):
+            out["sclk_mhz_per_xcd_mean"] = [round(sum(p[i] for p in per) / len(per), 1)
+                                            for i in range(len(per[0]))]
+        w = [x[3] for x in ss if x[3] is not None]
+        if w:
+            out["power_w_mean"] = round(sum(w) / len(w), 1)
         try:
             with open(self.cap) as f:
                 out["power_cap_w"] = float(f.read()) / 1e6
         except (OSError, TypeError, ValueError):
             pass
         return out
+
+
+def sustained_clock(step, stream, ms_per_step: float, seconds: float, settle_s: float = 1.0):
+    """Runs `step` back to back for `seconds` (untimed for the result; the
+    same call as the timed steps) and returns the clock and power sampled
+    after the first `settle_s` seconds, with the mean time per step over that
+    part (HIP events on the launch stream)."""
+    import torch
+    chunk = max(1, int(20.0 / max(ms_per_step, 1e-3)))  # ~20 ms between host syncs
+    e0 = e1 = None
+    n = 0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            if e0 is None and time.perf_counter() - t0 >= settle_s:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                n = 0
+            for _ in range(chunk):
+                step()
+            n += chunk
+            torch.cuda.synchronize()
+        if e0 is not None:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record(stream)
+            torch.cuda.synchronize()
+    out = clk.summary(after_s=settle_s) or {}
+    out["window_s"] = seconds
+    out["settle_s"] = settle_s
+    if e0 is not None and n:
+        out["ms_per_step"] = round(e0.elapsed_time(e1) / n, 5)
+        out["steps"] = n
+    return out
 
 
 def blas_threads() -> int:
@@ -349,6 +418,64 @@ def per_call_timing(step, stream, n):
     return {"samples": n, "hot": hot, "cold": cold}
 
 
+def library_context(args, cfg, A, B, C, D, stream):
+    """The same call on PyTorch's own GEMM (hipBLASLt on ROCm), f32 output from
+    16-bit operands, for context only. The operands are views of the same
+    stored buffers (a transposed view where the flag says so); the library
+    picks its own kernel. beta != 0 goes through addmm with the same C."""
+    import torch
+    if cfg.dtype not in ("bf16", "f16"):
+        print("library context covers 16-bit operands only", file=sys.stderr)
+        sys.exit(2)
+    opA = A[:, : cfg.M].t() if cfg.transA else A[:, : cfg.K]
+    opB = B[:, : cfg.K].t() if cfg.transB else B[:, : cfg.N]
+    Dv = D[:, : cfg.N]
+    if cfg.beta != 0.0:
+        Cv = C[:, : cfg.N]  # the same storage as Dv for the in-place workloads
+
+        def step():
+            torch.addmm(Cv, opA, opB, beta=cfg.beta, alpha=cfg.alpha,
+                        out_dtype=torch.float32, out=Dv)
+    elif cfg.alpha == 1.0:
+        def step():
+            torch.mm(opA, opB, out_dtype=torch.float32, out=Dv)
+    else:
+        def step():
+            torch.mm(opA, opB, out_dtype=torch.float32, out=Dv)
+            Dv.mul_(cfg.alpha)
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record(stream)
+        for i in range(args.steps):
+            step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = evs[0].elapsed_time(evs[-1]) / args.steps
+        clock = sustained_clock(step, stream, ms, args.clock_seconds) if args.clock_seconds > 0 else None
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    tflops = float(cfg.flops) / (ms * 1e-3) / 1e12
+    if clock and "ms_per_step" in clock:
+        clock["tflops"] = round(float(cfg.flops) / (clock["ms_per_step"] * 1e-3) / 1e12, 2)
+    print(json.dumps({
+        "context": True,
+        "library": f"torch {torch.__version__} mm/addmm, out_dtype=float32",
+        "metric": "TFLOP/s (2MNK/t)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "ms_per_step": round(ms, 5),
+        "step_ms": {"median": round(step_ms[len(step_ms) // 2], 5), "min": round(step_ms[0], 5),
+                    "max": round(step_ms[-1], 5)},
+        "pct_of_mfma_peak": round(100.0 * tflops / PEAK_TFLOPS[cfg.dtype], 2),
+        "clock": clock,
+        "config": {"workload": cfg.name, "M": cfg.M, "N": cfg.N, "K": cfg.K,
+                   "transA": cfg.transA, "transB": cfg.transB, "alpha": cfg.alpha,
+                   "beta": cfg.beta},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,12 +483,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gemm8192_nt")
     ap.add_argument("--shape", default=None,
-                    help="an ad-hoc workload instead: M,N,K,dtype,transA,transB[,alpha,beta] "
+                    help="an ad-hoc workload instead: M,N,K,dtype,transA,transB[,alpha,beta"
+                         "[,lda[,ldb]]] "
                          "(normal(0,1) inputs, seed 7; for tile-choice measurements)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--clock-seconds", type=float, default=2.5,
+                    help="length of the sustained run after the timed steps over which the "
+                         "clock and power are read (0: skip)")
+    ap.add_argument("--library-context", action="store_true",
+                    help="time PyTorch's own GEMM (hipBLASLt on ROCm) on the same operands "
+                         "instead of this library, for context; prints a line marked "
+                         '"context": true')
     ap.add_argument("--per-call", type=int, default=None,
                     help="samples of per-call hot and cold timing (default: 200 for the "
                          "workloads that fit in the MALL, 0 otherwise)")
@@ -391,9 +526,13 @@ def main():
     if args.shape:
         f = args.shape.split(",")
         alpha, beta = (float(f[6]), float(f[7])) if len(f) >= 8 else (1.0, 0.0)
-        cfg = workloads.Config(f"shape{f[0]}x{f[1]}x{f[2]}_{f[3]}_{f[4]}{f[5]}", int(f[0]),
-                               int(f[1]), int(f[2]), f[3], int(f[4]), int(f[5]), alpha, beta,
-                               "normal", 7)
+        lda = int(f[8]) if len(f) >= 9 else None
+        ldb = int(f[9]) if len(f) >= 10 else None
+        name = f"shape{f[0]}x{f[1]}x{f[2]}_{f[3]}_{f[4]}{f[5]}"
+        if lda is not None or ldb is not None:
+            name += f"_lda{lda}_ldb{ldb}"
+        cfg = workloads.Config(name, int(f[0]), int(f[1]), int(f[2]), f[3], int(f[4]), int(f[5]),
+                               alpha, beta, "normal", 7, lda=lda, ldb=ldb)
     else:
         cfg = {**workloads.CONFIGS, **workloads.EXTRA_CONFIGS}[args.workload]
     lda, ldb, ldc, ldd = cfg.lds()
@@ -413,6 +552,10 @@ def main():
         dgt.gemm(cfg.M, cfg.N, cfg.K, cfg.dtype, cfg.transA, cfg.transB, cfg.alpha, cfg.beta,
                  A, lda, B, ldb, C, ldc, D, ldd, stream=stream)
 
+    if args.library_context:
+        library_context(args, cfg, A, B, C, D, stream)
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -423,14 +566,13 @@ def main():
     # stream): whole-region time and each step's own time.
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        w0 = time.perf_counter()
-        evs[0].record(stream)
-        for i in range(args.steps):
-            step()
-            evs[i + 1].record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - w0
+    w0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
     gpu_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = gpu_ms / args.steps
     step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
@@ -439,6 +581,14 @@ def main():
     if n_per_call is None:
         n_per_call = 200 if cfg.name in PER_CALL_DEFAULT else 0
     per_call = per_call_timing(step, stream, n_per_call) if n_per_call > 0 else None
+
+    # Clock and power: the sensors refresh about once a second, far longer
+    # than the timed steps, so they are read over a sustained run of the same
+    # step after the timed region (its own time per step reported beside).
+    clock = sustained_clock(step, stream, ms_per_step, args.clock_seconds) \
+        if args.clock_seconds > 0 else None
+    if clock and "ms_per_step" in clock:
+        clock["tflops"] = round(float(cfg.flops) / (clock["ms_per_step"] * 1e-3) / 1e12, 2)
 
     # Parity of what was timed: a fresh call, then sampled rows against the oracle.
     max_rel = None
@@ -504,7 +654,7 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "step_ms": {"median": round(step_ms[len(step_ms) // 2], 5), "min": round(step_ms[0], 5),
                     "max": round(step_ms[-1], 5)},
-        "clock": clock.summary(),
+        "clock": clock,
         "roofline": roofline,
     }
     if per_call is not None:
