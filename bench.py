@@ -174,6 +174,29 @@ class ClockSampler:
         return out
 
 
+def warm_up(step, steps: int, seconds: float):
+    """Runs `steps` untimed steps, then more until `seconds` have passed since
+    the first (host syncs every ~20 ms). Returns what was run."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(steps):
+        step()
+        n += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < seconds:
+        t1 = time.perf_counter()
+        k = 0
+        while time.perf_counter() - t1 < 0.02:
+            step()
+            k += 1
+            if k % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        n += k
+    return {"steps": n, "seconds": round(time.perf_counter() - t0, 3)}
+
+
 def sustained_clock(step, stream, ms_per_step: float, seconds: float, settle_s: float = 1.0):
     """Runs `step` back to back for `seconds` (untimed for the result; the
     same call as the timed steps) and returns the clock and power sampled
@@ -295,9 +318,7 @@ def bench_i8(args):
     def step():
         dgt.gemm_i8(M, N, K, 0, 1, 1, 0, Ad, K, Bd, K, None, N, D, N, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup, args.warmup_seconds)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(args.steps):
@@ -347,9 +368,7 @@ def bench_fp8(args):
     def step():
         dgt.gemm(M, N, K, "f8e4m3", 0, 1, 1.0, 0.0, Ad, K, Bd, K, None, N, D, N, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup, args.warmup_seconds)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(args.steps):
@@ -444,9 +463,7 @@ def library_context(args, cfg, A, B, C, D, stream):
             torch.mm(opA, opB, out_dtype=torch.float32, out=Dv)
             Dv.mul_(cfg.alpha)
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
+        warm = warm_up(step, args.warmup, args.warmup_seconds)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         evs[0].record(stream)
         for i in range(args.steps):
@@ -466,6 +483,7 @@ def library_context(args, cfg, A, B, C, D, stream):
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "ms_per_step": round(ms, 5),
+        "warmup_run": warm,
         "step_ms": {"median": round(step_ms[len(step_ms) // 2], 5), "min": round(step_ms[0], 5),
                     "max": round(step_ms[-1], 5)},
         "pct_of_mfma_peak": round(100.0 * tflops / PEAK_TFLOPS[cfg.dtype], 2),
@@ -490,6 +508,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="after the --warmup steps, keep running untimed steps until this many "
+                         "seconds of warmup have passed: an idle GPU sits at a sleep clock and "
+                         "ramps up over about a second of load (0: the --warmup steps only)")
     ap.add_argument("--clock-seconds", type=float, default=2.5,
                     help="length of the sustained run after the timed steps over which the "
                          "clock and power are read (0: skip)")
@@ -556,9 +578,7 @@ def main():
         library_context(args, cfg, A, B, C, D, stream)
         return
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm = warm_up(step, args.warmup, args.warmup_seconds)
     path = dgt.gemm_last_path()
 
     # The timed steps, back to back, with a HIP event on the launch stream
@@ -639,6 +659,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": warm,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -33,6 +33,7 @@ struct MfmaPath {
   const char* epi;
   bool pingpong, masked, k16_tail, ring;
   int ring_mode;
+  int atom;           // 16: the two-group kernel on 16x16x32 atoms; 0: the tile's own
   const char* src32;  // "", " f32->f16" or " f32->bf16"
   std::string elem_reason;  // operands read in narrow pieces (general kernel)
   std::string staged;       // operands staged through registers (ring kernel)
@@ -45,9 +46,11 @@ const std::string& current_path() {
     const MfmaPath& m = g_mpath;
     char buf[512], ksplit[32] = "";
     if (m.ti->kg > 1) std::snprintf(ksplit, sizeof ksplit, " ksplit%d", m.ti->kg);
+    const bool a16 = m.atom == 16;
     std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s%s%s%s%s%s%s",
-                  m.ti->name, m.ti->waves_m, m.pingpong ? 4 : m.ti->waves_n, m.ti->atom_m,
-                  m.ti->atom_n, m.ti->atom_k, m.ops, m.epi, ksplit,
+                  m.ti->name, m.ti->waves_m, m.pingpong ? 4 : m.ti->waves_n,
+                  a16 ? 16 : m.ti->atom_m, a16 ? 16 : m.ti->atom_n, a16 ? 32 : m.ti->atom_k,
+                  m.ops, m.epi, ksplit,
                   m.pingpong ? " pingpong" : "",
                   !m.ring ? ""
                   : m.ring_mode == RING_KSPLIT2 ? " ring ksplit2"
@@ -479,6 +482,9 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   g_mpath.ops = ops;
   g_mpath.epi = epi_name;
   g_mpath.pingpong = pingpong;
+  // The two-group kernel for 16-bit operands multiplies on 16x16x32 atoms
+  // when A is K-contiguous (see gemm_mfma_pingpong.h).
+  g_mpath.atom = pingpong && !plan.pp_f32 && !transA ? 16 : 0;
   g_mpath.ring = plan.ring;
   g_mpath.ring_mode = a.ring_mode;
   g_mpath.staged.swap(staged);

@@ -10,8 +10,14 @@
 //  * Eight waves, two groups of four. Wave w runs on SIMD w % 4, so every SIMD
 //    holds one wave of each group. Group g owns output rows [128g, 128g+128)
 //    of the tile, wave w within it the 64 columns [64(w%4), +64): a 128x64
-//    block of 4x2 v_mfma_f32_32x32x16 atoms (128 accumulator registers, so two
-//    waves fit one SIMD's register file).
+//    block of atoms (128 accumulator registers, so two waves fit one SIMD's
+//    register file). The atom is v_mfma_f32_16x16x32 (8x4 of them) when A is
+//    K-contiguous and v_mfma_f32_32x32x16 (4x2) when A is M-contiguous. Both
+//    give the same sums bit for bit here; the chip runs this kernel at its
+//    power limit, and the 16x16x32 form draws less power per cycle, so it
+//    clocks higher: measured +5% at 8192^3 with B [N][K], +3% with B [K][N],
+//    but -1 to -5% when A is [K][M], whose transposed fragment reads then
+//    wait longer.
 //  * Time is cut into phases at workgroup barriers. In each phase one group
 //    multiplies a whole K slice of 64 from registers (32 MFMAs per wave, no
 //    memory instruction in between) while the other group reads its next
@@ -30,16 +36,23 @@
 //    the phase in which the second group read it, and every load has at least
 //    one further phase to land before the barrier that certifies it.
 //  * K-contiguous operand slot: 256 rows (M or N) of 128 bytes (64 K-values,
-//    eight 16-byte chunks); chunk c of row r sits at chunk position
-//    c ^ ((r ^ (r>>3)) & 7), as in the general kernel. A fragment (8
-//    consecutive K-values of one row) is one ds_read_b128.
+//    eight 16-byte chunks); chunk c of row r sits at chunk position c ^ s(r).
+//    A fragment (8 consecutive K-values of one row) is one ds_read_b128. For
+//    the 32x32x16 atom s(r) = (r ^ (r>>3)) & 7, as in the general kernel; the
+//    16x16x32 atom reads 16 rows x 4 chunks per instruction instead of 32 x
+//    2, which that swizzle serves with 2-way bank conflicts (measured), so it
+//    uses s(r) = r1 | (r0 ^ r3) << 1 | r2 << 2 (ri: bit i of r), chosen to be
+//    conflict-free under every lane grouping of the LDS that agrees with the
+//    conflict counts measured for both atoms, and measured conflict-free.
 //  * M/N-contiguous operand slot: 64 rows (K) of 512 bytes (256 M or N values,
-//    32 chunks); chunk c of row r sits at c ^ (4 * (r & 3)). A fragment is two
-//    ds_read_b64_tr_b16: in each group of 16 lanes, lane s names 4 consecutive
-//    values of row s/4, and lane i receives value i of the group's 16 columns
-//    from each of the four rows, i.e. 4 consecutive K-values of one column.
-//    The swizzle spreads the 4 rows x 64 bytes that 32 lanes read over all
-//    banks.
+//    32 chunks); chunk c of row r sits at c ^ (4 * (r & 3)), and for the
+//    16x16x32 atom also ^ (2 * r3). A fragment is two ds_read_b64_tr_b16: in
+//    each group of 16 lanes, lane s names 4 consecutive values of row s/4, and
+//    lane i receives value i of the group's 16 columns from each of the four
+//    rows, i.e. 4 consecutive K-values of one column. The swizzle spreads the
+//    rows that 32 lanes read over all banks (rows 0-3 and 0-3 of the next 16
+//    columns for the 32-wide atom, rows 0-3 and 8-11 of the same 16 columns
+//    for the 16-wide one).
 //  * This compiler inserts no waits between a direct-to-LDS load and LDS
 //    reads of the same bytes: each wave waits on vmcnt for its own loads of a
 //    slice before the barrier that precedes the slice's first read.
@@ -49,10 +62,11 @@
 
 namespace dgt {
 
-struct PingPongCfg {
+template <int ATOM>
+struct PingPongCfgT {
   static constexpr int BM = 256, BN = 256, BK = 64;
   static constexpr int WM = 2, WN = 4, THREADS = WM * WN * 64;
-  using At = Atom<32>;
+  using At = Atom<ATOM>;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // 128 x 64 per wave
   static constexpr int TM = WTM / At::M, TN = WTN / At::N;
   static constexpr int KSTEPS = BK / At::K;            // MFMA K sub-steps per slice
@@ -64,6 +78,8 @@ struct PingPongCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
   static_assert(LOADS == 8, "four waves load one 32 KiB half slice");
 };
+// The 1-byte-operand and float32-operand kernels use the 32x32 layout.
+using PingPongCfg = PingPongCfgT<32>;
 
 // s_waitcnt with the other counters left alone (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -95,21 +111,27 @@ typedef short pp_i16x4 __attribute__((ext_vector_type(4)));
 
 // One operand's loads (by the wave group that loads it) and fragment reads
 // (by every wave). MN: the operand is stored with M (or N) contiguous.
-// NFRAG atoms of 32 rows/columns per wave, starting at row0 of the tile.
-template <bool MN, int NFRAG>
+// NFRAG atoms of ATOM rows/columns per wave, starting at row0 of the tile.
+template <bool MN, int NFRAG, int ATOM = 32>
 struct PpOperand;
 
-template <int NFRAG>
-struct PpOperand<false, NFRAG> {
-  using C = PingPongCfg;
-  // Load side: this lane's byte offset for instruction 0 and its chunk.
-  const char* base;  // tile's first row (M or N index), K = 0
-  int ld2, row, c0;  // ld2: row pitch in bytes
+template <int NFRAG, int ATOM>
+struct PpOperand<false, NFRAG, ATOM> {
+  using C = PingPongCfgT<ATOM>;
+  using At = typename C::At;
+  // Load side: this lane's byte offset for instruction 0 and its chunk (for
+  // the 16-wide atom, c1 for the odd instructions).
+  const char* base;      // tile's first row (M or N index), K = 0
+  int ld2, row, c0, c1;  // ld2: row pitch in bytes
   // Read side: byte offset of each atom's fragment within a slot, sub-step 0.
   int off[NFRAG];
 
+  __device__ static inline int swz(int r) {
+    if constexpr (ATOM == 16) return ((r >> 1) & 1) | (((r ^ (r >> 3)) & 1) << 1) | (r & 4);
+    else return (r ^ (r >> 3)) & 7;
+  }
   __device__ static inline int lds_off(int r, int chunk) {
-    return r * 128 + ((chunk ^ ((r ^ (r >> 3)) & 7)) << 4);
+    return r * 128 + ((chunk ^ swz(r)) << 4);
   }
   // esz: bytes per element (2 for f16/bf16; 1 for the 1-byte-operand
   // kernels, whose 128-byte rows hold 128 K-values).
@@ -118,71 +140,91 @@ struct PpOperand<false, NFRAG> {
     base = static_cast<const char*>(X) + (int64_t)r0 * ld * esz;
     ld2 = (int)(ld * esz);
     // Instruction i of wave lw covers rows 64*lw + 8i .. +7. Lane l fills
-    // chunk slot l%8 of row 64*lw + 8i + l/8, whose swizzle is (l/8) ^ i, so
-    // it fetches chunk (l%8) ^ (l/8) ^ i of that row.
+    // chunk slot l%8 of row r = 64*lw + 8i + l/8, so it fetches chunk
+    // (l%8) ^ s(r) of that row: for the 32-wide atom s(r) = (l/8) ^ i, for
+    // the 16-wide one s depends on r & 15 = 8(i&1) + l/8.
     row = (lw * 64 + (lane >> 3)) * ld2;
-    c0 = (lane & 7) ^ (lane >> 3);
+    if constexpr (ATOM == 16) {
+      c0 = (lane & 7) ^ swz(lane >> 3);
+      c1 = (lane & 7) ^ swz(8 + (lane >> 3));
+    } else {
+      c0 = (lane & 7) ^ (lane >> 3);
+      c1 = 0;
+    }
   }
   __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
-    const int voff = row + ((c0 ^ i) << 4);
+    const int chunk = ATOM == 16 ? ((i & 1) ? c1 : c0) : c0 ^ i;
+    const int voff = row + (chunk << 4);
     const int soff = slice * 128 + i * 8 * ld2;  // a slice is 128 bytes of each row
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
                                              16, voff, soff, 0, 0);
   }
   __device__ inline void init_read(int row0, int lane) {
-    // Fragment rows keep their low three bits per lane and the chunk of
-    // sub-step ks is 2*ks + koct, so sub-step ks is the sub-step-0 offset with
-    // ks << 5 XOR-ed in (bits 5-6 of the chunk position).
+    // The chunk of sub-step ks is (K / 8) * ks + koct, whose sub-step term
+    // only touches chunk bits the lane's own koct leaves clear, so sub-step ks
+    // is the sub-step-0 offset with that term XOR-ed in (byte bits 5-6 for
+    // the 32-wide atom, bit 6 for the 16-wide one).
 #pragma unroll
     for (int t = 0; t < NFRAG; ++t)
-      off[t] = lds_off(row0 + t * 32 + (lane & 31), lane >> 5);
+      off[t] = lds_off(row0 + t * At::M + At::frag_row(lane), At::frag_koct(lane));
   }
   __device__ __forceinline__ u32x4 read(const char* slot, int t, int ks) const {
-    return *reinterpret_cast<const u32x4*>(slot + (off[t] ^ (ks << 5)));
+    return *reinterpret_cast<const u32x4*>(slot + (off[t] ^ (ks << (ATOM == 16 ? 6 : 5))));
   }
 };
 
-template <int NFRAG>
-struct PpOperand<true, NFRAG> {
-  using C = PingPongCfg;
+template <int NFRAG, int ATOM>
+struct PpOperand<true, NFRAG, ATOM> {
+  using C = PingPongCfgT<ATOM>;
+  static constexpr int NV = ATOM == 16 ? 4 : 2;  // distinct load offsets
   const uint16_t* base;  // tile's first column (M or N index), K = 0
   int64_t ld;
-  int voff[2];           // instructions with i even / odd
+  int voff[NV];          // by instruction i: i & 1 (and i >= 4 for the 16-wide atom)
   int off[NFRAG];
 
+  // Chunk swizzle of K row r of a slot.
+  __device__ static inline int swz(int r) {
+    return ATOM == 16 ? (4 * (r & 3)) ^ (2 * ((r >> 3) & 1)) : 4 * (r & 3);
+  }
   __device__ inline void init_load(const uint16_t* X, int64_t ld_, int c0, int lw, int lane) {
     base = X + c0;
     ld = ld_;
     // Instruction i of wave lw covers K rows 16*lw + 2i and +1 (512 bytes
-    // each). Lane l fills chunk slot l%32 of row 16*lw + 2i + l/32, whose
-    // swizzle is 4*((2i + l/32) & 3), so it fetches that chunk of the row.
+    // each). Lane l fills chunk slot l%32 of row r = 16*lw + 2i + l/32, so it
+    // fetches chunk (l%32) ^ swz(r) of that row; swz(r) depends on i & 1 and
+    // (16-wide atom) on i >= 4, which set r & 3 and bit 3 of r.
     const int hi = lane >> 5, p = lane & 31;
 #pragma unroll
-    for (int par = 0; par < 2; ++par)
-      voff[par] = (int)((lw * 16 + hi) * ld * 2) + ((p ^ (4 * ((2 * par + hi) & 3))) << 4);
+    for (int q = 0; q < NV; ++q)
+      voff[q] = (int)((lw * 16 + hi) * ld * 2) + ((p ^ swz(2 * (q & 1) + hi + 8 * (q >> 1))) << 4);
   }
   __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
     // The slice's first K row is folded into the resource base so that the
     // 32-bit offsets stay within 16 rows of the operand.
     const uint16_t* b = base + (int64_t)slice * C::BK * ld;
+    const int q = ATOM == 16 ? (i & 1) | ((i >= 4) << 1) : (i & 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(b), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
-                                             16, voff[i & 1], (int)(2 * i * ld * 2), 0, 0);
+                                             16, voff[q], (int)(2 * i * ld * 2), 0, 0);
   }
   __device__ inline void init_read(int col0, int lane) {
     // Lane l (group g = l/16, s = l%16) of the first transposed read of
-    // sub-step 0 names row 8*(l/32) + s/4, columns col0 + 16*(g&1) + 4*(s%4)
-    // .. +3. The second read is 4 rows down, sub-step ks is 16*ks rows down:
-    // both keep r & 3, so they are immediate offsets.
-    const int r = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    // sub-step 0 names row r, columns c .. c+3 of its atom, with
+    //   32-wide atom: r = 8*(l/32) + s/4, c = 16*(g&1) + 4*(s%4);
+    //   16-wide atom: r = 8*g + s/4,      c = 4*(s%4).
+    // The second read is 4 rows down, sub-step ks is K*ks rows down: both
+    // keep r & 3 and bit 3 of r, so they are immediate offsets.
+    const int r = ATOM == 16 ? 8 * (lane >> 4) + ((lane & 15) >> 2)
+                             : 8 * (lane >> 5) + ((lane & 15) >> 2);
 #pragma unroll
     for (int t = 0; t < NFRAG; ++t) {
-      const int col = col0 + t * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      off[t] = r * 512 + (((col >> 3) ^ (4 * (r & 3))) << 4) + ((col & 7) << 1);
+      const int col = ATOM == 16 ? col0 + t * 16 + 4 * (lane & 3)
+                                 : col0 + t * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      off[t] = r * 512 + (((col >> 3) ^ swz(r)) << 4) + ((col & 7) << 1);
     }
   }
   __device__ __forceinline__ u32x4 read(const char* slot, int t, int ks) const {
     typedef __attribute__((address_space(3))) pp_i16x4 lds_i16x4;
-    const char* p = slot + off[t] + ks * 16 * 512;
+    const char* p = slot + off[t] + ks * C::At::K * 512;
     const pp_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
     const pp_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * 512));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
@@ -204,13 +246,13 @@ __device__ __forceinline__ void pp_multiply(typename C::At::acc_t (&acc)[C::TM][
         acc[i][j] = At::mma(Tag{}, f[ks].a[i], f[ks].b[j], acc[i][j]);
 }
 
-template <bool AMN, bool BMN>
+template <bool AMN, bool BMN, int ATOM>
 struct PingPongPipe {
-  using C = PingPongCfg;
+  using C = PingPongCfgT<ATOM>;
   char* smem;
   int lw;  // wave index within its group
-  PpOperand<AMN, C::TM> a;
-  PpOperand<BMN, C::TN> b;
+  PpOperand<AMN, C::TM, ATOM> a;
+  PpOperand<BMN, C::TN, ATOM> b;
 
   __device__ inline void init(const GemmArgs& p, char* smem_, int m0, int n0, int group, int wave,
                               int lane, int wm, int wn) {
@@ -252,10 +294,18 @@ struct PingPongPipe {
     for (int t = 0; t < C::TM; ++t) asm volatile("" : "+v"(a.off[t]));
 #pragma unroll
     for (int t = 0; t < C::TN; ++t) asm volatile("" : "+v"(b.off[t]));
-    if constexpr (AMN) asm volatile("" : "+v"(a.voff[0]), "+v"(a.voff[1]));
-    else asm volatile("" : "+v"(a.row), "+v"(a.c0));
-    if constexpr (BMN) asm volatile("" : "+v"(b.voff[0]), "+v"(b.voff[1]));
-    else asm volatile("" : "+v"(b.row), "+v"(b.c0));
+    launder_operand<AMN>(a);
+    launder_operand<BMN>(b);
+  }
+  template <bool MN, class Op>
+  __device__ __forceinline__ static void launder_operand(Op& x) {
+    if constexpr (MN) {
+#pragma unroll
+      for (int q = 0; q < Op::NV; ++q) asm volatile("" : "+v"(x.voff[q]));
+    } else {
+      asm volatile("" : "+v"(x.row), "+v"(x.c0));
+      if constexpr (ATOM == 16) asm volatile("" : "+v"(x.c1));
+    }
   }
 };
 
@@ -270,7 +320,8 @@ struct PingPongPipe {
 // instantiated for the first one.
 template <class C, class Tag, int EPI, bool AMN, bool BMN>
 __device__ __forceinline__ void pp_mainloop(typename C::At::acc_t (&acc)[C::TM][C::TN],
-                                            const PingPongPipe<AMN, BMN>& pipe, int K, int group) {
+                                            const PingPongPipe<AMN, BMN, C::At::M>& pipe, int K,
+                                            int group) {
   const int KT = K / C::BK;  // whole slices (unmasked kernel)
   // Prologue: group 1 requests A of slices 0 and 1, group 0 B of slice 0.
   if (group == 1) {
@@ -292,7 +343,7 @@ __device__ __forceinline__ void pp_mainloop(typename C::At::acc_t (&acc)[C::TM][
   }
 
   Frags<C> f[C::KSTEPS];
-  PingPongPipe<AMN, BMN> pp = pipe;
+  PingPongPipe<AMN, BMN, C::At::M> pp = pipe;
   int h = 0;  // (2s) % 5: the slot of A of slice s
   for (int s = 0; s < KT; ++s) {
     pp.launder();
@@ -328,7 +379,7 @@ __device__ __forceinline__ void pp_mainloop(typename C::At::acc_t (&acc)[C::TM][
 
 template <class Tag, int EPI, bool AMN, bool BMN>
 __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_mfma_pingpong_kernel(const GemmArgs p) {
-  using C = PingPongCfg;
+  using C = PingPongCfgT<AMN ? 32 : 16>;  // the atom: see the notes at the top
   using At = typename C::At;
   using acc_t = typename At::acc_t;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
@@ -344,7 +395,7 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_mfma_pingpong_kerne
   const int m0 = tm * C::BM;
   const int n0 = tn * C::BN;
 
-  PingPongPipe<AMN, BMN> pipe;
+  PingPongPipe<AMN, BMN, C::At::M> pipe;
   pipe.init(p, smem, m0, n0, group, wave, lane, wm, wn);
 
   acc_t acc[C::TM][C::TN];

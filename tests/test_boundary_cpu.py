@@ -300,9 +300,12 @@ def test_huge_pitch_takes_64bit_addressing(lib):
 
 def test_tile_and_epilogue_choice(lib):
     assert _v(lib, M=8192, N=8192, K=8192, tB=1, dtype=1) == lib.GEMM_OK
-    assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 pingpong"
+    assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a16x16x32 NT epi=beta0 pingpong"
     assert _v(lib, M=4096, N=4096, K=4096, dtype=1, beta=1.0, C=D0) == lib.GEMM_OK
-    assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 NN epi=acc+c pingpong"
+    assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a16x16x32 NN epi=acc+c pingpong"
+    # A stored [K][M]: the two-group kernel keeps the 32x32x16 atom
+    assert _v(lib, M=4096, N=4096, K=4096, tA=1, dtype=1) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 TN epi=beta0 pingpong"
     assert _v(lib, M=512, N=512, K=512, alpha=1.5, beta=0.5) == lib.GEMM_OK
     assert lib.gemm_last_path() == "mfma t32x32x64k4 w1x1 a32x32x16 NN epi=general ksplit4"
 
