@@ -573,6 +573,87 @@ __device__ inline void store_tile_wide(typename Cfg::At::acc_t (&acc)[Cfg::TM][C
   }
 }
 
+// The 16-byte form for 16x16 atoms, two atoms (j, j+1) of a row of atoms at
+// a time. After the quad transpose a lane holds 4 consecutive columns of one
+// row in each atom, so a store instruction per atom would write 64 bytes of
+// each row: half of a 128-byte line, which the memory side then fills and
+// writes in part (measured at 8192^3: 1.4x D's bytes written and D's size
+// again read). Lanes l and l^1, which hold rows r and r+1, swap one chunk:
+// the even lane sends its atom-(j+1) chunk and the odd lane its atom-j chunk.
+// Then the first instruction writes row r (even lane: its own atom-j chunk,
+// odd lane: the received atom-(j+1) chunk) and the second writes row r+1,
+// each lane at the column of atom j + (l & 1): 8 lanes cover the row's 32
+// columns, 128 bytes. PLAIN_STORE as in store_tile_wide.
+template <class Cfg, int EPI, bool MASK, bool PLAIN_STORE>
+__device__ inline void store_tile_pairs16(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::TN],
+                                          const GemmArgs& p, int r0, int c0, int lane) {
+  using At = typename Cfg::At;
+  static_assert(At::M == 16 && At::NACC == 4 && Cfg::TN % 2 == 0, "pairs of 16x16 atoms");
+  constexpr int NP = Cfg::TN / 2;
+  const float alpha = p.alpha, beta = p.beta;
+  const int odd = lane & 1;
+  const int col = 16 * odd + 4 * ((lane >> 2) & 3);           // within the atom pair
+  const int rl = At::acc_row(lane, 0) + (lane & 3) - odd;     // row of the first store
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i) {
+    const int r = r0 + i * At::M + rl;
+    f32x4 cv[NP][2];
+    if constexpr (EPI != EPI_BETA0) {
+      // Every C value of the row of atoms is loaded before any D store (C
+      // may be D).
+#pragma unroll
+      for (int q = 0; q < NP; ++q) {
+        const int c = c0 + 32 * q + col;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          cv[q][h] = (!MASK || (r + h < p.M && c < p.N))
+                         ? *reinterpret_cast<const f32x4*>(p.C + (int64_t)(r + h) * p.ldc + c)
+                         : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      float x[4] = {acc[i][2 * q][0], acc[i][2 * q][1], acc[i][2 * q][2], acc[i][2 * q][3]};
+      float y[4] = {acc[i][2 * q + 1][0], acc[i][2 * q + 1][1], acc[i][2 * q + 1][2],
+                    acc[i][2 * q + 1][3]};
+      quad_transpose(x, lane);
+      quad_transpose(y, lane);
+      float w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                             __builtin_bit_cast(int, odd ? x[k] : y[k]), 0xB1,
+                                             0xF, 0xF, false));
+      const int c = c0 + 32 * q + col;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float v = h == 0 ? (odd ? w[k] : x[k]) : (odd ? y[k] : w[k]);
+          if constexpr (EPI != EPI_BETA0) o[k] = epi_one<EPI>(v, cv[q][h][k], alpha, beta);
+          else o[k] = epi_one<EPI>(v, 0.0f, alpha, beta);
+        }
+        if (!MASK || (r + h < p.M && c < p.N)) {
+          f32x4* dst = reinterpret_cast<f32x4*>(p.D + (int64_t)(r + h) * p.ldd + c);
+          if constexpr (PLAIN_STORE) *dst = o;
+          else __builtin_nontemporal_store(o, dst);
+        }
+      }
+    }
+  }
+}
+
+// store_tile_pairs16 where the atoms pair up, else store_tile_wide.
+template <class Cfg, int EPI, bool MASK, bool PLAIN_STORE>
+__device__ inline void store_tile_pairs_or_wide(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::TN],
+                                                const GemmArgs& p, int r0, int c0, int lane) {
+  if constexpr (Cfg::At::M == 16 && Cfg::TN % 2 == 0)
+    store_tile_pairs16<Cfg, EPI, MASK, PLAIN_STORE>(acc, p, r0, c0, lane);
+  else
+    store_tile_wide<Cfg, EPI, MASK, PLAIN_STORE>(acc, p, r0, c0, lane, WideC<Cfg>{}, false);
+}
+
 template <class Cfg, int EPI, bool MASK>
 __device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::TN],
                                   const GemmArgs& p, int r0, int c0, int lane,
@@ -589,13 +670,18 @@ __device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::T
     // each store measured 3-4% slower on the 128x128 kernels. Plain stores
     // where D is C gain 1.2-1.8% on the in-place accumulate at 4096^3;
     // with a separate C they lose up to 5%.
+    // 16x16 atoms in pairs write whole 128-byte rows per instruction (C
+    // prefetched into registers is only passed with 32x32 atoms).
+    constexpr bool PAIRS = Cfg::At::M == 16 && Cfg::TN % 2 == 0;
     if constexpr (EPI != EPI_BETA0) {
       if (static_cast<const void*>(p.C) == p.D) {
-        store_tile_wide<Cfg, EPI, MASK, true>(acc, p, r0, c0, lane, pre, use_pre);
+        if (PAIRS && !use_pre) store_tile_pairs_or_wide<Cfg, EPI, MASK, true>(acc, p, r0, c0, lane);
+        else store_tile_wide<Cfg, EPI, MASK, true>(acc, p, r0, c0, lane, pre, use_pre);
         return;
       }
     }
-    store_tile_wide<Cfg, EPI, MASK, false>(acc, p, r0, c0, lane, pre, use_pre);
+    if (PAIRS && !use_pre) store_tile_pairs_or_wide<Cfg, EPI, MASK, false>(acc, p, r0, c0, lane);
+    else store_tile_wide<Cfg, EPI, MASK, false>(acc, p, r0, c0, lane, pre, use_pre);
     return;
   }
 #pragma unroll
