@@ -429,13 +429,15 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   // and the edges cutting its contiguous dimension fall on multiples of 8
   // elements, else staged through registers.
   std::string staged;
-  plan.ring = tile == TILE_128x128 && !src32 && !big_pitch;
+  // Float32 operands off the two-group kernel's NT fast path take the ring
+  // kernel too, both staged through registers and rounded there.
+  plan.ring = tile == TILE_128x128 && !big_pitch;
   if (plan.ring) {
     auto direct = [&](int vw, bool mn_contig, int64_t mn) {
       return vw == 8 && (mn_contig ? mn % 8 == 0 : K % 8 == 0);
     };
-    a.a_direct = direct(a_vw, transA != 0, M) ? 1 : 0;
-    a.b_direct = direct(b_vw, transB == 0, N) ? 1 : 0;
+    a.a_direct = !src32 && direct(a_vw, transA != 0, M) ? 1 : 0;
+    a.b_direct = !src32 && direct(b_vw, transB == 0, N) ? 1 : 0;
     auto why = [&](const char* name, const void* ptr, int64_t ld, int vw, bool mn_contig) {
       char w[160];
       if (vw != 8) {
@@ -450,8 +452,12 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
       }
       return std::string(w);
     };
-    if (!a.a_direct) staged = why("A", A, lda, a_vw, transA != 0);
-    if (!a.b_direct) staged += (staged.empty() ? "" : "; ") + why("B", B, ldb, b_vw, transB == 0);
+    if (src32) {
+      staged = "A, B: float32 values rounded in registers";
+    } else {
+      if (!a.a_direct) staged = why("A", A, lda, a_vw, transA != 0);
+      if (!a.b_direct) staged += (staged.empty() ? "" : "; ") + why("B", B, ldb, b_vw, transB == 0);
+    }
     elem_reason.clear();
     // "masked": edge tiles or a K tail (the ring kernel masks in place)
     plan.masked = (M % ti.bm) || (N % ti.bn) || (K % ti.bk);

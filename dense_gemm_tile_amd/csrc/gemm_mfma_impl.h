@@ -143,6 +143,25 @@ __device__ static inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
                                            0x00020000);
 }
 
+// Rounding of one float32 value to a 16-bit pattern, to nearest with ties to
+// even: mode 1 gives f16 (the hardware conversion, which rounds so in the
+// default mode), mode 2 bf16 (on the bit pattern; NaN stays a quiet NaN).
+__device__ inline unsigned round_f32_16(float x, int mode) {
+  if (mode == 1) return __builtin_bit_cast(unsigned short, (_Float16)x);
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+// Eight float32 values rounded and packed into one 16-byte piece.
+__device__ inline u32x4 round8_f32_16(const float (&f)[8], int mode) {
+  u32x4 r;
+  r.x = round_f32_16(f[0], mode) | (round_f32_16(f[1], mode) << 16);
+  r.y = round_f32_16(f[2], mode) | (round_f32_16(f[3], mode) << 16);
+  r.z = round_f32_16(f[4], mode) | (round_f32_16(f[5], mode) << 16);
+  r.w = round_f32_16(f[6], mode) | (round_f32_16(f[7], mode) << 16);
+  return r;
+}
+
 // One operand's R x 64 box (R rows of M or N, 64 K-values) per K step.
 // KCONTIG: element (r, k) is X[(r0 + r) * ld + k0 + k]  (A with transA = 0,
 //          B with transB = 1); otherwise X[(k0 + k) * ld + r0 + r].
@@ -177,22 +196,9 @@ struct Stager {
     return *reinterpret_cast<const u32x4_a2*>(p);
   }
 
-  // Rounding of one float32 value to a 16-bit pattern, to nearest with ties
-  // to even: mode 1 gives f16 (the hardware conversion, which rounds so in
-  // the default mode), mode 2 bf16 (on the bit pattern; NaN stays a quiet NaN).
-  __device__ static inline unsigned round16(float x, int mode) {
-    if (mode == 1) return __builtin_bit_cast(unsigned short, (_Float16)x);
-    const unsigned u = __builtin_bit_cast(unsigned, x);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  }
+  __device__ static inline unsigned round16(float x, int mode) { return round_f32_16(x, mode); }
   __device__ static inline u32x4 round8(const float (&f)[8], int mode) {
-    u32x4 r;
-    r.x = round16(f[0], mode) | (round16(f[1], mode) << 16);
-    r.y = round16(f[2], mode) | (round16(f[3], mode) << 16);
-    r.z = round16(f[4], mode) | (round16(f[5], mode) << 16);
-    r.w = round16(f[6], mode) | (round16(f[7], mode) << 16);
-    return r;
+    return round8_f32_16(f, mode);
   }
   // n_valid (0..8) float32 values of a piece, vw-element loads when whole.
   __device__ static inline u32x4 load_f32(const float* q, int n_valid, int vw, int mode) {

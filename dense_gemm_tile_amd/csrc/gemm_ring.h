@@ -92,19 +92,38 @@ __device__ inline u32x4 keep_first(u32x4 v, int nv) {
   return v;
 }
 
+// Registers of one operand's staged pieces between their loads and their
+// LDS writes: 16-bit values as the dwords that cover each piece (v, one more
+// dword e) and the piece's byte shift sh; float32 values as two 16-byte
+// halves (v, v2), rounded when written.
+template <bool SRC32, int L>
+struct RingStaged {
+  u32x4 v[L];
+  unsigned e[L], sh[L];
+};
+template <int L>
+struct RingStaged<true, L> {
+  u32x4 v[L], v2[L];
+};
+
 // One operand: its loads into a half-slot (direct or staged through
 // registers) and its fragment reads. MN: stored with M (or N) contiguous.
+// SRC32: the operand holds float32 values, staged only, each piece rounded
+// to the kernel's 16-bit type (ties to even) on its way into LDS, where it
+// takes the place a 16-bit piece would.
 // Instruction i (0..3) of wave w writes LDS bytes [(4w + i) KiB, +1 KiB) of
 // the half-slot, lane l the 16 bytes at l * 16 of that.
-template <bool MN, int ROWS>
+template <bool MN, int ROWS, bool SRC32 = false>
 struct RingOperand {
   using Cfg = RingCfg<ROWS>;
   static constexpr int LOADS = Cfg::LOADS;
   static constexpr int NFRAG = Cfg::TM;   // atoms per wave along this operand
   static constexpr int RB = ROWS * 2;     // bytes of one K-row of an M/N-contiguous slot
+  static constexpr int ESZ = SRC32 ? 4 : 2;  // bytes per stored element
+  using Staged = RingStaged<SRC32, LOADS>;
   const char* X;  // operand base
   int64_t ld2;    // row pitch in bytes
-  int64_t ext;    // bytes of the stored extent ((rows - 1) * ld + cols) * 2
+  int64_t ext;    // bytes of the stored extent ((rows - 1) * ld + cols) * ESZ
   int r0;         // tile origin along M (or N)
   int rlim;       // M (or N)
   int klim;       // K
@@ -129,11 +148,11 @@ struct RingOperand {
   __device__ inline void init(const void* Xv, int64_t ld, int r0_, int rlim_, int klim_,
                               int wsub, int lane) {
     X = static_cast<const char*>(Xv);
-    ld2 = ld * 2;
+    ld2 = ld * ESZ;
     r0 = r0_;
     rlim = rlim_;
     klim = klim_;
-    ext = MN ? ((int64_t)(klim - 1) * ld + rlim) * 2 : ((int64_t)(rlim - 1) * ld + klim) * 2;
+    ext = MN ? ((int64_t)(klim - 1) * ld + rlim) * ESZ : ((int64_t)(rlim - 1) * ld + klim) * ESZ;
     if constexpr (!MN) {
 #pragma unroll
       for (int t = 0; t < NFRAG; ++t)
@@ -157,23 +176,24 @@ struct RingOperand {
   // outside the operand. `start` is the piece's first index along the
   // contiguous dimension and `lim` that dimension's size (for masking).
   __device__ inline const char* slice_base(int t) const {
-    return MN ? X + (int64_t)t * Cfg::BK * ld2 + (int64_t)r0 * 2 : X + (int64_t)r0 * ld2;
+    return MN ? X + (int64_t)t * Cfg::BK * ld2 + (int64_t)r0 * ESZ : X + (int64_t)r0 * ld2;
   }
   __device__ inline int piece_off(int t, int rr, int cc, int& start, int& lim) const {
     if constexpr (!MN) {
       start = t * Cfg::BK + cc * 8;
       lim = klim;
       const bool in = r0 + rr < rlim && start < klim;
-      return in ? (int)(rr * ld2) + start * 2 : kOutOfRange;
+      return in ? (int)(rr * ld2) + start * ESZ : kOutOfRange;
     } else {
       start = r0 + cc * 8;
       lim = rlim;
       const bool in = t * Cfg::BK + rr < klim && start < rlim;
-      return in ? (int)(rr * ld2) + cc * 16 : kOutOfRange;
+      return in ? (int)(rr * ld2) + cc * 8 * ESZ : kOutOfRange;
     }
   }
 
   __device__ __forceinline__ void issue_direct(char* slot, int t, int w, int lane) const {
+    static_assert(!SRC32, "float32 operands are staged");
     const char* b = slice_base(t);
     const auto rs = make_rsrc_n(b, nrec_from(X, ext, b));
 #pragma unroll
@@ -192,10 +212,26 @@ struct RingOperand {
   // count then cuts at a dword boundary (the extent rounded up to a dword),
   // so no dword that holds part of an element is dropped and nothing past
   // the operand's last dword is read.
-  __device__ __forceinline__ void load_staged(u32x4 (&v)[LOADS],
-                                              unsigned (&e)[LOADS],
-                                              unsigned (&sh)[LOADS], int t, int w,
-                                              int lane) const {
+  __device__ __forceinline__ void load_staged(Staged& r, int t, int w, int lane) const {
+    if constexpr (SRC32) {
+      // Float32 elements are dword-aligned: each piece is two 16-byte loads
+      // at its own address (out-of-range offsets read zeros).
+      const char* b = slice_base(t);
+      const auto rs = make_rsrc_n(b, nrec_from(X, ext, b));
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        int rr, cc, start, lim;
+        piece(w, i, lane, rr, cc);
+        const int off = piece_off(t, rr, cc, start, lim);
+        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        r.v2[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, off == kOutOfRange ? kOutOfRange : off + 16, 0, 0);
+      }
+      return;
+    } else {
+    u32x4 (&v)[LOADS] = r.v;
+    unsigned (&e)[LOADS] = r.e;
+    unsigned (&sh)[LOADS] = r.sh;
     // The resource starts at the dword holding the slice's first byte, so
     // every dword-aligned offset below a piece's start is still >= 0.
     const char* b0 = slice_base(t);
@@ -216,23 +252,30 @@ struct RingOperand {
       e[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, aoff == kOutOfRange ? kOutOfRange : aoff + 16,
                                                   0, 0);
     }
+    }
   }
 
   // Shift each piece into place (the dwords were read from the dword at or
   // below its start), zero the elements past the edge of the contiguous
   // dimension (pieces that straddle it), then write the pieces where a
   // direct load would have.
-  __device__ __forceinline__ void store_staged(char* slot, const u32x4 (&v)[LOADS],
-                                               const unsigned (&e)[LOADS],
-                                               const unsigned (&sh)[LOADS], int t,
-                                               int w, int lane, bool edge) const {
+  // mode (float32 operands): 1 rounds to f16, 2 to bf16.
+  __device__ __forceinline__ void store_staged(char* slot, const Staged& r, int t, int w, int lane,
+                                               bool edge, int mode) const {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       u32x4 x;
-      x[0] = __builtin_amdgcn_alignbyte(v[i][1], v[i][0], sh[i]);
-      x[1] = __builtin_amdgcn_alignbyte(v[i][2], v[i][1], sh[i]);
-      x[2] = __builtin_amdgcn_alignbyte(v[i][3], v[i][2], sh[i]);
-      x[3] = __builtin_amdgcn_alignbyte(e[i], v[i][3], sh[i]);
+      if constexpr (SRC32) {
+        const f32x4 lo = __builtin_bit_cast(f32x4, r.v[i]);
+        const f32x4 hi = __builtin_bit_cast(f32x4, r.v2[i]);
+        const float f[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        x = round8_f32_16(f, mode);
+      } else {
+        x[0] = __builtin_amdgcn_alignbyte(r.v[i][1], r.v[i][0], r.sh[i]);
+        x[1] = __builtin_amdgcn_alignbyte(r.v[i][2], r.v[i][1], r.sh[i]);
+        x[2] = __builtin_amdgcn_alignbyte(r.v[i][3], r.v[i][2], r.sh[i]);
+        x[3] = __builtin_amdgcn_alignbyte(r.e[i], r.v[i][3], r.sh[i]);
+      }
       if (edge) {
         int rr, cc, start, lim;
         piece(w, i, lane, rr, cc);
@@ -270,8 +313,9 @@ struct RingRow : C {
 // independent waves. The groups' accumulators are summed in group order.
 // ROWS: tile side (128: 64x64 per wave, two workgroups per CU with KG = 1).
 // STAGING: operands staged through registers are supported (otherwise both
-// must be direct).
-template <int ROWS, class Tag, int EPI, bool AMN, bool BMN, int KG, bool STAGING>
+// must be direct). SRC32: both operands hold float32 values (staged, rounded
+// to Tag's type with mode p.src32).
+template <int ROWS, class Tag, int EPI, bool AMN, bool BMN, int KG, bool STAGING, bool SRC32 = false>
 __global__ void __launch_bounds__(RingCfg<ROWS>::THREADS * KG, RingCfg<ROWS>::MIN_WG / KG)
 gemm_ring_kernel(const GemmArgs p) {
   using C = RingCfg<ROWS>;
@@ -289,13 +333,16 @@ gemm_ring_kernel(const GemmArgs p) {
   schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
 
-  RingOperand<AMN, ROWS> a;
-  RingOperand<BMN, ROWS> b;
+  static_assert(!SRC32 || STAGING, "float32 operands are staged");
+  RingOperand<AMN, ROWS, SRC32> a;
+  RingOperand<BMN, ROWS, SRC32> b;
   a.init(p.A, p.lda, m0, p.M, p.K, wm, lane);
   b.init(p.B, p.ldb, n0, p.N, p.K, wn, lane);
+  const int mode = p.src32;
   // Staging modes (uniform over the launch) and, for staged operands, whether
   // this tile's pieces can straddle the edge of the contiguous dimension.
-  const bool a_dir = !STAGING || p.a_direct, b_dir = !STAGING || p.b_direct;
+  const bool a_dir = !SRC32 && (!STAGING || p.a_direct);
+  const bool b_dir = !SRC32 && (!STAGING || p.b_direct);
   const bool a_edge = AMN ? (m0 + C::BM > p.M && p.M % 8 != 0) : (p.K % 8 != 0);
   const bool b_edge = BMN ? (n0 + C::BN > p.N && p.N % 8 != 0) : (p.K % 8 != 0);
   const bool staged = !a_dir || !b_dir;
@@ -323,9 +370,9 @@ gemm_ring_kernel(const GemmArgs p) {
   const int NJ = KT > grp ? (KT - grp + KG - 1) / KG : 0;  // this group's slices
   auto gs = [&](int j) { return j * KG + grp; };
   auto slot = [&](int h) { return smem + (h % C::SLOTS) * C::HALF_BYTES; };
-  // Staged operands: the covering dwords of each piece and its byte shift.
-  u32x4 va[C::LOADS], vb[C::LOADS];
-  unsigned ea[C::LOADS], eb[C::LOADS], sa_[C::LOADS], sb_[C::LOADS];
+  // Staged operands' pieces between their loads and their LDS writes.
+  typename RingOperand<AMN, ROWS, SRC32>::Staged ra;
+  typename RingOperand<BMN, ROWS, SRC32>::Staged rb;
 
   // With two K groups each group finishes one atom row of its waves' blocks
   // (row grp). On interior tiles that read C it requests those C values
@@ -339,11 +386,17 @@ gemm_ring_kernel(const GemmArgs p) {
   // Prologue: local slice 0 into slots 0 and 1, then A of local slice 1
   // (direct) into slot 2, or local slice 1 (staged) into registers.
   if (NJ > 0) {
-    if (a_dir) a.issue_direct(slot(0), gs(0), w, lane);
-    else a.load_staged(va, ea, sa_, gs(0), w, lane);
-    if (b_dir) b.issue_direct(slot(1), gs(0), w, lane);
-    else b.load_staged(vb, eb, sb_, gs(0), w, lane);
-    if (a_dir && NJ > 1) a.issue_direct(slot(2), gs(1), w, lane);
+    if (a_dir) {
+      if constexpr (!SRC32) a.issue_direct(slot(0), gs(0), w, lane);
+    } else {
+      a.load_staged(ra, gs(0), w, lane);
+    }
+    if (b_dir) {
+      if constexpr (!SRC32) b.issue_direct(slot(1), gs(0), w, lane);
+    } else {
+      b.load_staged(rb, gs(0), w, lane);
+    }
+    if constexpr (!SRC32) { if (a_dir && NJ > 1) a.issue_direct(slot(2), gs(1), w, lane); }
   }
   if constexpr (PRE_C) {
     if (pre_c)
@@ -353,11 +406,11 @@ gemm_ring_kernel(const GemmArgs p) {
   if (NJ > 0) {
     if (staged) {
       pp_wait_vm<0>();
-      if (!a_dir) a.store_staged(slot(0), va, ea, sa_, gs(0), w, lane, a_edge);
-      if (!b_dir) b.store_staged(slot(1), vb, eb, sb_, gs(0), w, lane, b_edge);
+      if (!a_dir) a.store_staged(slot(0), ra, gs(0), w, lane, a_edge, mode);
+      if (!b_dir) b.store_staged(slot(1), rb, gs(0), w, lane, b_edge, mode);
       if (NJ > 1) {
-        if (!a_dir) a.load_staged(va, ea, sa_, gs(1), w, lane);
-        if (!b_dir) b.load_staged(vb, eb, sb_, gs(1), w, lane);
+        if (!a_dir) a.load_staged(ra, gs(1), w, lane);
+        if (!b_dir) b.load_staged(rb, gs(1), w, lane);
       }
       pp_wait_lgkm0();
     } else if (NJ > 1) {
@@ -379,16 +432,18 @@ gemm_ring_kernel(const GemmArgs p) {
       // then request local slice j+2 into the same registers.
       if (staged && j + 1 < NJ) {
         pp_wait_vm<0>();
-        if (!a_dir) a.store_staged(slot(2 * j + 2), va, ea, sa_, gs(j + 1), w, lane, a_edge);
-        if (!b_dir) b.store_staged(slot(2 * j + 3), vb, eb, sb_, gs(j + 1), w, lane, b_edge);
+        if (!a_dir) a.store_staged(slot(2 * j + 2), ra, gs(j + 1), w, lane, a_edge, mode);
+        if (!b_dir) b.store_staged(slot(2 * j + 3), rb, gs(j + 1), w, lane, b_edge, mode);
       }
       // Direct loads into the slots local slice j-1 has left: B of j+1
       // first, then A of j+2 (slot 2j+4, left by B of j-1).
-      if (b_dir && j + 1 < NJ) b.issue_direct(slot(2 * j + 3), gs(j + 1), w, lane);
-      if (a_dir && j + 2 < NJ) a.issue_direct(slot(2 * j + 4), gs(j + 2), w, lane);
+      if constexpr (!SRC32) {
+        if (b_dir && j + 1 < NJ) b.issue_direct(slot(2 * j + 3), gs(j + 1), w, lane);
+        if (a_dir && j + 2 < NJ) a.issue_direct(slot(2 * j + 4), gs(j + 2), w, lane);
+      }
       if (staged && j + 2 < NJ) {
-        if (!a_dir) a.load_staged(va, ea, sa_, gs(j + 2), w, lane);
-        if (!b_dir) b.load_staged(vb, eb, sb_, gs(j + 2), w, lane);
+        if (!a_dir) a.load_staged(ra, gs(j + 2), w, lane);
+        if (!b_dir) b.load_staged(rb, gs(j + 2), w, lane);
       }
 
       // Multiply local slice j (edge waves: only their atoms that hold

@@ -212,17 +212,21 @@ def test_f32_operand_dtypes(lib, monkeypatch):
     assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 pingpong f32->bf16"
     assert _v(lib, M=4096, N=4096, K=4096 + 32, tB=1, dtype=2, beta=1.0, C=D0) == lib.GEMM_OK
     assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 NT epi=acc+c pingpong f32->f16"
-    # otherwise rounded while staged on the masked kernel: other layouts, K not
-    # a multiple of 32, rows not 16-byte aligned
+    # otherwise (other layouts, K not a multiple of 32, rows not 16-byte
+    # aligned) the 128x128 ring kernel stages both operands through registers
+    # and rounds them there; a K tail makes it masked
     for kw in (dict(tB=0), dict(tA=1, tB=1), dict(tB=1, K=8192 + 16),
                dict(tB=1, lda=8192 + 2)):
         args = dict(M=8192, N=8192, K=8192, dtype=lib.GEMM_DTYPE_F32_BF16)
         args.update(kw)
         assert _v(lib, **args) == lib.GEMM_OK
         path = lib.gemm_last_path()
-        # (the 256x256 tile exists only as the two-group kernel for whole
-        # tiles; a call that needs masking takes the 128x128 masked kernel)
-        assert path.startswith("mfma t128x128x64 w2x2") and " masked f32->bf16" in path, (kw, path)
+        masked = " masked" if "K" in kw else ""
+        assert path.startswith("mfma t128x128x64 w2x2 a32x32x16") and path.endswith(
+            f" ring{masked} f32->bf16 staged (A, B: float32 values rounded in registers)"), (kw, path)
+    # large pitches (64-bit addressing) keep the masked general kernel
+    assert _v(lib, M=256, N=256, K=256, tB=1, dtype=3, lda=1 << 22, A=1 << 40) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" masked f32->bf16"), lib.gemm_last_path()
     assert _v(lib, dtype=lib.GEMM_DTYPE_F32_F16) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith("masked f32->f16"), lib.gemm_last_path()
     # pitches count 4-byte elements: 66 floats = 264 B is 8-byte aligned only

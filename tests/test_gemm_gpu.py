@@ -183,9 +183,11 @@ def test_tiled_shapes_narrow_staging(tile, dtype, monkeypatch):
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("dtype", ["f32_f16", "f32_bf16"])
 def test_tiled_shapes_f32_operands(tile, dtype, monkeypatch):
-    """float32 A and B rounded to f16/bf16 (while staged on the masked
-    kernel; as read from LDS on whole NT tiles): every layout, general epilogue, aligned and 8-/4-byte pitches,
-    bases 4 bytes past a 16-byte boundary; NaN in the padding is never read."""
+    """float32 A and B rounded to f16/bf16 (as staged: through registers on
+    the 128x128 ring kernel, on the masked kernel at the other tiles; as read
+    from LDS on whole NT tiles): every layout, general epilogue, aligned and
+    8-/4-byte pitches, bases 4 bytes past a 16-byte boundary; NaN in the
+    padding is never read."""
     monkeypatch.setenv("GEMM_FORCE_TILE", tile)
     seed = 6000
     for (M, N, K) in SHAPES[::2] + [(512, 256, 192)]:
@@ -233,15 +235,49 @@ def test_f32_operands_pingpong(dtype, monkeypatch):
             assert "pingpong f32->" + dtype in r.path and "masked" not in r.path, r.path
             r.check()
             r.check_padding_untouched()
-    # other layouts, K not a multiple of 32, or 8-byte rows: the masked kernel
+    # other layouts, K not a multiple of 32, or 8-byte rows: the 128x128 ring
+    # kernel, both operands staged and rounded in registers
     for (tA, tB, K, ldb) in [(0, 0, 64, None), (1, 1, 64, None), (0, 1, 48, None),
                              (0, 1, 64, 66)]:
         seed += 1
         cfg = workloads.Config(f"f32pp{seed}", 512, 256, K, "f32_" + dtype, tA, tB, 1.0, 0.0,
                                "uniform", seed, ldb=ldb)
         r = run(cfg)
-        assert " masked" in r.path and "pingpong" not in r.path, r.path
+        assert " ring" in r.path and "staged (A, B: float32" in r.path and "pingpong" not in r.path, \
+            r.path
         r.check()
+
+
+@pytest.mark.parametrize("mode", ["shared", "ksplit2"])
+@pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_f32_ring_rounding_bitwise(dtype, tA, tB, mode, monkeypatch):
+    """float32 operands on the 128x128 ring kernel are rounded in registers
+    and written where 16-bit pieces would go: D must equal, bitwise, D of the
+    same ring form fed the operands the oracle rounds (ties of both parities,
+    values one ulp off a tie, subnormals of the 16-bit format), in every
+    layout, with M/N edges that cut a 16-byte piece and a K tail."""
+    monkeypatch.setenv("GEMM_FORCE_TILE", "t128x128x64")
+    monkeypatch.setenv("GEMM_RING_MODE", mode)
+    rng = np.random.default_rng(70 + 2 * tA + tB)
+    M, N, K = 300, 260, 200
+    code = 0 if dtype == "f16" else 1
+    A32 = _tie_heavy_f32((K, M) if tA else (M, K), dtype, rng)
+    B32 = _tie_heavy_f32((N, K) if tB else (K, N), dtype, rng)
+
+    def oracle_rounded(x):
+        bits = oracle.round_f32_bits(x.numpy().reshape(-1), code)
+        return torch.tensor(oracle.decode_bits(bits, code).astype(np.float32).reshape(x.shape))
+
+    cfg32 = workloads.Config("f32ring", M, N, K, "f32_" + dtype, tA, tB, 1.0, 0.0, "uniform", 1)
+    r32 = run(cfg32, workloads.make_inputs(cfg32, A_src=A32, B_src=B32))
+    assert " ring" in r32.path and "staged (A, B: float32" in r32.path, r32.path
+    cfg16 = workloads.Config("f32ring16", M, N, K, dtype, tA, tB, 1.0, 0.0, "uniform", 1)
+    r16 = run(cfg16, workloads.make_inputs(cfg16, A_src=oracle_rounded(A32),
+                                           B_src=oracle_rounded(B32)))
+    assert " ring" in r16.path and (" ring ksplit2" in r16.path) == (mode == "ksplit2"), r16.path
+    assert torch.equal(r32.D, r16.D)
+    r32.check()
 
 
 def _tie_heavy_f32(shape, dtype, rng):
