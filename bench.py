@@ -326,6 +326,9 @@ def bench_i8(args):
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    clock = sustained_clock(step, stream, ms, args.clock_seconds) if args.clock_seconds > 0 else None
+    if clock and "ms_per_step" in clock:
+        clock["tops"] = round(2.0 * M * N * K / (clock["ms_per_step"] * 1e-3) / 1e12, 2)
     ok = None
     if not args.no_check:
         import oracle
@@ -344,7 +347,7 @@ def bench_i8(args):
         "vs_baseline": None, "dtype": "i8", "data": "synthetic (seed 1007; uniform int8)",
         "config": {"workload": "gemm8192_i8_nt", "M": M, "N": N, "K": K, "transA": 0,
                    "transB": 1, "alpha": 1, "beta": 0, "parallelism": "single GPU"},
-        "oracle_bit_exact_sampled_rows": ok, "path": dgt.gemm_last_path(),
+        "oracle_bit_exact_sampled_rows": ok, "path": dgt.gemm_last_path(), "clock": clock,
         "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": PEAK_INT8_TOPS,
                      "unit": "TOP/s", "frac": round(tops / PEAK_INT8_TOPS, 4), "traffic": None},
     }), flush=True)
@@ -376,6 +379,9 @@ def bench_fp8(args):
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    clock = sustained_clock(step, stream, ms, args.clock_seconds) if args.clock_seconds > 0 else None
+    if clock and "ms_per_step" in clock:
+        clock["tflops"] = round(2.0 * M * N * K / (clock["ms_per_step"] * 1e-3) / 1e12, 2)
     max_rel = None
     if not args.no_check:
         import oracle
@@ -396,7 +402,7 @@ def bench_fp8(args):
         "data": "synthetic (seed 1008; uniform over finite E4M3 codes)",
         "config": {"workload": "gemm8192_f8e4m3_nt", "M": M, "N": N, "K": K, "transA": 0,
                    "transB": 1, "alpha": 1.0, "beta": 0.0, "parallelism": "single GPU"},
-        "oracle_max_rel_err": max_rel, "path": dgt.gemm_last_path(),
+        "oracle_max_rel_err": max_rel, "path": dgt.gemm_last_path(), "clock": clock,
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None},
     }), flush=True)

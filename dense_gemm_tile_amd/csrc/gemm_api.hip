@@ -171,7 +171,7 @@ bool byte_pingpong(const GemmByteArgs& b, int transA, int transB) {
   const int t = byte_pp_tile();
   const int64_t ldmax = b.lda > b.ldb ? b.lda : b.ldb;
   return !transA && transB && b.M % t == 0 && b.N % t == 0 && b.K > 0 && b.K % 128 == 0 &&
-         b.a_vec16 && b.b_vec16 && ldmax * t + 4096 < (int64_t{1} << 31);
+         b.a_vec16 && b.b_vec16 && b.cd_vec16 && ldmax * t + 4096 < (int64_t{1} << 31);
 }
 
 void set_byte_tiles(GemmByteArgs& b, int transA, int transB) {
@@ -321,6 +321,8 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     b.read_c = reads_c ? 1 : 0;
     b.a_vec16 = ((uintptr_t)A % 16 == 0 && lda % 16 == 0) ? 1 : 0;
     b.b_vec16 = ((uintptr_t)B % 16 == 0 && ldb % 16 == 0) ? 1 : 0;
+    b.cd_vec16 = ((uintptr_t)D % 16 == 0 && ldd % 4 == 0 &&
+                  (!reads_c || ((uintptr_t)C % 16 == 0 && a.ldc % 4 == 0))) ? 1 : 0;
     set_byte_tiles(b, transA, transB);
     b.group_m = 8;
     if ((int64_t)b.tiles_m * b.tiles_n > 0x7fffffff)
@@ -329,9 +331,10 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     plan.byte_kind = dtype == GEMM_DTYPE_F8_E4M3 ? BYTE_F8E4M3 : BYTE_F8E5M2;
     const char* ops8 = transA ? (transB ? "TT" : "TN") : (transB ? "NT" : "NN");
     const int t8 = b.pingpong ? byte_pp_tile() : byte_tile_m();
-    std::snprintf(buf, sizeof buf, "fp8 %s mfma t%dx%dx128 %s a32x32x64 %s epi=%s%s%s",
+    std::snprintf(buf, sizeof buf, "fp8 %s mfma t%dx%dx128 %s %s %s epi=%s%s%s",
                   dtype == GEMM_DTYPE_F8_E4M3 ? "e4m3" : "e5m2", t8, t8,
-                  b.pingpong ? "w2x4" : "w2x2", ops8, epi_name, b.pingpong ? " pingpong" : "",
+                  b.pingpong ? "w2x4" : "w2x2", b.pingpong ? "a16x16x128" : "a32x32x64", ops8,
+                  epi_name, b.pingpong ? " pingpong" : "",
                   (!b.a_vec16 || !b.b_vec16) ? " bytewise staging" : "");
     g_path = buf;
     return GEMM_OK;
@@ -570,14 +573,17 @@ int plan_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alp
   a.read_c = reads_c ? 1 : 0;
   a.a_vec16 = ((uintptr_t)A % 16 == 0 && lda % 16 == 0) ? 1 : 0;
   a.b_vec16 = ((uintptr_t)B % 16 == 0 && ldb % 16 == 0) ? 1 : 0;
+  a.cd_vec16 = ((uintptr_t)D % 16 == 0 && ldd % 4 == 0 &&
+                (!reads_c || ((uintptr_t)C % 16 == 0 && ldc % 4 == 0))) ? 1 : 0;
   set_byte_tiles(a, transA, transB);
   a.group_m = 8;
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7fffffff)
     return fail(GEMM_ERR_UNSUPPORTED, "too many output tiles for one launch");
   const char* ops = transA ? (transB ? "TT" : "TN") : (transB ? "NT" : "NN");
   const int t8 = a.pingpong ? byte_pp_tile() : byte_tile_m();
-  std::snprintf(buf, sizeof buf, "i8 mfma t%dx%dx128 %s a32x32x32 %s epi=%s%s%s%s", t8, t8,
-                a.pingpong ? "w2x4" : "w2x2", ops, reads_c ? "general" : "beta0",
+  std::snprintf(buf, sizeof buf, "i8 mfma t%dx%dx128 %s %s %s epi=%s%s%s%s", t8, t8,
+                a.pingpong ? "w2x4" : "w2x2", a.pingpong ? "a16x16x64" : "a32x32x32", ops,
+                reads_c ? "general" : "beta0",
                 a.pingpong ? " pingpong" : "",
                 reads_ab ? "" : " (K == 0 or alpha == 0: D = beta*C)",
                 (reads_ab && (!a.a_vec16 || !a.b_vec16)) ? " bytewise staging" : "");

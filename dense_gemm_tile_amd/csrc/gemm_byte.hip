@@ -49,6 +49,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // int8 -> int32 atom: 32 K-values per MFMA, 16 bytes per lane.
 struct KindI8 {
+  static constexpr int ATOM = 32;
   using acc_t = i32x16;
   using frag_t = i32x4;
   static constexpr int KATOM = 32;
@@ -77,6 +78,7 @@ struct KindI8 {
 // lane; block scales of 1 (E8M0 code 127).
 template <int FMT>
 struct KindF8 {
+  static constexpr int ATOM = 32;
   using acc_t = f32x16_t;
   using frag_t = i32x8;
   static constexpr int KATOM = 64;
@@ -103,6 +105,115 @@ struct KindF8 {
   }
 };
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// The two-group kernel's 16x16 atoms (see gemm_mfma_pingpong.h: under the
+// chip's power limit the 16-wide form clocks higher). A lane's fragment is
+// 16 bytes of row (or column) l % 16; D bits are combined from accumulator
+// and C bits as the 32-wide kinds' store() does.
+// int8 -> int32, 16x16x64: K bytes 16 (l / 16) .. +15 of the atom's 64, so a
+// 128-byte LDS row holds two sub-steps (chunk 4 ks + l / 16).
+struct KindI8x16 {
+  static constexpr int ATOM = 16;
+  using acc_t = i32x4;
+  using frag_t = i32x4;
+  static constexpr int KATOM = 64;
+  __device__ static inline frag_t read_off(const char* base, int off, int ks) {
+    return *reinterpret_cast<const i32x4*>(base + (off ^ (ks << 6)));
+  }
+  __device__ static inline acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline unsigned combine(const GemmByteArgs& p, unsigned acc, unsigned c) {
+    unsigned d = (unsigned)p.alpha_i * acc;
+    if (p.read_c) d += (unsigned)p.beta_i * c;
+    return d;
+  }
+};
+// 8-bit float -> f32, 16x16x128 (unit block scales): 32 K bytes per lane,
+// taken as chunks g and g + 4 of the 128-byte row (g = l / 16) instead of 2g
+// and 2g + 1: a K order that A and B share, so the same products are summed,
+// and the chunk pattern of one read is the 16-bit 16x16x32 kernel's, whose
+// swizzle serves it without bank conflicts.
+template <int FMT>
+struct KindF8x16 {
+  static constexpr int ATOM = 16;
+  using acc_t = f32x4;
+  using frag_t = i32x8;
+  static constexpr int KATOM = 128;
+  __device__ static inline frag_t read_off(const char* base, int off, int) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(base + off);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(base + (off ^ 64));  // chunk g ^ 4
+    return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  }
+  __device__ static inline acc_t mma(frag_t a, frag_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, 0, 127, 0, 127);
+  }
+  __device__ static inline unsigned combine(const GemmByteArgs& p, unsigned acc, unsigned c) {
+    float d = p.alpha_f * __builtin_bit_cast(float, acc);
+    if (p.read_c) d = __builtin_fmaf(p.beta_f, __builtin_bit_cast(float, c), d);
+    return __builtin_bit_cast(unsigned, d);
+  }
+};
+
+// Epilogue of a wave's sub-tile of 16x16 atoms on whole tiles with 16-byte
+// C/D rows, two atoms at a time, as store_tile_pairs16 does for the float
+// kernels: after a quad transpose each lane holds 4 consecutive columns of one
+// row per atom; lanes l and l^1 swap one chunk so that every store
+// instruction writes whole 128-byte rows. All C values of a row of atoms are
+// read before its first D store (C may be D).
+template <class Kind, class C>
+__device__ inline void byte_store_pairs16(const GemmByteArgs& p, int r0, int c0,
+                                          typename Kind::acc_t (&acc)[C::TM][C::TN], int lane) {
+  static_assert(Kind::ATOM == 16 && C::TN % 2 == 0, "pairs of 16x16 atoms");
+  constexpr int NP = C::TN / 2;
+  const int odd = lane & 1;
+  const int col = 16 * odd + 4 * ((lane >> 2) & 3);
+  const int rl = 4 * (lane >> 4) + (lane & 3) - odd;
+  const bool c_is_d = p.read_c && p.C == static_cast<const void*>(p.D);
+  const unsigned* Cb = static_cast<const unsigned*>(p.C);
+  unsigned* Db = static_cast<unsigned*>(p.D);
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int r = r0 + 16 * i + rl;
+    u32x4_t cv[NP][2];
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        cv[q][h] = p.read_c ? *reinterpret_cast<const u32x4_t*>(Cb + (int64_t)(r + h) * p.ldc + c0 +
+                                                                  32 * q + col)
+                            : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      // (whole-vector casts: a bit cast of one element of a vector reference
+      // compiled to reads of element 0)
+      const f32x4 xv = __builtin_bit_cast(f32x4, acc[i][2 * q]);
+      const f32x4 yv = __builtin_bit_cast(f32x4, acc[i][2 * q + 1]);
+      float x[4] = {xv[0], xv[1], xv[2], xv[3]};
+      float y[4] = {yv[0], yv[1], yv[2], yv[3]};
+      quad_transpose(x, lane);
+      quad_transpose(y, lane);
+      float w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                             __builtin_bit_cast(int, odd ? x[k] : y[k]), 0xB1,
+                                             0xF, 0xF, false));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4_t o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float v = h == 0 ? (odd ? w[k] : x[k]) : (odd ? y[k] : w[k]);
+          o[k] = Kind::combine(p, __builtin_bit_cast(unsigned, v), cv[q][h][k]);
+        }
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(Db + (int64_t)(r + h) * p.ldd + c0 + 32 * q + col);
+        if (c_is_d) *dst = o;
+        else __builtin_nontemporal_store(o, dst);
+      }
+    }
+  }
+}
 
 // Epilogue of one 32x32 atom whose top-left output element is (r0, c0): lane
 // l's accumulator v is row 8*(v/4) + 4*(l/32) + v%4, column l%32. C (32-bit
@@ -278,12 +389,24 @@ __global__ void __launch_bounds__(kThreads) gemm_byte_kernel(const GemmByteArgs 
 // 1024 cycles.
 template <class Kind>
 struct PpByteFrags {
-  typename Kind::frag_t a[4], b[2];
+  typename Kind::frag_t a[PingPongCfgT<Kind::ATOM>::TM], b[PingPongCfgT<Kind::ATOM>::TN];
 };
+
+// Fragment offset (sub-step 0) of the atom whose first row of the slot is
+// row0: 32-wide kinds take K half l / 32 of a row l % 32 (chunk CHUNK0 *
+// half), 16-wide ones chunk l / 16 of row l % 16, with their swizzles.
+template <class Kind>
+__device__ inline int pp_byte_frag_off(int row0, int lane) {
+  if constexpr (Kind::ATOM == 16)
+    return PpOperand<false, 1, 16>::lds_off(row0 + (lane & 15), lane >> 4);
+  else
+    return lds_off_b(row0 + (lane & 31), Kind::CHUNK0 * (lane >> 5));
+}
 
 template <class Kind>
 __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(const GemmByteArgs p) {
-  using C = PingPongCfg;
+  using C = PingPongCfgT<Kind::ATOM>;
+  using At = typename C::At;
   using acc_t = typename Kind::acc_t;
   constexpr int KS = 128 / Kind::KATOM;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
@@ -295,18 +418,17 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
   schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
 
-  PpOperand<false, C::TM> a;
-  PpOperand<false, C::TN> b;
+  using OpA = PpOperand<false, C::TM, Kind::ATOM>;
+  using OpB = PpOperand<false, C::TN, Kind::ATOM>;
+  OpA a;
+  OpB b;
   a.init_load(p.A, p.lda, m0, lw, lane, 1);
   b.init_load(p.B, p.ldb, n0, lw, lane, 1);
-  const int half = lane >> 5;
   int offA[C::TM], offB[C::TN];  // fragment offsets within a slot, sub-step 0
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-    offA[i] = lds_off_b(wm * C::WTM + 32 * i + (lane & 31), Kind::CHUNK0 * half);
+  for (int i = 0; i < C::TM; ++i) offA[i] = pp_byte_frag_off<Kind>(wm * C::WTM + At::M * i, lane);
 #pragma unroll
-  for (int j = 0; j < C::TN; ++j)
-    offB[j] = lds_off_b(wn * C::WTN + 32 * j + (lane & 31), Kind::CHUNK0 * half);
+  for (int j = 0; j < C::TN; ++j) offB[j] = pp_byte_frag_off<Kind>(wn * C::WTN + At::N * j, lane);
 
   acc_t acc[C::TM][C::TN];
 #pragma unroll
@@ -314,9 +436,9 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
 #pragma unroll
     for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+      for (int v = 0; v < At::NACC; ++v) acc[i][j][v] = 0;
 
-  auto issue = [&](const PpOperand<false, C::TM>& x, int slice, int slot) {
+  auto issue = [&](const OpA& x, int slice, int slot) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) x.issue(smem + slot * C::SLOT_BYTES, lw, i, slice);
   };
@@ -350,8 +472,11 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
   int h = 0;
   for (int s = 0; s < KT; ++s) {
     asm volatile("" : "+v"(a.row), "+v"(a.c0), "+v"(b.row), "+v"(b.c0));
-    asm volatile("" : "+v"(offA[0]), "+v"(offA[1]), "+v"(offA[2]), "+v"(offA[3]),
-                 "+v"(offB[0]), "+v"(offB[1]));
+    if constexpr (Kind::ATOM == 16) asm volatile("" : "+v"(a.c1), "+v"(b.c1));
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) asm volatile("" : "+v"(offA[i]));
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) asm volatile("" : "+v"(offB[j]));
     const int sa = h, sb = h == 4 ? 0 : h + 1;
     const char* pa = smem + sa * C::SLOT_BYTES;
     const char* pb = smem + sb * C::SLOT_BYTES;
@@ -384,19 +509,24 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
   }
   if (group == 0) pp_barrier();
 
+  if constexpr (Kind::ATOM == 16) {
+    byte_store_pairs16<Kind, C>(p, m0 + wm * C::WTM, n0 + wn * C::WTN, acc, lane);
+  } else {
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      epilogue<Kind, false>(p, m0 + wm * C::WTM + 32 * i, n0 + wn * C::WTN + 32 * j, acc[i][j],
-                            lane);
+      for (int j = 0; j < C::TN; ++j)
+        epilogue<Kind, false>(p, m0 + wm * C::WTM + 32 * i, n0 + wn * C::WTN + 32 * j, acc[i][j],
+                              lane);
+  }
 }
 
-template <class Kind>
+// Kind: the 128x128 kernel's 32-wide atom; KindPP: the two-group kernel's.
+template <class Kind, class KindPP>
 hipError_t launch_kind(bool ta, bool tb, const GemmByteArgs& a, hipStream_t s) {
   const dim3 grid(a.tiles_m * a.tiles_n);
   if (a.pingpong)
-    return launch_kernel(gemm_pp_byte_kernel<Kind>, grid, dim3(PingPongCfg::THREADS), s, a);
+    return launch_kernel(gemm_pp_byte_kernel<KindPP>, grid, dim3(PingPongCfg::THREADS), s, a);
   const dim3 block(kThreads);
   if (!ta && tb) return launch_kernel(gemm_byte_kernel<Kind, false, true>, grid, block, s, a);
   if (!ta && !tb) return launch_kernel(gemm_byte_kernel<Kind, false, false>, grid, block, s, a);
@@ -407,9 +537,9 @@ hipError_t launch_kind(bool ta, bool tb, const GemmByteArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_byte(int kind, bool ta, bool tb, const GemmByteArgs& a, hipStream_t s) {
-  if (kind == BYTE_I8) return launch_kind<KindI8>(ta, tb, a, s);
-  if (kind == BYTE_F8E4M3) return launch_kind<KindF8<0>>(ta, tb, a, s);
-  return launch_kind<KindF8<1>>(ta, tb, a, s);
+  if (kind == BYTE_I8) return launch_kind<KindI8, KindI8x16>(ta, tb, a, s);
+  if (kind == BYTE_F8E4M3) return launch_kind<KindF8<0>, KindF8x16<0>>(ta, tb, a, s);
+  return launch_kind<KindF8<1>, KindF8x16<1>>(ta, tb, a, s);
 }
 
 int byte_tile_m() { return kBM; }

@@ -267,6 +267,21 @@ def test_fp8_dtypes_take_the_byte_kernel(lib, monkeypatch):
     assert _v(lib, dtype=5) == lib.GEMM_ERR_UNSUPPORTED
 
 
+def test_byte_two_group_kernel_needs_16_byte_cd_rows(lib):
+    # whole 256x256 NT tiles take the two-group kernel on 16-wide atoms, whose
+    # epilogue stores 16 bytes per lane: D (and C when read) need 16-byte rows
+    assert _v8(lib, M=512, N=512, K=256, tB=1) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "i8 mfma t256x256x128 w2x4 a16x16x64 NT epi=beta0 pingpong"
+    assert _v(lib, M=512, N=512, K=256, tB=1, dtype=lib.GEMM_DTYPE_F8_E4M3) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "fp8 e4m3 mfma t256x256x128 w2x4 a16x16x128 NT epi=beta0 pingpong"
+    assert _v8(lib, M=512, N=512, K=256, tB=1, ldd=514) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "i8 mfma t128x128x128 w2x2 a32x32x32 NT epi=beta0"
+    assert _v8(lib, M=512, N=512, K=256, tB=1, beta=1, C=D0, ldc=512) == lib.GEMM_OK
+    assert "pingpong" in lib.gemm_last_path()
+    assert _v8(lib, M=512, N=512, K=256, tB=1, beta=1, C=C0 + 4, ldc=512) == lib.GEMM_OK
+    assert "pingpong" not in lib.gemm_last_path()
+
+
 def test_i8_form_checks_and_paths(lib):
     assert _v8(lib, tB=1) == lib.GEMM_OK
     assert lib.gemm_last_path() == "i8 mfma t128x128x128 w2x2 a32x32x32 NT epi=beta0"
