@@ -165,17 +165,18 @@ int choose_tile(int64_t M, int64_t N, int64_t K) {
   return TILE_64x64;
 }
 
-// Whole 256x256 NT tiles of a 1-byte-operand call take the two-group kernel
-// (K a multiple of its 128-byte slices, 16-byte rows, 32-bit load offsets).
-bool byte_pingpong(const GemmByteArgs& b, int transA, int transB) {
+// Whole 256x256 tiles of a 1-byte-operand call, in any layout, take the
+// two-group kernel (K a multiple of its 128-byte slices, 16-byte operand and
+// C/D rows, 32-bit load offsets).
+bool byte_pingpong(const GemmByteArgs& b) {
   const int t = byte_pp_tile();
   const int64_t ldmax = b.lda > b.ldb ? b.lda : b.ldb;
-  return !transA && transB && b.M % t == 0 && b.N % t == 0 && b.K > 0 && b.K % 128 == 0 &&
-         b.a_vec16 && b.b_vec16 && b.cd_vec16 && ldmax * t + 4096 < (int64_t{1} << 31);
+  return b.M % t == 0 && b.N % t == 0 && b.K > 0 && b.K % 128 == 0 && b.a_vec16 && b.b_vec16 &&
+         b.cd_vec16 && ldmax * t + 4096 < (int64_t{1} << 31);
 }
 
 void set_byte_tiles(GemmByteArgs& b, int transA, int transB) {
-  b.pingpong = byte_pingpong(b, transA, transB) ? 1 : 0;
+  b.pingpong = byte_pingpong(b) ? 1 : 0;
   const int tm = b.pingpong ? byte_pp_tile() : byte_tile_m();
   const int tn = b.pingpong ? byte_pp_tile() : byte_tile_n();
   b.tiles_m = (int)((b.M + tm - 1) / tm);

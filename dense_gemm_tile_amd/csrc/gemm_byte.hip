@@ -32,6 +32,7 @@
 #include "gemm_mfma_pingpong.h"
 
 #include <cstdint>
+#include <type_traits>
 
 namespace dgt {
 
@@ -106,6 +107,17 @@ struct KindF8 {
 };
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
+typedef int v2i __attribute__((ext_vector_type(2)));
+// ds_read_b64_tr_b8 (lane layout measured with an in-bounds probe): within
+// each group of 16 lanes, lane t receives byte t % 8 of the 8-byte blocks
+// named by lanes 2b + t / 8, b = 0 .. 7. Lane 2b + h naming K-row k0 + b,
+// columns c0 + 8h .. +7 gives lane t the 8 consecutive K-values k0 .. k0+7
+// of column c0 + t.
+__device__ inline v2i ds_read_tr8(const char* p) {
+  typedef __attribute__((address_space(3))) v2i lds_v2i;
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p));
+}
+
 // The two-group kernel's 16x16 atoms (see gemm_mfma_pingpong.h: under the
 // chip's power limit the 16-wide form clocks higher). A lane's fragment is
 // 16 bytes of row (or column) l % 16; D bits are combined from accumulator
@@ -122,6 +134,13 @@ struct KindI8x16 {
   }
   __device__ static inline acc_t mma(frag_t a, frag_t b, acc_t c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+  }
+  // M/N-contiguous slot (K-rows of 256 bytes): two transposed reads, K-rows
+  // k .. k+7 and k+8 .. k+15 of the lane's column; sub-step ks is 64 rows on.
+  __device__ static inline frag_t read_mn(const char* q, int ks) {
+    const char* r = q + ks * 64 * 256;
+    const v2i lo = ds_read_tr8(r), hi = ds_read_tr8(r + 8 * 256);
+    return frag_t{lo.x, lo.y, hi.x, hi.y};
   }
   __device__ static inline unsigned combine(const GemmByteArgs& p, unsigned acc, unsigned c) {
     unsigned d = (unsigned)p.alpha_i * acc;
@@ -147,6 +166,13 @@ struct KindF8x16 {
   }
   __device__ static inline acc_t mma(frag_t a, frag_t b, acc_t c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, 0, 127, 0, 127);
+  }
+  // M/N-contiguous slot: K-rows 16g .. +15 and 16g + 64 .. +15 of the lane's
+  // column (the same K order as read_off), four transposed reads.
+  __device__ static inline frag_t read_mn(const char* q, int) {
+    const v2i a = ds_read_tr8(q), b = ds_read_tr8(q + 8 * 256);
+    const v2i c = ds_read_tr8(q + 64 * 256), d = ds_read_tr8(q + 72 * 256);
+    return frag_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
   }
   __device__ static inline unsigned combine(const GemmByteArgs& p, unsigned acc, unsigned c) {
     float d = p.alpha_f * __builtin_bit_cast(float, acc);
@@ -387,6 +413,50 @@ __global__ void __launch_bounds__(kThreads) gemm_byte_kernel(const GemmByteArgs 
 // A slice is 4 int8 or 2 fp8 sub-steps of 8 MFMAs per wave, each MFMA twice
 // the 16-bit one's work at twice its rate, so a compute phase stays about
 // 1024 cycles.
+// An M/N-contiguous 1-byte operand of the two-group kernel (A stored [K][M]
+// or B stored [K][N]): a slot is 128 K-rows of 256 bytes (the tile's 256
+// M or N values); chunk c (16 bytes) of row r sits at c ^ s(r),
+// s(r) = (r & 7) ^ 8 r4. A transposed read touches 8 consecutive rows of one
+// chunk per 16 lanes (rows 16g .. 16g + 7 for lane group g); the swizzle puts
+// those 8 rows, and the next group's, on all 64 banks. Instruction i of wave
+// lw fills K-rows 32 lw + 4i .. +3, lane l chunk slot l % 16 of row
+// 32 lw + 4i + l / 16.
+template <int NFRAG>
+struct PpByteMN {
+  const char* base;  // tile's first column (M or N index), K = 0
+  int64_t ld;        // row pitch in bytes
+  int voff[4];       // by i & 1 and i >= 4 (they set r & 7 and bit 4 of r)
+  int off[NFRAG];    // transposed-read offset of each atom, sub-step 0
+
+  __device__ static inline int swz(int r) { return (r & 7) ^ (8 * ((r >> 4) & 1)); }
+  __device__ inline void init_load(const void* X, int64_t ld_, int c0, int lw, int lane) {
+    base = static_cast<const char*>(X) + c0;
+    ld = ld_;
+    const int rsub = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      voff[q] = (int)((32 * lw + rsub) * ld) + ((p ^ swz(4 * (q & 1) + rsub + 16 * (q >> 1))) << 4);
+  }
+  __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
+    // the slice's first K-row is folded into the resource base
+    const char* b = base + (int64_t)slice * 128 * ld;
+    const int q = (i & 1) | ((i >= 4) << 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(b), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
+                                             16, voff[q], (int)(4 * i * ld), 0, 0);
+  }
+  // Lane l (group g = l / 16, t = l % 16) names K-row k = 16 g + t / 2,
+  // columns col0 + 8 (t & 1) .. +7 of atom t's 16 columns.
+  __device__ inline void init_read(int col0, int lane) {
+    const int g = lane >> 4, t = lane & 15;
+    const int k = 16 * g + (t >> 1);
+#pragma unroll
+    for (int a = 0; a < NFRAG; ++a) {
+      const int col = col0 + 16 * a;
+      off[a] = k * 256 + (((col >> 4) ^ swz(k)) << 4) + 8 * (t & 1);
+    }
+  }
+};
+
 template <class Kind>
 struct PpByteFrags {
   typename Kind::frag_t a[PingPongCfgT<Kind::ATOM>::TM], b[PingPongCfgT<Kind::ATOM>::TN];
@@ -403,8 +473,10 @@ __device__ inline int pp_byte_frag_off(int row0, int lane) {
     return lds_off_b(row0 + (lane & 31), Kind::CHUNK0 * (lane >> 5));
 }
 
-template <class Kind>
+// AMN / BMN: A stored [K][M] / B stored [K][N] (16-wide kinds only).
+template <class Kind, bool AMN, bool BMN>
 __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(const GemmByteArgs p) {
+  static_assert(Kind::ATOM == 16 || (!AMN && !BMN), "M/N-contiguous operands use 16-wide atoms");
   using C = PingPongCfgT<Kind::ATOM>;
   using At = typename C::At;
   using acc_t = typename Kind::acc_t;
@@ -418,17 +490,39 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
   schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
 
-  using OpA = PpOperand<false, C::TM, Kind::ATOM>;
-  using OpB = PpOperand<false, C::TN, Kind::ATOM>;
+  using OpA = std::conditional_t<AMN, PpByteMN<C::TM>, PpOperand<false, C::TM, Kind::ATOM>>;
+  using OpB = std::conditional_t<BMN, PpByteMN<C::TN>, PpOperand<false, C::TN, Kind::ATOM>>;
   OpA a;
   OpB b;
-  a.init_load(p.A, p.lda, m0, lw, lane, 1);
-  b.init_load(p.B, p.ldb, n0, lw, lane, 1);
   int offA[C::TM], offB[C::TN];  // fragment offsets within a slot, sub-step 0
+  if constexpr (AMN) {
+    a.init_load(p.A, p.lda, m0, lw, lane);
+    a.init_read(wm * C::WTM, lane);
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) offA[i] = pp_byte_frag_off<Kind>(wm * C::WTM + At::M * i, lane);
+    for (int i = 0; i < C::TM; ++i) offA[i] = a.off[i];
+  } else {
+    a.init_load(p.A, p.lda, m0, lw, lane, 1);
 #pragma unroll
-  for (int j = 0; j < C::TN; ++j) offB[j] = pp_byte_frag_off<Kind>(wn * C::WTN + At::N * j, lane);
+    for (int i = 0; i < C::TM; ++i) offA[i] = pp_byte_frag_off<Kind>(wm * C::WTM + At::M * i, lane);
+  }
+  if constexpr (BMN) {
+    b.init_load(p.B, p.ldb, n0, lw, lane);
+    b.init_read(wn * C::WTN, lane);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) offB[j] = b.off[j];
+  } else {
+    b.init_load(p.B, p.ldb, n0, lw, lane, 1);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) offB[j] = pp_byte_frag_off<Kind>(wn * C::WTN + At::N * j, lane);
+  }
+  auto read_a = [&](const char* slot, int i, int ks) {
+    if constexpr (AMN) return Kind::read_mn(slot + offA[i], ks);
+    else return Kind::read_off(slot, offA[i], ks);
+  };
+  auto read_b = [&](const char* slot, int j, int ks) {
+    if constexpr (BMN) return Kind::read_mn(slot + offB[j], ks);
+    else return Kind::read_off(slot, offB[j], ks);
+  };
 
   acc_t acc[C::TM][C::TN];
 #pragma unroll
@@ -471,8 +565,18 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
   PpByteFrags<Kind> f[KS];
   int h = 0;
   for (int s = 0; s < KT; ++s) {
-    asm volatile("" : "+v"(a.row), "+v"(a.c0), "+v"(b.row), "+v"(b.c0));
-    if constexpr (Kind::ATOM == 16) asm volatile("" : "+v"(a.c1), "+v"(b.c1));
+    if constexpr (AMN) {
+      asm volatile("" : "+v"(a.voff[0]), "+v"(a.voff[1]), "+v"(a.voff[2]), "+v"(a.voff[3]));
+    } else {
+      asm volatile("" : "+v"(a.row), "+v"(a.c0));
+      if constexpr (Kind::ATOM == 16) asm volatile("" : "+v"(a.c1));
+    }
+    if constexpr (BMN) {
+      asm volatile("" : "+v"(b.voff[0]), "+v"(b.voff[1]), "+v"(b.voff[2]), "+v"(b.voff[3]));
+    } else {
+      asm volatile("" : "+v"(b.row), "+v"(b.c0));
+      if constexpr (Kind::ATOM == 16) asm volatile("" : "+v"(b.c1));
+    }
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) asm volatile("" : "+v"(offA[i]));
 #pragma unroll
@@ -483,9 +587,9 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i) f[ks].a[i] = Kind::read_off(pa, offA[i], ks);
+      for (int i = 0; i < C::TM; ++i) f[ks].a[i] = read_a(pa, i, ks);
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) f[ks].b[j] = Kind::read_off(pb, offB[j], ks);
+      for (int j = 0; j < C::TN; ++j) f[ks].b[j] = read_b(pb, j, ks);
     }
     if (group == 0) {
       if (s + 1 < KT) issue_b(s + 1, h >= 2 ? h - 2 : h + 3);
@@ -525,8 +629,14 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
 template <class Kind, class KindPP>
 hipError_t launch_kind(bool ta, bool tb, const GemmByteArgs& a, hipStream_t s) {
   const dim3 grid(a.tiles_m * a.tiles_n);
-  if (a.pingpong)
-    return launch_kernel(gemm_pp_byte_kernel<KindPP>, grid, dim3(PingPongCfg::THREADS), s, a);
+  if (a.pingpong) {
+    const dim3 block(PingPongCfg::THREADS);
+    // A is M-contiguous when stored transposed; B is N-contiguous when not.
+    if (!ta && tb) return launch_kernel(gemm_pp_byte_kernel<KindPP, false, false>, grid, block, s, a);
+    if (!ta && !tb) return launch_kernel(gemm_pp_byte_kernel<KindPP, false, true>, grid, block, s, a);
+    if (ta && tb) return launch_kernel(gemm_pp_byte_kernel<KindPP, true, false>, grid, block, s, a);
+    return launch_kernel(gemm_pp_byte_kernel<KindPP, true, true>, grid, block, s, a);
+  }
   const dim3 block(kThreads);
   if (!ta && tb) return launch_kernel(gemm_byte_kernel<Kind, false, true>, grid, block, s, a);
   if (!ta && !tb) return launch_kernel(gemm_byte_kernel<Kind, false, false>, grid, block, s, a);

@@ -119,32 +119,38 @@ def test_fp8_full_size_sampled_rows():
     assert oracle.check(D[rows].cpu().numpy().astype(np.float64), D_ref, bound)["ok"]
 
 
+@pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 1), (1, 0)])
 @pytest.mark.parametrize("dt", ["f8e4m3", "f8e5m2"])
-def test_fp8_pingpong_whole_tiles_slice_counts(dt):
-    """Whole 256x256 NT tiles take the two-group kernel: K from one 128-byte
-    slice to several turns of the five-slot ring, padded leading dimensions."""
-    seed = 950
+def test_fp8_pingpong_whole_tiles_slice_counts(dt, tA, tB):
+    """Whole 256x256 tiles take the two-group kernel in every layout: K from
+    one 128-byte slice to several turns of the five-slot ring, padded leading
+    dimensions."""
+    seed = 950 + 20 * (2 * tA + tB)
     for K in (128, 256, 384, 640, 1152):
         seed += 1
         M, N = 512, 768
-        lda, ldb = K + (16 if seed % 2 else 0), K + 32
-        D, D_ref, bound, path = run_fp8(dt, M, N, K, 0, 1, 0.5, -1.0, seed=seed, lda=lda,
+        lda = (M if tA else K) + (16 if seed % 2 else 0)
+        ldb = (K if tB else N) + 32
+        D, D_ref, bound, path = run_fp8(dt, M, N, K, tA, tB, 0.5, -1.0, seed=seed, lda=lda,
                                         ldb=ldb, ldd=N + 4)
-        assert "pingpong" in path, path
+        assert "pingpong" in path and " a16x16x128 " in path, path
         assert oracle.check(D[:M, :N].astype(np.float64), D_ref, bound)["ok"], (dt, K)
         assert np.all(D[:M, N:].view(np.uint32) == D_SENTINEL)
 
 
-def test_fp8_pingpong_exact_small_integers():
-    rng = np.random.default_rng(8)
+@pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 1), (1, 0)])
+def test_fp8_pingpong_exact_small_integers(tA, tB):
+    """Small integers are exact in E4M3 and their sums exact in f32, so D
+    must equal the integer product bitwise in every layout."""
+    rng = np.random.default_rng(8 + 2 * tA + tB)
     M, N, K = 256, 512, 384
     table = {-2: 0xC0, -1: 0xB8, 0: 0x00, 1: 0x38, 2: 0x40}
     av = rng.integers(-2, 3, (M, K))
     bv = rng.integers(-2, 3, (N, K))
     enc = np.vectorize(lambda v: table[int(v)])
-    A = torch.from_numpy(enc(av).astype(np.uint8))
-    B = torch.from_numpy(enc(bv).astype(np.uint8))
-    D, _, _, path = run_fp8("f8e4m3", M, N, K, 0, 1, 1.0, 0.0, A=A, B=B)
+    A = torch.from_numpy(np.ascontiguousarray(enc(av.T if tA else av).astype(np.uint8)))
+    B = torch.from_numpy(np.ascontiguousarray(enc(bv if tB else bv.T).astype(np.uint8)))
+    D, _, _, path = run_fp8("f8e4m3", M, N, K, tA, tB, 1.0, 0.0, A=A, B=B)
     assert "pingpong" in path, path
     assert np.array_equal(D[:M, :N], (av @ bv.T).astype(np.float32))
 
@@ -153,12 +159,13 @@ def test_fp8_pingpong_exact_small_integers():
 def test_fp8_inplace_c_is_d(dt):
     """D may be C itself: each element of C is read before the same lane
     writes D there. Both the 128x128 kernel (a ragged shape) and the
-    two-group kernel (whole 256x256 NT tiles) are run with C == D and a
+    two-group kernel (whole 256x256 tiles, two layouts) are run with C == D and a
     general epilogue, against the oracle on the original C."""
-    for (M, N, K, tA, tB) in [(300, 129, 520, 1, 0), (512, 768, 384, 0, 1)]:
-        D, D_ref, bound, path = run_fp8(dt, M, N, K, tA, tB, 1.5, -0.75, seed=970 + M,
+    for (M, N, K, tA, tB) in [(300, 129, 520, 1, 0), (512, 768, 384, 0, 1),
+                              (512, 768, 384, 1, 0)]:
+        D, D_ref, bound, path = run_fp8(dt, M, N, K, tA, tB, 1.5, -0.75, seed=970 + M + tA,
                                         inplace=True)
-        if (tA, tB) == (0, 1):
+        if M == 512:
             assert "pingpong" in path, path
         else:
             assert "pingpong" not in path, path

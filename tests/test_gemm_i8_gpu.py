@@ -122,29 +122,56 @@ def test_i8_full_size_sampled_rows():
     assert np.array_equal(got, ref)
 
 
-def test_i8_pingpong_whole_tiles_slice_counts():
-    """Whole 256x256 NT tiles take the two-group kernel: K from one 128-byte
-    slice (prologue only) to several turns of the five-slot ring, padded
-    leading dimensions, both epilogues; bit-exact."""
-    seed = 900
+@pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 1), (1, 0)])
+def test_i8_pingpong_whole_tiles_slice_counts(tA, tB):
+    """Whole 256x256 tiles take the two-group kernel in every layout (K-
+    contiguous operands read with ds_read_b128, M/N-contiguous ones with
+    transposed ds_read_b64_tr_b8): K from one 128-byte slice (prologue only)
+    to several turns of the five-slot ring, padded leading dimensions, both
+    epilogues; bit-exact."""
+    seed = 900 + 40 * (2 * tA + tB)
     for K in (128, 256, 384, 512, 640, 1152):
         for alpha, beta in [(1, 0), (-7, 3)]:
             seed += 1
             M, N = 512, 768
-            lda, ldb = K + (16 if seed % 2 else 0), K + (32 if seed % 3 == 0 else 0)
-            got, ref, path = run_i8(M, N, K, 0, 1, alpha, beta, seed=seed, lda=lda, ldb=ldb,
+            lda = (M if tA else K) + (16 if seed % 2 else 0)
+            ldb = (K if tB else N) + (32 if seed % 3 == 0 else 0)
+            got, ref, path = run_i8(M, N, K, tA, tB, alpha, beta, seed=seed, lda=lda, ldb=ldb,
                                     ldd=N + 4)
-            assert "pingpong" in path, path
+            assert "pingpong" in path and " a16x16x64 " in path, path
             assert np.array_equal(got[:M, :N], ref), (K, alpha, beta)
             assert np.all(got[:M, N:] == SENTINEL)
 
 
+@pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 1), (1, 0)])
+def test_i8_pingpong_permutations_pin_layouts(tA, tB):
+    """P @ X and X @ Q with int8 X: every element lands in a known place, so a
+    wrong lane, swizzle or transposed-read position in either operand shows
+    up; bit-exact against the oracle."""
+    rng = np.random.default_rng(60 + 2 * tA + tB)
+    M = N = K = 256
+    X = rng.integers(-128, 128, (M, N)).astype(np.int8)
+    P = np.eye(M, dtype=np.int8)[rng.permutation(M)]
+    Q = np.eye(N, dtype=np.int8)[:, rng.permutation(N)]
+    for Am, Bm in [(P, X), (X, Q)]:
+        As = np.ascontiguousarray(Am.T if tA else Am).reshape(-1)
+        Bs = np.ascontiguousarray(Bm.T if tB else Bm).reshape(-1)
+        got, ref, path = run_i8(M, N, K, tA, tB, 1, 0, A=As, B=Bs)
+        assert "pingpong" in path, path
+        assert np.array_equal(got[:M, :N], ref)
+        assert np.array_equal(got[:M, :N], (Am.astype(np.int32) @ Bm.astype(np.int32)))
+
+
 def test_i8_inplace_c_is_d_on_both_kernels():
     """C == D with a general epilogue on the two-group kernel (whole 256x256
-    NT tiles) and on the 128x128 kernel (other layouts), bit-exact."""
+    tiles, two layouts) and on the 128x128 kernel (a ragged shape),
+    bit-exact."""
     got, ref, path = run_i8(512, 768, 640, 0, 1, -3, 2, seed=930, inplace=True)
     assert "pingpong" in path, path
     assert np.array_equal(got[:512, :768], ref)
     got, ref, path = run_i8(512, 768, 640, 1, 0, 5, -1, seed=931, inplace=True)
-    assert "pingpong" not in path, path
+    assert "pingpong" in path, path
     assert np.array_equal(got[:512, :768], ref)
+    got, ref, path = run_i8(300, 200, 520, 1, 0, 5, -1, seed=932, inplace=True)
+    assert "pingpong" not in path, path
+    assert np.array_equal(got[:300, :200], ref)
