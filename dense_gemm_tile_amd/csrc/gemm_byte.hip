@@ -601,12 +601,17 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
       else pp_wait_vm_lgkm0<0>();
     }
     pp_barrier();
+    // The K sub-steps of one accumulator back to back, as in the 16-bit
+    // kernel (an MFMA that takes the previous one's output as its accumulator
+    // issues faster than one that reads another accumulator).
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i)
+      for (int j = 0; j < C::TN; ++j) {
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = Kind::mma(f[ks].a[i], f[ks].b[j], acc[i][j]);
+        for (int ks = 0; ks < KS; ++ks) acc[i][j] = Kind::mma(f[ks].a[i], f[ks].b[j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     if (group == 0) pp_wait_vm<0>();
     pp_barrier();
     h = h >= 3 ? h - 3 : h + 2;
