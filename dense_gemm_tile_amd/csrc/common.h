@@ -44,6 +44,9 @@ enum RingMode : int {
   RING_KSPLIT2 = 1,  // two K groups of 4 waves per workgroup, a ring each
   RING_DEEP = 2,     // ten half-slots (160 KiB), slices requested four ahead;
                      //    both operands loaded straight into LDS
+  RING_PP = 3,       // two wave groups taking turns, five half-slots (80 KiB);
+                     //    both operands loaded straight into LDS
+  RING_PP_DEEP = 4,  // the same with ten half-slots (160 KiB), loads further ahead
 };
 
 // Arguments of the 1-byte-operand kernels (see gemm_byte.hip): int8 ->

@@ -48,13 +48,18 @@ const std::string& current_path() {
     if (m.ti->kg > 1) std::snprintf(ksplit, sizeof ksplit, " ksplit%d", m.ti->kg);
     const bool a16 = m.atom == 16;
     std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s%s%s%s%s%s%s",
-                  m.ti->name, m.ti->waves_m, m.pingpong ? 4 : m.ti->waves_n,
+                  m.ti->name, m.ti->waves_m,
+                  m.pingpong || (m.ring && (m.ring_mode == RING_PP || m.ring_mode == RING_PP_DEEP))
+                      ? 4
+                      : m.ti->waves_n,
                   a16 ? 16 : m.ti->atom_m, a16 ? 16 : m.ti->atom_n, a16 ? 32 : m.ti->atom_k,
                   m.ops, m.epi, ksplit,
                   m.pingpong ? " pingpong" : "",
                   !m.ring ? ""
                   : m.ring_mode == RING_KSPLIT2 ? " ring ksplit2"
-                  : m.ring_mode == RING_DEEP ? " ring deep" : " ring",
+                  : m.ring_mode == RING_DEEP ? " ring deep"
+                  : m.ring_mode == RING_PP ? " ring two-group"
+                  : m.ring_mode == RING_PP_DEEP ? " ring two-group deep" : " ring",
                   m.masked ? " masked" : "", m.k16_tail ? " k16-tail" : "", m.src32,
                   m.elem_reason.empty() ? "" : " narrow staging (", m.elem_reason.c_str(),
                   m.elem_reason.empty() ? "" : ")",
@@ -465,24 +470,36 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     elem_reason.clear();
     // "masked": edge tiles or a K tail (the ring kernel masks in place)
     plan.masked = (M % ti.bm) || (N % ti.bn) || (K % ti.bk);
-    // Grids of at most one tile per CU: the deep ring (every slice requested
-    // four slices ahead from 160 KiB of LDS) when both operands go straight
-    // into LDS, else K split over two wave groups per workgroup (8 waves,
-    // two rings), so that each SIMD still alternates between two waves.
-    // Larger grids: one group per workgroup, two workgroups per CU.
+    // Both operands straight into LDS: two wave groups taking turns (five
+    // half-slots, two workgroups per CU) on grids of more than one tile per
+    // CU; on smaller grids the deep ring (one wave per SIMD, every slice
+    // requested four ahead from 160 KiB) when B is K-contiguous, else the
+    // two-group form with ten half-slots, whose second wave per SIMD hides
+    // the transposed B reads (measured on 2048^3 and 4096x1024x1024 in all
+    // four layouts). A staged operand: K split over two wave groups per
+    // workgroup (8 waves, two rings) on small grids, so that each SIMD still
+    // alternates between two waves; one group per workgroup and two
+    // workgroups per CU beyond.
     const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
-    a.ring_mode = ntiles > 256 ? RING_SHARED
-                  : (a.a_direct && a.b_direct) ? RING_DEEP : RING_KSPLIT2;
+    const bool both_direct = a.a_direct && a.b_direct;
+    a.ring_mode = ntiles > 256 ? (both_direct ? RING_PP : RING_SHARED)
+                  : !both_direct ? RING_KSPLIT2
+                  : transB ? RING_DEEP : RING_PP_DEEP;
     if (const char* rm = g_env.ring_mode) {
       if (std::strcmp(rm, "shared") == 0) a.ring_mode = RING_SHARED;
       else if (std::strcmp(rm, "ksplit2") == 0) a.ring_mode = RING_KSPLIT2;
       else if (std::strcmp(rm, "deep") == 0 && a.a_direct && a.b_direct) a.ring_mode = RING_DEEP;
-      else if (std::strcmp(rm, "deep") == 0)
-        return fail(GEMM_ERR_UNSUPPORTED,
-                    "GEMM_RING_MODE=deep needs both operands loaded straight into LDS");
+      else if (std::strcmp(rm, "pp") == 0 && a.a_direct && a.b_direct) a.ring_mode = RING_PP;
+      else if (std::strcmp(rm, "ppdeep") == 0 && a.a_direct && a.b_direct)
+        a.ring_mode = RING_PP_DEEP;
+      else if (std::strcmp(rm, "deep") == 0 || std::strcmp(rm, "pp") == 0 ||
+               std::strcmp(rm, "ppdeep") == 0)
+        return fail(GEMM_ERR_UNSUPPORTED, std::string("GEMM_RING_MODE=") + rm +
+                                              " needs both operands loaded straight into LDS");
       else
         return fail(GEMM_ERR_INVALID_ARG,
-                    std::string("GEMM_RING_MODE must be shared, ksplit2 or deep, got ") + rm);
+                    std::string("GEMM_RING_MODE must be shared, ksplit2, deep, pp or ppdeep, got ") +
+                        rm);
     }
   }
   // A last K step whose valid part ends within the first half of a 16x16x32

@@ -154,6 +154,148 @@ gemm_ring128_deep_kernel(const GemmArgs p) {
   else store_tile<C, EPI, true>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane);
 }
 
+// Two wave groups taking turns on 128x128 tiles, both operands loaded
+// straight into LDS: the phase design of the 256x256 two-group kernel
+// (gemm_mfma_pingpong.h) at the ring's slot geometry. Eight waves; group g
+// owns rows [64g, 64g+64) of the tile, wave w of the group the 32 columns
+// [32w, 32w+32): 2x1 atoms of 32x32x16, 32 accumulator registers. With one
+// wave of each group per SIMD, one wave multiplies a slice while the other
+// reads the next slice's fragments and issues loads, so the matrix cores do
+// not stop for the loads' waits and barriers as they do with one wave per
+// SIMD.
+//
+// A of slice t lives in half-slot 2t % SLOTS, B in (2t+1) % SLOTS. Group 1
+// loads A of slice s+AA in its memory phase for slice s, group 0 B of slice
+// s+BA in its own: five half-slots (80 KiB, two workgroups per CU) with
+// AA = 2, BA = 1, or, for grids of at most one tile per CU, ten (160 KiB)
+// with AA = 4, BA = 3. Each refill goes into the slots of a slice whose last
+// reader finished at least one phase earlier (A of s+AA replaces A of s+AA-
+// SLOTS/2, read last in phase 2s; B of s+BA replaces B of s+BA-SLOTS/2, read
+// last by phase 2s), and each group waits for its own loads of slice s+1
+// before the barrier that ends phase 2s+2, after which slice s+1 is read.
+// Edges: pieces outside the operands read as zeros (the ring operand's
+// out-of-range offsets), D is stored with bounds checks.
+struct Pp128Wave {  // the epilogue's view of a wave's 64x32 block
+  using At = Atom<32>;
+  static constexpr int TM = 2, TN = 1;
+};
+
+// s_waitcnt vmcnt(n * LOADS) and lgkmcnt(0) for a run-time n in 0..3.
+template <int LOADS>
+__device__ __forceinline__ void pp128_wait_slices(int n) {
+  if (n >= 3) pp_wait_vm_lgkm0<3 * LOADS>();
+  else if (n == 2) pp_wait_vm_lgkm0<2 * LOADS>();
+  else if (n == 1) pp_wait_vm_lgkm0<LOADS>();
+  else pp_wait_vm_lgkm0<0>();
+}
+
+template <class Tag, int EPI, bool AMN, bool BMN, bool DEEP>
+__global__ void __launch_bounds__(2 * Ring128Cfg::THREADS, DEEP ? 1 : 2)
+gemm_pp128_kernel(const GemmArgs p) {
+  using C = Ring128Cfg;
+  using At = typename C::At;
+  using acc_t = typename At::acc_t;
+  constexpr int SLOTS = DEEP ? 10 : 5, AA = DEEP ? 4 : 2, BA = DEEP ? 3 : 1;
+  static_assert(AA - 1 <= 3 && BA - 1 <= 3, "pp128_wait_slices counts up to three slices");
+  __shared__ __attribute__((aligned(1024))) char smem[SLOTS * C::HALF_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int group = wave >> 2, w = wave & 3;
+  int tm, tn;
+  schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+
+  RingOperand<AMN, 128> a;
+  RingOperand<BMN, 128> b;
+  a.init(p.A, p.lda, m0, p.M, p.K, group, lane);  // atoms at rows 64 group + 32 t
+  b.init(p.B, p.ldb, n0, p.N, p.K, w >> 1, lane);  // atoms at columns 64 (w/2) + 32 t
+  const int boff = (w & 1) ? b.off[1] : b.off[0];  // this wave's columns 32 w .. +31
+
+  acc_t acc[2][1];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < At::NACC; ++v) acc[i][0][v] = 0.0f;
+
+  const int KT = (p.K + C::BK - 1) / C::BK;
+  auto slot = [&](int h) { return smem + (h % SLOTS) * C::HALF_BYTES; };
+  // Loads of this group issued after its loads of slice t, when the last
+  // slice requested so far is `last` (in slices, at most three).
+  auto after = [](int t, int last) { return last - t < 0 ? 0 : last - t; };
+  // Prologue: group 1 requests A of slices 0 .. AA-1, group 0 B of slices
+  // 0 .. BA-1; group 1 then waits one more barrier, which puts it a phase
+  // behind.
+  int alast = -1, blast = -1;
+  if (group == 1) {
+    for (int t = 0; t < AA && t < KT; ++t) a.issue_direct(slot(2 * t), t, w, lane);
+    alast = (AA < KT ? AA : KT) - 1;
+    pp128_wait_slices<C::LOADS>(after(0, alast));
+  } else {
+    for (int t = 0; t < BA && t < KT; ++t) b.issue_direct(slot(2 * t + 1), t, w, lane);
+    blast = (BA < KT ? BA : KT) - 1;
+    pp128_wait_slices<C::LOADS>(after(0, blast));
+  }
+  pp_barrier();
+  if (group == 1) {
+    pp128_wait_slices<C::LOADS>(after(1, alast));  // A of slice 1, read from phase 3 on
+    pp_barrier();
+  }
+
+  u32x4 fa[C::KSTEPS][2], fb[C::KSTEPS];
+  for (int s = 0; s < KT; ++s) {
+    const char* sa = slot(2 * s);
+    const char* sb = slot(2 * s + 1);
+    // Memory phase (issue priority over the other group's MFMA stream).
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      fa[ks][0] = a.read(sa, 0, ks);
+      fa[ks][1] = a.read(sa, 1, ks);
+      fb[ks] = RingOperand<BMN, 128>::read_at(sb, boff, ks);
+    }
+    if (group == 0) {
+      if (s + BA < KT) {
+        b.issue_direct(slot(2 * (s + BA) + 1), s + BA, w, lane);
+        blast = s + BA;
+      }
+      pp_wait_lgkm0();
+    } else {
+      if (s + AA < KT) {
+        a.issue_direct(slot(2 * (s + AA)), s + AA, w, lane);
+        alast = s + AA;
+      }
+      // A of slice s+1 is needed from the next phase on.
+      pp128_wait_slices<C::LOADS>(after(s + 1, alast));
+    }
+    pp_barrier();
+    __builtin_amdgcn_s_setprio(0);
+    // Compute phase.
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i][0] = At::mma(Tag{}, fa[ks][i], fb[ks], acc[i][0]);
+    if (group == 0) pp128_wait_slices<C::LOADS>(after(s + 1, blast));  // B of slice s+1
+    pp_barrier();
+  }
+  if (group == 0) pp_barrier();  // matches group 1's extra prologue barrier
+
+  const bool inner = m0 + C::BM <= p.M && n0 + C::BN <= p.N;
+  if (inner) store_tile<Pp128Wave, EPI, false>(acc, p, m0 + 64 * group, n0 + 32 * w, lane);
+  else store_tile<Pp128Wave, EPI, true>(acc, p, m0 + 64 * group, n0 + 32 * w, lane);
+}
+
+template <class Tag, bool AMN, bool BMN, bool DEEP>
+hipError_t launch_pp128_form(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid(a.tiles_m * a.tiles_n), block(2 * Ring128Cfg::THREADS);
+  if (a.epi == EPI_BETA0)
+    return launch_kernel(gemm_pp128_kernel<Tag, EPI_BETA0, AMN, BMN, DEEP>, grid, block, s, a);
+  if (a.epi == EPI_ACC_PLUS_C)
+    return launch_kernel(gemm_pp128_kernel<Tag, EPI_ACC_PLUS_C, AMN, BMN, DEEP>, grid, block, s,
+                         a);
+  return launch_kernel(gemm_pp128_kernel<Tag, EPI_GENERAL, AMN, BMN, DEEP>, grid, block, s, a);
+}
+
 template <class Tag, bool AMN, bool BMN>
 hipError_t launch_ring_deep(const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.tiles_m * a.tiles_n), block(Ring128Cfg::THREADS);
@@ -188,8 +330,10 @@ hipError_t launch_ring_kg(const GemmArgs& a, hipStream_t s) {
 
 template <class Tag, bool AMN, bool BMN>
 hipError_t launch_ring(const GemmArgs& a, hipStream_t s) {
-  if (a.ring_mode == RING_DEEP) {
+  if (a.ring_mode == RING_DEEP || a.ring_mode == RING_PP || a.ring_mode == RING_PP_DEEP) {
     if (a.src32 || !a.a_direct || !a.b_direct) return hipErrorInvalidValue;  // never planned
+    if (a.ring_mode == RING_PP) return launch_pp128_form<Tag, AMN, BMN, false>(a, s);
+    if (a.ring_mode == RING_PP_DEEP) return launch_pp128_form<Tag, AMN, BMN, true>(a, s);
     return launch_ring_deep<Tag, AMN, BMN>(a, s);
   }
   if (a.ring_mode == RING_KSPLIT2) return launch_ring_kg<Tag, AMN, BMN, 2>(a, s);

@@ -287,11 +287,15 @@ struct RingOperand {
   }
 
   __device__ __forceinline__ u32x4 read(const char* slot, int t, int ks) const {
+    return read_at(slot, off[t], ks);
+  }
+  // The fragment whose sub-step-0 offset is o (one of off[]).
+  __device__ __forceinline__ static u32x4 read_at(const char* slot, int o, int ks) {
     if constexpr (!MN) {
-      return *reinterpret_cast<const u32x4*>(slot + (off[t] ^ (ks << 5)));
+      return *reinterpret_cast<const u32x4*>(slot + (o ^ (ks << 5)));
     } else {
       typedef __attribute__((address_space(3))) pp_i16x4 lds_i16x4;
-      const char* q = slot + off[t] + ks * 16 * RB;
+      const char* q = slot + o + ks * 16 * RB;
       const pp_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q));
       const pp_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * RB));
       const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);

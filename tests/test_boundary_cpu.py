@@ -125,14 +125,19 @@ def test_unaligned_pitch_stays_on_mfma_with_narrow_staging(lib):
     # contiguous dimension off a multiple of 8), B is loaded straight into LDS
     assert _v(lib, M=4097, N=1000, K=1032, tA=1, lda=4104) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" ring masked staged (A: M % 8 != 0)")
-    # (256 tiles, at most one per CU: the deep ring when both operands go
-    # straight into LDS, else K split over two wave groups)
+    # (256 tiles, at most one per CU: with both operands straight into LDS
+    # the deep ring when B is K-contiguous, else the two-group form with ten
+    # half-slots; with a staged operand K split over two wave groups)
     assert _v(lib, M=4096, N=1000, K=1032, tA=1, lda=4104) == lib.GEMM_OK
-    assert lib.gemm_last_path().endswith(" TN epi=beta0 ring deep masked"), lib.gemm_last_path()
+    assert lib.gemm_last_path().endswith(" TN epi=beta0 ring two-group deep masked"), \
+        lib.gemm_last_path()
+    assert _v(lib, M=4096, N=1000, K=1032, tA=1, tB=1, lda=4104) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" TT epi=beta0 ring deep masked"), lib.gemm_last_path()
     assert _v(lib, M=4096, N=1024, K=1028, tA=0, lda=1032) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" ring ksplit2 masked staged (A: K % 8 != 0)")
     assert _v(lib, M=4096, N=1000, K=1024, tA=0, tB=0, ldb=1000) == lib.GEMM_OK
-    assert lib.gemm_last_path().endswith(" NN epi=beta0 ring deep masked"), lib.gemm_last_path()
+    assert lib.gemm_last_path().endswith(" NN epi=beta0 ring two-group deep masked"), \
+        lib.gemm_last_path()
     assert _v(lib, M=4096, N=1004, K=1024, tA=0, tB=0, ldb=1008) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" ring ksplit2 masked staged (B: N % 8 != 0)")
     assert _v(lib, A=A0 + 2) == lib.GEMM_OK
@@ -160,16 +165,25 @@ def test_unaligned_pitch_stays_on_mfma_with_narrow_staging(lib):
 
 
 def test_ring_modes(lib, monkeypatch):
-    # at most one 128x128 tile per CU: the deep ring (both operands direct)
+    # at most one 128x128 tile per CU, both operands direct: the two-group
+    # form with ten half-slots when B is N-contiguous, the deep ring when it
+    # is K-contiguous
     assert _v(lib, M=2048, N=2048, K=2048, dtype=1) == lib.GEMM_OK
-    assert lib.gemm_last_path() == "mfma t128x128x64 w2x2 a32x32x16 NN epi=beta0 ring deep"
+    assert lib.gemm_last_path() == \
+        "mfma t128x128x64 w2x4 a32x32x16 NN epi=beta0 ring two-group deep"
+    assert _v(lib, M=2048, N=2048, K=2048, dtype=1, tB=1) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "mfma t128x128x64 w2x2 a32x32x16 NT epi=beta0 ring deep"
     # ... or two K groups when an operand is staged through registers
     assert _v(lib, M=2048, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_OK
     assert lib.gemm_last_path().startswith(
         "mfma t128x128x64 w2x2 a32x32x16 NN epi=beta0 ring ksplit2 staged (A: row pitch")
-    # more tiles than CUs: one group, two workgroups per CU
+    # more tiles than CUs: two workgroups per CU, of two wave groups taking
+    # turns (both operands direct) or of one group (a staged operand)
     assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_OK
-    assert lib.gemm_last_path() == "mfma t128x128x64 w2x2 a32x32x16 NN epi=beta0 ring"
+    assert lib.gemm_last_path() == "mfma t128x128x64 w2x4 a32x32x16 NN epi=beta0 ring two-group"
+    assert _v(lib, M=4096, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith(
+        "mfma t128x128x64 w2x2 a32x32x16 NN epi=beta0 ring staged (A: row pitch")
     monkeypatch.setenv("GEMM_RING_MODE", "shared")
     assert _v(lib, M=2048, N=2048, K=2048, dtype=1) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" ring")
@@ -179,6 +193,14 @@ def test_ring_modes(lib, monkeypatch):
     monkeypatch.setenv("GEMM_RING_MODE", "deep")
     assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" ring deep")
+    assert _v(lib, M=2048, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_ERR_UNSUPPORTED
+    monkeypatch.setenv("GEMM_RING_MODE", "pp")
+    assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "mfma t128x128x64 w2x4 a32x32x16 NN epi=beta0 ring two-group"
+    monkeypatch.setenv("GEMM_RING_MODE", "ppdeep")
+    assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" ring two-group deep")
+    assert _v(lib, M=2048, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_ERR_UNSUPPORTED
     assert _v(lib, M=2048, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_ERR_UNSUPPORTED
     monkeypatch.setenv("GEMM_RING_MODE", "wide")
     assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_ERR_INVALID_ARG

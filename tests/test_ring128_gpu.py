@@ -36,7 +36,7 @@ LAYOUTS = [(0, 1), (0, 0), (1, 1), (1, 0)]
 MODES = [(True, True), (False, True), (True, False), (False, False)]
 
 
-@pytest.mark.parametrize("kg", ["shared", "ksplit2", "deep"])
+@pytest.mark.parametrize("kg", ["shared", "ksplit2", "deep", "pp", "ppdeep"])
 @pytest.mark.parametrize("tA,tB", LAYOUTS)
 @pytest.mark.parametrize("mode", MODES)
 def test_ring_layouts_modes_and_slice_counts(tA, tB, mode, kg, monkeypatch):
@@ -45,11 +45,13 @@ def test_ring_layouts_modes_and_slice_counts(tA, tB, mode, kg, monkeypatch):
     turns of the ring, K tails that cut a 16-byte piece (K % 8 != 0) and ones
     that do not; whole tiles and edge tiles on both M and N; one K group per
     workgroup and two; the deep ring (ten half-slots, four slices ahead, both
-    operands loaded straight into LDS)."""
+    operands loaded straight into LDS); the two-group forms (two wave groups
+    taking turns, both operands straight into LDS, five or ten half-slots)."""
     monkeypatch.setenv("GEMM_RING_MODE", kg)
     a_al, b_al = mode
-    if kg == "deep" and mode != (True, True):
-        pytest.skip("the deep ring loads both operands straight into LDS")
+    direct_only = kg in ("deep", "pp", "ppdeep")
+    if direct_only and mode != (True, True):
+        pytest.skip("this form loads both operands straight into LDS")
     seed = 7000 + 97 * LAYOUTS.index((tA, tB)) + 13 * MODES.index(mode) + 1000 * len(kg)
     cases = [(256, 384, 64), (256, 128, 128), (384, 256, 192), (128, 128, 320),
              (300, 260, 72), (136, 200, 1000), (264, 136, 1032), (129, 127, 17)]
@@ -58,27 +60,29 @@ def test_ring_layouts_modes_and_slice_counts(tA, tB, mode, kg, monkeypatch):
             seed += 1
             lda = _ld(M if tA else K, a_al)
             ldb = _ld(K if tB else N, b_al)
-            if kg == "deep" and ((M % 8 and tA) or (N % 8 and not tB) or K % 8):
-                continue  # an edge cuts a 16-byte piece: staged, not the deep ring
+            if direct_only and ((M % 8 and tA) or (N % 8 and not tB) or K % 8):
+                continue  # an edge cuts a 16-byte piece: staged, not this form
             cfg = workloads.Config(f"ring{seed}", M, N, K, "bf16" if seed % 2 else "f16", tA, tB,
                                    alpha, beta, "uniform", seed, lda=lda, ldb=ldb,
                                    ldc=N + 3, ldd=N + 3)
             r = run(cfg)
             assert " ring" in r.path and (" ring deep" in r.path) == (kg == "deep") \
-                and (" ring ksplit2" in r.path) == (kg == "ksplit2"), r.path
+                and (" ring ksplit2" in r.path) == (kg == "ksplit2") \
+                and (" ring two-group" in r.path) == (kg in ("pp", "ppdeep")) \
+                and (" two-group deep" in r.path) == (kg == "ppdeep"), r.path
             r.check()
             r.check_padding_untouched()
 
 
-@pytest.mark.parametrize("kg", ["shared", "ksplit2", "deep"])
+@pytest.mark.parametrize("kg", ["shared", "ksplit2", "deep", "pp", "ppdeep"])
 @pytest.mark.parametrize("tA,tB", LAYOUTS)
 @pytest.mark.parametrize("aligned", [True, False])
 def test_ring_permutations_pin_layouts_bitwise(tA, tB, aligned, kg, monkeypatch):
     """P @ X and X @ Q move every element to a known place exactly: a wrong
     swizzle, fragment lane or slot in either staging mode, or a wrong row in
     the K groups' exchange, shows up."""
-    if kg == "deep" and not aligned:
-        pytest.skip("the deep ring loads both operands straight into LDS")
+    if kg in ("deep", "pp", "ppdeep") and not aligned:
+        pytest.skip("this form loads both operands straight into LDS")
     monkeypatch.setenv("GEMM_RING_MODE", kg)
     rng = np.random.default_rng(300 + 2 * tA + tB + (8 if aligned else 0))
     M, N, K = 256, 256, 256
