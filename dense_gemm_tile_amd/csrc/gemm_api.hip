@@ -473,18 +473,19 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     // Both operands straight into LDS: two wave groups taking turns (five
     // half-slots, two workgroups per CU) on grids of more than one tile per
     // CU; on smaller grids the deep ring (one wave per SIMD, every slice
-    // requested four ahead from 160 KiB) when B is K-contiguous, else the
-    // two-group form with ten half-slots, whose second wave per SIMD hides
-    // the transposed B reads (measured on 2048^3 and 4096x1024x1024 in all
-    // four layouts). A staged operand: K split over two wave groups per
-    // workgroup (8 waves, two rings) on small grids, so that each SIMD still
-    // alternates between two waves; one group per workgroup and two
-    // workgroups per CU beyond.
+    // requested four ahead from 160 KiB), except with B N-contiguous and a
+    // long K, where the two-group form with ten half-slots hides the
+    // transposed B reads behind the second wave per SIMD (measured, NN and
+    // TN: 8-15 % faster at K = 2048, 5-8 % slower at K = 1024, where the
+    // deep ring's earlier start counts more; slower with B K-contiguous). A
+    // staged operand: K split over two wave groups per workgroup (8 waves,
+    // two rings) on small grids, so that each SIMD still alternates between
+    // two waves; one group per workgroup and two workgroups per CU beyond.
     const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
     const bool both_direct = a.a_direct && a.b_direct;
     a.ring_mode = ntiles > 256 ? (both_direct ? RING_PP : RING_SHARED)
                   : !both_direct ? RING_KSPLIT2
-                  : transB ? RING_DEEP : RING_PP_DEEP;
+                  : (transB || K < 2048) ? RING_DEEP : RING_PP_DEEP;
     if (const char* rm = g_env.ring_mode) {
       if (std::strcmp(rm, "shared") == 0) a.ring_mode = RING_SHARED;
       else if (std::strcmp(rm, "ksplit2") == 0) a.ring_mode = RING_KSPLIT2;

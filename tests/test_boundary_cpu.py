@@ -126,9 +126,12 @@ def test_unaligned_pitch_stays_on_mfma_with_narrow_staging(lib):
     assert _v(lib, M=4097, N=1000, K=1032, tA=1, lda=4104) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" ring masked staged (A: M % 8 != 0)")
     # (256 tiles, at most one per CU: with both operands straight into LDS
-    # the deep ring when B is K-contiguous, else the two-group form with ten
-    # half-slots; with a staged operand K split over two wave groups)
+    # the deep ring, or the two-group form with ten half-slots when B is
+    # N-contiguous and K at least 2048; with a staged operand K split over
+    # two wave groups)
     assert _v(lib, M=4096, N=1000, K=1032, tA=1, lda=4104) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" TN epi=beta0 ring deep masked"), lib.gemm_last_path()
+    assert _v(lib, M=4096, N=1000, K=2056, tA=1, lda=4104) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" TN epi=beta0 ring two-group deep masked"), \
         lib.gemm_last_path()
     assert _v(lib, M=4096, N=1000, K=1032, tA=1, tB=1, lda=4104) == lib.GEMM_OK
@@ -136,8 +139,7 @@ def test_unaligned_pitch_stays_on_mfma_with_narrow_staging(lib):
     assert _v(lib, M=4096, N=1024, K=1028, tA=0, lda=1032) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" ring ksplit2 masked staged (A: K % 8 != 0)")
     assert _v(lib, M=4096, N=1000, K=1024, tA=0, tB=0, ldb=1000) == lib.GEMM_OK
-    assert lib.gemm_last_path().endswith(" NN epi=beta0 ring two-group deep masked"), \
-        lib.gemm_last_path()
+    assert lib.gemm_last_path().endswith(" NN epi=beta0 ring deep masked"), lib.gemm_last_path()
     assert _v(lib, M=4096, N=1004, K=1024, tA=0, tB=0, ldb=1008) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" ring ksplit2 masked staged (B: N % 8 != 0)")
     assert _v(lib, A=A0 + 2) == lib.GEMM_OK
@@ -166,8 +168,8 @@ def test_unaligned_pitch_stays_on_mfma_with_narrow_staging(lib):
 
 def test_ring_modes(lib, monkeypatch):
     # at most one 128x128 tile per CU, both operands direct: the two-group
-    # form with ten half-slots when B is N-contiguous, the deep ring when it
-    # is K-contiguous
+    # form with ten half-slots when B is N-contiguous and K >= 2048, else
+    # the deep ring
     assert _v(lib, M=2048, N=2048, K=2048, dtype=1) == lib.GEMM_OK
     assert lib.gemm_last_path() == \
         "mfma t128x128x64 w2x4 a32x32x16 NN epi=beta0 ring two-group deep"
