@@ -5,8 +5,8 @@
 //    integer form of the same contraction (Phobos `@tensorcore`: an i8 dot
 //    takes the integer tensor cores whenever its shape allows, "When it
 //    declines").
-//  * 8-bit floats (OCP E4M3 or E5M2) -> f32 (v_mfma_scale_f32_32x32x64_f8f6f4
-//    with unit scales): f32 C/D and alpha/beta, the epilogue of the 16-bit
+//  * 8-bit floats (OCP E4M3 or E5M2) -> f32 (v_mfma_f32_32x32x64_f8f6f4, the
+//    form without block scales): f32 C/D and alpha/beta, the epilogue of the 16-bit
 //    kernels. The fp8 precision of the `gemm_async` variants (TVM `gemm`,
 //    restated: the precision list).
 //
@@ -95,7 +95,8 @@ struct KindF8 {
     return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   }
   __device__ static inline acc_t mma(frag_t a, frag_t b, acc_t c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, 127, 0, 127);
+    // scale operands 0: the unscaled form, as in KindF8x16
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, 0, 0, 0);
   }
   // cbits: C[r][c] as read by epilogue() (when p.read_c).
   __device__ static inline void store(const GemmByteArgs& p, int64_t r, int c, acc_t v, int e,
@@ -164,8 +165,14 @@ struct KindF8x16 {
     const i32x4 hi = *reinterpret_cast<const i32x4*>(base + (off ^ 64));  // chunk g ^ 4
     return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   }
+  // Scale operands of 0 select the form of the instruction without block
+  // scales (v_mfma_f32_16x16x128_f8f6f4), which multiplies the codes as they
+  // are, as unit scales would. Measured: the scaled form with unit scales
+  // (127) ran 29 % slower at 8192^3 in the two-group kernel, as fast as the
+  // unscaled one only when no loads were in flight; the same fragments fed
+  // to two int8 MFMAs of the same total cycles ran at the unscaled speed.
   __device__ static inline acc_t mma(frag_t a, frag_t b, acc_t c) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, 0, 127, 0, 127);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, 0, 0, 0, 0);
   }
   // M/N-contiguous slot: K-rows 16g .. +15 and 16g + 64 .. +15 of the lane's
   // column (the same K order as read_off), four transposed reads.
