@@ -36,6 +36,10 @@ struct GemmArgs {
   int b_direct;  //    (16-byte rows, edges of its contiguous dimension on
                  //    multiples of 8 elements), 0 if staged through registers
   int ring_mode; // 128x128 ring kernel: RingMode below
+  int mfold;     // 128x128 ring kernel (two K groups, 16-bit operands):
+                 //    rows M - mfold .. M - 1 (0 < mfold <= 4) lie past the
+                 //    tiles_m whole tile rows and are computed by the last of
+                 //    them; 0: none
 };
 
 // Forms of the 128x128 ring kernel.

@@ -33,6 +33,7 @@ struct MfmaPath {
   const char* epi;
   bool pingpong, masked, k16_tail, ring;
   int ring_mode;
+  int mfold;          // rows folded into the last tile row (ring kernel)
   int atom;           // 16: the two-group kernel on 16x16x32 atoms; 0: the tile's own
   const char* src32;  // "", " f32->f16" or " f32->bf16"
   std::string elem_reason;  // operands read in narrow pieces (general kernel)
@@ -44,10 +45,12 @@ thread_local bool g_path_lazy = false;
 const std::string& current_path() {
   if (g_path_lazy) {
     const MfmaPath& m = g_mpath;
-    char buf[512], ksplit[32] = "";
+    char buf[512], ksplit[32] = "", fold[48] = "";
     if (m.ti->kg > 1) std::snprintf(ksplit, sizeof ksplit, " ksplit%d", m.ti->kg);
+    if (m.ring && m.mfold > 0)
+      std::snprintf(fold, sizeof fold, " fold(%d row%s)", m.mfold, m.mfold > 1 ? "s" : "");
     const bool a16 = m.atom == 16;
-    std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s%s%s%s%s%s%s",
+    std::snprintf(buf, sizeof buf, "mfma %s w%dx%d a%dx%dx%d %s epi=%s%s%s%s%s%s%s%s%s%s%s%s%s%s",
                   m.ti->name, m.ti->waves_m,
                   m.pingpong || (m.ring && (m.ring_mode == RING_PP || m.ring_mode == RING_PP_DEEP))
                       ? 4
@@ -60,7 +63,7 @@ const std::string& current_path() {
                   : m.ring_mode == RING_DEEP ? " ring deep"
                   : m.ring_mode == RING_PP ? " ring two-group"
                   : m.ring_mode == RING_PP_DEEP ? " ring two-group deep" : " ring",
-                  m.masked ? " masked" : "", m.k16_tail ? " k16-tail" : "", m.src32,
+                  fold, m.masked ? " masked" : "", m.k16_tail ? " k16-tail" : "", m.src32,
                   m.elem_reason.empty() ? "" : " narrow staging (", m.elem_reason.c_str(),
                   m.elem_reason.empty() ? "" : ")",
                   m.staged.empty() ? "" : " staged (", m.staged.c_str(),
@@ -481,8 +484,22 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     // staged operand: K split over two wave groups per workgroup (8 waves,
     // two rings) on small grids, so that each SIMD still alternates between
     // two waves; one group per workgroup and two workgroups per CU beyond.
-    const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
+    int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
     const bool both_direct = a.a_direct && a.b_direct;
+    // A staged operand and up to 4 rows past the last whole tile row that
+    // alone push the grid past one tile per CU: the last tile row computes
+    // them (one more row of 16x16x32 atoms, A read element by element), so
+    // the grid keeps one tile per CU and takes the two-K-group form.
+    a.mfold = 0;
+    const int64_t mrem = M % ti.bm;
+    if (!src32 && !both_direct && mrem >= 1 && mrem <= 4 && M >= ti.bm) {
+      const int64_t folded = (M / ti.bm) * a.tiles_n;
+      if (ntiles > 256 && folded <= 256) {
+        a.mfold = (int)mrem;
+        a.tiles_m = (int)(M / ti.bm);
+        ntiles = folded;
+      }
+    }
     a.ring_mode = ntiles > 256 ? (both_direct ? RING_PP : RING_SHARED)
                   : !both_direct ? RING_KSPLIT2
                   : (transB || K < 2048) ? RING_DEEP : RING_PP_DEEP;
@@ -502,6 +519,10 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
                     std::string("GEMM_RING_MODE must be shared, ksplit2, deep, pp or ppdeep, got ") +
                         rm);
     }
+    if (a.mfold > 0 && a.ring_mode != RING_KSPLIT2) {  // a forced form: no folded rows
+      a.mfold = 0;
+      a.tiles_m = (int)((M + ti.bm - 1) / ti.bm);
+    }
   }
   // A last K step whose valid part ends within the first half of a 16x16x32
   // sub-step finishes with v_mfma_f32_16x16x16 (no product of staged zeros).
@@ -515,6 +536,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   g_mpath.atom = pingpong && !plan.pp_f32 && !transA ? 16 : 0;
   g_mpath.ring = plan.ring;
   g_mpath.ring_mode = a.ring_mode;
+  g_mpath.mfold = plan.ring ? a.mfold : 0;
   g_mpath.staged.swap(staged);
   g_mpath.masked = plan.masked;
   g_mpath.k16_tail = k16_tail;

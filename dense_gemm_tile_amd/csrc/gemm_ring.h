@@ -311,6 +311,89 @@ struct RingRow : C {
   static constexpr int TM = 1;
 };
 
+// Rows past the last whole tile row (at most kMaxFold: p.mfold) folded into
+// that tile row's workgroups, so that a shape such as 4097 x 1000 runs as
+// 256 tiles (one per CU) instead of 264. The extra rows form one row of
+// 16x16x32 atoms under the tile: wave w of each K group owns the 32
+// columns [32w, 32w+32) (two atoms). Their A values are loaded one slice
+// ahead and before the slice's other loads, so every wait that covers those
+// loads covers them too: for each extra row, lanes 0-31 load the slice's 64
+// K values as 32 pairs (two 2-byte loads per lane, any alignment, rows past
+// M and K past the end reading zeros), and each lane then gathers its
+// fragment's four pairs with ds_bpermute. Lanes whose fragment row is not an
+// extra row keep whatever they gather: their output rows are not stored.
+// Their B fragments are read from the B slot the tile already holds. The K
+// groups' sums meet through LDS after the loop, in group order, like the
+// tile's.
+constexpr int kMaxFold = 4;
+struct RingFoldRow {  // the epilogue's view: one row of two 16x16 atoms
+  using At = Atom<16>;
+  static constexpr int TM = 1, TN = 2;
+};
+
+template <bool MN, int ROWS>
+struct RingFold {
+  using A16 = Atom<16>;
+  // Slice t's A values of extra row i (row0 + i, i < nrows): lane l < 32
+  // gets K values t*64 + 2l and +1 as one dword (zeros past M or K).
+  __device__ static inline void load_pairs(unsigned (&pr)[kMaxFold], const uint16_t* A,
+                                           int64_t lda, int row0, int nrows, int M, int K, int t,
+                                           int lane) {
+#pragma unroll
+    for (int i = 0; i < kMaxFold; ++i) {
+      const int row = row0 + i;
+      const int k = t * 64 + 2 * lane;
+      unsigned lo = 0u, hi = 0u;
+      if (i < nrows && lane < 32 && row < M) {
+        if (k < K) lo = MN ? A[(int64_t)k * lda + row] : A[(int64_t)row * lda + k];
+        if (k + 1 < K) hi = MN ? A[(int64_t)(k + 1) * lda + row] : A[(int64_t)row * lda + k + 1];
+      }
+      pr[i] = lo | (hi << 16);
+    }
+  }
+  // The A fragment of sub-step ks from the pairs: lane l (fragment row
+  // l%16, K values 32 ks + 8 (l/16) .. +7) takes pairs 16 ks + 4 (l/16) .. +3
+  // of extra row l%16.
+  __device__ static inline u32x4 gather(const unsigned (&pr)[kMaxFold], int nrows, int ks,
+                                        int lane) {
+    const int src = 16 * ks + 4 * (lane >> 4);
+    u32x4 f = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kMaxFold; ++i) {
+      if (i < nrows) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const unsigned v = (unsigned)__builtin_amdgcn_ds_bpermute(4 * (src + d), (int)pr[i]);
+          if ((lane & 15) == i) f[d] = v;
+        }
+      }
+    }
+    return f;
+  }
+  // B fragment of a 16x16x32 atom whose first column is col0 (within the
+  // tile), sub-step ks, from a B slot in the ring's layout.
+  __device__ static inline u32x4 read_b(const char* slot, int col0, int ks, int lane) {
+    if constexpr (!MN) {
+      // K-contiguous slot: row n, chunk 4 ks + l/16
+      return *reinterpret_cast<const u32x4*>(slot + lds_off(col0 + (lane & 15), 4 * ks + (lane >> 4)));
+    } else {
+      // M/N-contiguous slot: two transposed reads give lane l column
+      // col0 + l%16 at K rows 32 ks + 8 (l/16) .. +7; lane s of each group
+      // of 16 names row 32 ks + 8 g + s/4, columns col0 + 4 (s%4) .. +3.
+      typedef __attribute__((address_space(3))) pp_i16x4 lds_i16x4;
+      constexpr int RB = ROWS * 2;
+      const int s = lane & 15, g = lane >> 4;
+      const int col = col0 + 4 * (s & 3);
+      const int r = 32 * ks + 8 * g + (s >> 2);
+      const char* q = slot + r * RB + (((col >> 3) ^ (4 * (r & 3))) << 4) + ((col & 7) << 1);
+      const pp_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q));
+      const pp_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * RB));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{l2.x, l2.y, h2.x, h2.y};
+    }
+  }
+};
+
 // KG K groups of 4 waves each: group g multiplies the tile's slices g, g+KG,
 // g+2KG, ... with a ring of its own; with KG = 2 a tile takes 160 KiB of LDS
 // and 8 waves, so grids of about one tile per CU still give every SIMD two
@@ -319,7 +402,10 @@ struct RingRow : C {
 // STAGING: operands staged through registers are supported (otherwise both
 // must be direct). SRC32: both operands hold float32 values (staged, rounded
 // to Tag's type with mode p.src32).
-template <int ROWS, class Tag, int EPI, bool AMN, bool BMN, int KG, bool STAGING, bool SRC32 = false>
+// FOLD: the instantiation for p.mfold > 0 (two K groups, 16-bit operands),
+// which leaves out the early C requests to make room for the folded rows.
+template <int ROWS, class Tag, int EPI, bool AMN, bool BMN, int KG, bool STAGING, bool SRC32 = false,
+          bool FOLD = false>
 __global__ void __launch_bounds__(RingCfg<ROWS>::THREADS * KG, RingCfg<ROWS>::MIN_WG / KG)
 gemm_ring_kernel(const GemmArgs p) {
   using C = RingCfg<ROWS>;
@@ -359,6 +445,17 @@ gemm_ring_kernel(const GemmArgs p) {
   const int nvi = nvalid(m0 + wm * C::WTM, p.M, C::TM);
   const int nvj = nvalid(n0 + wn * C::WTN, p.N, C::TN);
   const bool full_wave = nvi == C::TM && nvj == C::TN;
+  // Folded rows (see RingFold).
+  static_assert(!FOLD || (KG == 2 && !SRC32), "rows are folded with two K groups, 16-bit operands");
+  using A16 = Atom<16>;
+  const bool fold = FOLD && tm == p.tiles_m - 1;  // uniform
+  const int frow0 = m0 + C::BM, fnrows = p.mfold;
+  typename A16::acc_t facc[1][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int v = 0; v < A16::NACC; ++v) facc[0][t][v] = 0.0f;
+  unsigned fpc[kMaxFold], fpn[kMaxFold];  // folded rows' A pairs: this slice, the next
 
   acc_t acc[C::TM][C::TN];
 #pragma unroll
@@ -382,13 +479,19 @@ gemm_ring_kernel(const GemmArgs p) {
   // (row grp). On interior tiles that read C it requests those C values
   // right after the prologue's loads, so they arrive while the K loop runs
   // instead of after it (32 registers per lane).
-  constexpr bool PRE_C = KG == 2 && EPI != EPI_BETA0;
+  constexpr bool PRE_C = KG == 2 && EPI != EPI_BETA0 && !FOLD;
   const bool inner = m0 + C::BM <= p.M && n0 + C::BN <= p.N;
   const bool pre_c = PRE_C && p.wide_epi && inner;
   WideC<RingRow<C>> cpre;
 
   // Prologue: local slice 0 into slots 0 and 1, then A of local slice 1
-  // (direct) into slot 2, or local slice 1 (staged) into registers.
+  // (direct) into slot 2, or local slice 1 (staged) into registers. The
+  // folded rows' A of slice 0 goes first.
+  if constexpr (FOLD) {
+    if (fold && NJ > 0)
+      RingFold<AMN, ROWS>::load_pairs(fpc, static_cast<const uint16_t*>(p.A), p.lda, frow0,
+                                      fnrows, p.M, p.K, gs(0), lane);
+  }
   if (NJ > 0) {
     if (a_dir) {
       if constexpr (!SRC32) a.issue_direct(slot(0), gs(0), w, lane);
@@ -430,6 +533,13 @@ gemm_ring_kernel(const GemmArgs p) {
 
   for (int j = 0; j < JT; ++j) {
     if (j < NJ) {
+      // Folded rows: A of local slice j+1, before this iteration's other
+      // loads.
+      if constexpr (FOLD) {
+        if (fold && j + 1 < NJ)
+          RingFold<AMN, ROWS>::load_pairs(fpn, static_cast<const uint16_t*>(p.A), p.lda, frow0,
+                                          fnrows, p.M, p.K, gs(j + 1), lane);
+      }
       // Staged operands: local slice j+1 arrived in registers during the
       // previous iteration (this waits for every older load); write it into
       // its slots (A: 2j+2, left by B of j-2; B: 2j+3, left by A of j-1),
@@ -468,6 +578,19 @@ gemm_ring_kernel(const GemmArgs p) {
             if (full_wave || (i < nvi && jj < nvj))
               acc[i][jj] = At::mma(Tag{}, fa[i], fb[jj], acc[i][jj]);
       }
+      if constexpr (FOLD) {
+        if (fold) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const u32x4 fa16 = RingFold<AMN, ROWS>::gather(fpc, fnrows, ks, lane);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+              facc[0][t] = A16::mma(Tag{}, fa16,
+                                    RingFold<BMN, ROWS>::read_b(sb, 32 * w + 16 * t, ks, lane),
+                                    facc[0][t]);
+          }
+        }
+      }
 
       // Local slice j+1 must be in LDS by the next barrier. A direct B of
       // j+1 was issued first in this iteration, so at most the one
@@ -485,6 +608,12 @@ gemm_ring_kernel(const GemmArgs p) {
       }
     }
     pp_barrier();
+    if constexpr (FOLD) {
+      if (fold) {
+#pragma unroll
+        for (int i = 0; i < kMaxFold; ++i) fpc[i] = fpn[i];
+      }
+    }
   }
 
   if constexpr (KG == 1) {
@@ -505,6 +634,17 @@ gemm_ring_kernel(const GemmArgs p) {
         for (int v = 0; v < At::NACC; ++v)  // (a select: no dynamic index into registers)
           dst[(jj * At::NACC + v) * 64] = grp == 0 ? acc[1][jj][v] : acc[0][jj][v];
     }
+    // Folded rows: group 1 hands its sums to group 0 (after the 64 KiB the
+    // tile's exchange uses).
+    float* fx_lds = x + 8 * NV * 64;
+    if constexpr (FOLD) {
+      if (fold && grp == 1) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int v = 0; v < A16::NACC; ++v) fx_lds[(w * 8 + t * 4 + v) * 64 + lane] = facc[0][t][v];
+      }
+    }
     pp_wait_lgkm0();
     pp_barrier();
     acc_t fin[1][C::TN];
@@ -521,6 +661,15 @@ gemm_ring_kernel(const GemmArgs p) {
     const int r0 = m0 + wm * C::WTM + grp * At::M;
     if (inner) store_tile<RingRow<C>, EPI, false>(fin, p, r0, n0 + wn * C::WTN, lane, cpre, pre_c);
     else store_tile<RingRow<C>, EPI, true>(fin, p, r0, n0 + wn * C::WTN, lane);
+    if constexpr (FOLD) {
+      if (fold && grp == 0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int v = 0; v < A16::NACC; ++v) facc[0][t][v] += fx_lds[(w * 8 + t * 4 + v) * 64 + lane];
+        store_tile<RingFoldRow, EPI, true>(facc, p, m0 + C::BM, n0 + 32 * w, lane);
+      }
+    }
   }
 }
 

@@ -118,13 +118,23 @@ def test_unaligned_pitch_stays_on_mfma_with_narrow_staging(lib):
     st = _v(lib, M=4097, N=1000, K=1032, tA=1, lda=4097, alpha=2.0, beta=-1.0)
     assert st == lib.GEMM_OK
     path = lib.gemm_last_path()
-    # (264 tiles: two workgroups per CU where needed)
-    assert path == ("mfma t128x128x64 w2x2 a32x32x16 TN epi=general ring masked staged "
-                    "(A: row pitch 8194 B is not a multiple of 16 B)"), path
+    # (row 4096 is folded into the last whole tile row: 256 tiles instead of
+    # 264, one per CU, on two K groups)
+    assert path == ("mfma t128x128x64 w2x2 a32x32x16 TN epi=general ring ksplit2 fold(1 row) "
+                    "masked staged (A: row pitch 8194 B is not a multiple of 16 B)"), path
     # same shape with a 16-byte pitch: A is still staged (M = 4097 cuts its
     # contiguous dimension off a multiple of 8), B is loaded straight into LDS
     assert _v(lib, M=4097, N=1000, K=1032, tA=1, lda=4104) == lib.GEMM_OK
-    assert lib.gemm_last_path().endswith(" ring masked staged (A: M % 8 != 0)")
+    assert lib.gemm_last_path().endswith(" ring ksplit2 fold(1 row) masked staged (A: M % 8 != 0)")
+    # up to 4 rows fold, and only where that brings the grid to one tile per
+    # CU
+    assert _v(lib, M=4100, N=1000, K=1032, tA=1, lda=4101) == lib.GEMM_OK
+    assert " ring ksplit2 fold(4 rows) masked" in lib.gemm_last_path(), lib.gemm_last_path()
+    assert _v(lib, M=4101, N=1000, K=1032, tA=1, lda=4101) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith(
+        "mfma t128x128x64 w2x2 a32x32x16 TN epi=beta0 ring masked staged"), lib.gemm_last_path()
+    assert _v(lib, M=8193, N=1000, K=1032, tA=1, lda=8193) == lib.GEMM_OK
+    assert "fold" not in lib.gemm_last_path(), lib.gemm_last_path()
     # (256 tiles, at most one per CU: with both operands straight into LDS
     # the deep ring, or the two-group form with ten half-slots when B is
     # N-contiguous and K at least 2048; with a staged operand K split over

@@ -39,7 +39,8 @@ def test_workload_parity_full(name):
     r.check_padding_untouched()
     assert r.path.startswith("mfma "), r.path
     if name == "ragged4097x1000x1032_tn":
-        assert " ring masked staged (A: row pitch 8194 B" in r.path, r.path
+        # row 4096 folded into the last whole tile row (256 tiles, two K groups)
+        assert " ring ksplit2 fold(1 row) masked staged (A: row pitch 8194 B" in r.path, r.path
 
 
 @pytest.mark.parametrize("name", ["gemm4096_inplace", "gemm8192_nt"])

@@ -142,3 +142,41 @@ def test_ring_edge_waves_and_inplace(tA, tB, monkeypatch):
         assert " ring" in r.path, r.path
         r.check()
         r.check_padding_untouched()
+
+
+@pytest.mark.parametrize("tA,tB", LAYOUTS)
+def test_ring_fold_rows_past_the_last_tile_row(tA, tB, monkeypatch):
+    """Up to 4 rows past the last whole tile row, computed by that tile
+    row's workgroups when that keeps the grid at one tile per CU (16x16x32
+    atoms under the tile, A loaded as K pairs and gathered across lanes, B
+    from the tile's own slot, the two K groups' sums met through LDS):
+    remainders 1, 3 and 4,
+    K tails, every epilogue, C == D; elementwise against the oracle on rows
+    that cover every tile row and all folded rows; D untouched outside
+    M x N. The same shapes with the single-group ring forced take the extra
+    tile row instead and must agree."""
+    monkeypatch.delenv("GEMM_RING_MODE", raising=False)
+    seed = 9700 + 10 * LAYOUTS.index((tA, tB))
+    for (M, N, K, alpha, beta, inplace) in [(2049, 2048, 200, 1.0, 0.0, False),
+                                            (2051, 2000, 137, 1.5, -0.5, False),
+                                            (1028, 4096, 72, 1.0, 1.0, True)]:
+        seed += 1
+        lda = _ld(M if tA else K, False)  # staged A: the fold applies
+        ldb = _ld(K if tB else N, seed % 2 == 0)
+        ld = N + (0 if inplace else 4)
+        cfg = workloads.Config(f"fold{seed}", M, N, K, "bf16" if seed % 2 else "f16", tA, tB,
+                               alpha, beta, "uniform", seed, lda=lda, ldb=ldb, ldc=ld, ldd=ld,
+                               inplace=inplace)
+        inp = workloads.make_inputs(cfg)
+        r = run(cfg, inp)
+        nfold = M % 128
+        assert f" ring ksplit2 fold({nfold} row" in r.path, r.path
+        rows = np.unique(np.concatenate([np.arange(M - 130, M),
+                                         np.arange(0, M, 97), np.arange(127, M, 128)]))
+        r.check(rows=rows)
+        r.check_padding_untouched()
+        monkeypatch.setenv("GEMM_RING_MODE", "shared")
+        r2 = run(cfg, inp)
+        monkeypatch.delenv("GEMM_RING_MODE")
+        assert " ring" in r2.path and "fold" not in r2.path, r2.path
+        r2.check(rows=rows)
