@@ -407,11 +407,11 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     const int64_t ldmax = lda > ldb ? lda : ldb;
     big_pitch = ldmax * esz * rows + 4096 >= (int64_t{1} << 31);
     if (big_pitch) plan.masked = true;
-    // Float32 operands, both K-contiguous, 16-byte rows, whole 256x256 tiles
-    // and K a multiple of its 32-deep slices: the two-group kernel rounds them
-    // as it reads fragments. Every other float32 call is rounded while the
-    // masked kernel stages it.
-    plan.pp_f32 = src32 && t == TILE_256x256 && !transA && transB && !a_elem && !b_elem &&
+    // Float32 operands with 16-byte rows, whole 256x256 tiles and K a
+    // multiple of its 32-deep slices, any layout: the two-group kernel rounds
+    // them as it reads fragments. Every other float32 call is rounded while
+    // it is staged (ring kernel, or the masked kernel for 64-bit pitches).
+    plan.pp_f32 = src32 && t == TILE_256x256 && !a_elem && !b_elem &&
                   !big_pitch && M % ti.bm == 0 && N % ti.bn == 0 && K % pp_f32_slice() == 0;
     if (plan.pp_f32) plan.masked = false;
     else if (a_elem || b_elem || src32) plan.masked = true;
@@ -637,7 +637,7 @@ hipError_t launch_plan(const Plan& plan, int dtype, int transA, int transB, hipS
   if (plan.noop) return hipSuccess;
   if (plan.scale_only) return launch_scale_c(plan.args, s);
   if (plan.byte8) return launch_byte(plan.byte_kind, transA != 0, transB != 0, plan.bargs, s);
-  if (plan.pp_f32) return launch_pp_f32(dtype & 1, plan.args, s);
+  if (plan.pp_f32) return launch_pp_f32(dtype & 1, transA != 0, transB != 0, plan.args, s);
   if (plan.ring) return launch_ring128(dtype & 1, transA != 0, transB != 0, plan.args, s);
   if (plan.mfma)
     return launch_mfma(plan.tile, dtype & 1, transA != 0, transB != 0, plan.masked, plan.args, s);

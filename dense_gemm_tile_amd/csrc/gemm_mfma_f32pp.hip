@@ -1,6 +1,6 @@
-// Whole 256x256 tiles of float32 operands, both K-contiguous (A stored [M][K],
-// B stored [N][K]), on the two-group direct-to-LDS design of the 16-bit
-// kernel. The operands reach LDS as float32 and are rounded to f16 or bf16
+// Whole 256x256 tiles of float32 operands, in any of the four layouts, on the
+// two-group direct-to-LDS design of the 16-bit kernel. The operands reach
+// LDS as float32 and are rounded to f16 or bf16
 // (nearest, ties to even) in registers as each fragment is read, so an f32
 // call moves no more than its own operand bytes through HBM and the matrix
 // cores see the same 16-bit values as when the caller rounds beforehand
@@ -11,6 +11,15 @@
 // MFMA sub-steps (16 MFMAs per wave) per compute phase against the same 32 KiB
 // half slice of loads per memory phase as the 16-bit kernel. Ring, slots,
 // phases, waits and barriers are the 16-bit kernel's.
+//
+// An M/N-contiguous operand (A stored [K][M], B stored [K][N]) fills a slot
+// as the slice's 32 K-rows of 256 values (1 KiB each); 16-byte chunk c of
+// row r sits at position c ^ (8 * r3) (r3: bit 3 of r). A load instruction
+// of wave lw covers one row (8 lw + i), lane l filling position l. A lane's
+// fragment (8 consecutive K of one column) is 8 ds_read_b32 down the rows,
+// 1 KiB apart; lanes 0-31 read 32 consecutive columns of one row and lanes
+// 32-63 the same columns 8 rows down, which the swizzle moves to the other
+// half of the banks.
 #include "gemm_mfma_pingpong.h"
 
 namespace dgt {
@@ -43,7 +52,55 @@ __device__ __forceinline__ u32x4 read_f32_frag(const char* slot, int off, int ks
                cvt_pk(Tag{}, hi[0], hi[1]), cvt_pk(Tag{}, hi[2], hi[3])};
 }
 
-template <class Tag, int EPI>
+// An M/N-contiguous float32 operand of the two-group kernel (see above).
+struct PpF32MN {
+  const float* base;  // tile's first column (M or N index), K = 0
+  int64_t ld;         // row pitch in elements
+  int voff;           // this lane's byte offset within the wave's first row
+  __device__ inline void init_load(const void* X, int64_t ld_, int c0, int lw, int lane) {
+    base = static_cast<const float*>(X) + c0;
+    ld = ld_;
+    // rows 8 lw .. 8 lw + 7 all have r3 = lw & 1
+    voff = (int)((int64_t)(8 * lw) * ld * 4) + ((lane ^ (8 * (lw & 1))) << 4);
+  }
+  __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
+    // The slice's first K row is folded into the resource base, so the
+    // 32-bit offsets stay within its 32 rows.
+    const float* b = base + (int64_t)slice * 32 * ld;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(b), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
+                                             16, voff, (int)(i * ld * 4), 0, 0);
+  }
+  // Sub-step-0 byte offset of lane l's fragment of the 32x32 atom whose
+  // first column is col0 (within the tile): column col0 + l%32, rows
+  // 8 (l/32) .. +7.
+  __device__ static inline int frag_off(int col0, int lane) {
+    const int col = col0 + (lane & 31), h = lane >> 5;
+    return (8 * h) * 1024 + (((col >> 2) ^ (8 * h)) << 4) + ((col & 3) << 2);
+  }
+};
+
+// Lane l's fragment of an M/N-contiguous operand in sub-step ks (rows 16 ks
+// + 8 (l/32) .. +7 of its column), rounded to Tag's type.
+template <class Tag>
+__device__ __forceinline__ u32x4 read_f32_frag_mn(const char* slot, int off, int ks) {
+  const float* q = reinterpret_cast<const float*>(slot + off + ks * 16 * 1024);
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = q[e * 256];
+  return u32x4{cvt_pk(Tag{}, v[0], v[1]), cvt_pk(Tag{}, v[2], v[3]), cvt_pk(Tag{}, v[4], v[5]),
+               cvt_pk(Tag{}, v[6], v[7])};
+}
+
+template <bool MN, int NFRAG>
+struct PpF32Op {
+  using type = PpOperand<false, NFRAG>;
+};
+template <int NFRAG>
+struct PpF32Op<true, NFRAG> {
+  using type = PpF32MN;
+};
+
+template <class Tag, int EPI, bool AMN, bool BMN>
 __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_f32_kernel(const GemmArgs p) {
   using C = PingPongCfg;
   using At = typename C::At;
@@ -59,17 +116,23 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_f32_kernel(const
   schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
 
-  PpOperand<false, C::TM> a;
-  PpOperand<false, C::TN> b;
-  a.init_load(p.A, p.lda, m0, lw, lane, 4);
-  b.init_load(p.B, p.ldb, n0, lw, lane, 4);
+  typename PpF32Op<AMN, C::TM>::type a;
+  typename PpF32Op<BMN, C::TN>::type b;
+  if constexpr (AMN) a.init_load(p.A, p.lda, m0, lw, lane);
+  else a.init_load(p.A, p.lda, m0, lw, lane, 4);
+  if constexpr (BMN) b.init_load(p.B, p.ldb, n0, lw, lane);
+  else b.init_load(p.B, p.ldb, n0, lw, lane, 4);
   int offA[C::TM], offB[C::TN];  // fragment offsets within a slot, sub-step 0
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
-    offA[i] = PpOperand<false, C::TM>::lds_off(wm * C::WTM + 32 * i + (lane & 31), 2 * (lane >> 5));
+    offA[i] = AMN ? PpF32MN::frag_off(wm * C::WTM + 32 * i, lane)
+                  : PpOperand<false, C::TM>::lds_off(wm * C::WTM + 32 * i + (lane & 31),
+                                                     2 * (lane >> 5));
 #pragma unroll
   for (int j = 0; j < C::TN; ++j)
-    offB[j] = PpOperand<false, C::TN>::lds_off(wn * C::WTN + 32 * j + (lane & 31), 2 * (lane >> 5));
+    offB[j] = BMN ? PpF32MN::frag_off(wn * C::WTN + 32 * j, lane)
+                  : PpOperand<false, C::TN>::lds_off(wn * C::WTN + 32 * j + (lane & 31),
+                                                     2 * (lane >> 5));
 
   acc_t acc[C::TM][C::TN];
 #pragma unroll
@@ -112,7 +175,10 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_f32_kernel(const
   u32x4 fa[KS][C::TM], fb[KS][C::TN];
   int h = 0;  // (2s) % 5: the slot of A of slice s
   for (int s = 0; s < KT; ++s) {
-    asm volatile("" : "+v"(a.row), "+v"(a.c0), "+v"(b.row), "+v"(b.c0));
+    if constexpr (AMN) asm volatile("" : "+v"(a.voff));
+    else asm volatile("" : "+v"(a.row), "+v"(a.c0));
+    if constexpr (BMN) asm volatile("" : "+v"(b.voff));
+    else asm volatile("" : "+v"(b.row), "+v"(b.c0));
     asm volatile("" : "+v"(offA[0]), "+v"(offA[1]), "+v"(offA[2]), "+v"(offA[3]),
                  "+v"(offB[0]), "+v"(offB[1]));
     const int sa = h, sb = h == 4 ? 0 : h + 1;
@@ -122,9 +188,11 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_f32_kernel(const
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i) fa[ks][i] = read_f32_frag<Tag>(pa, offA[i], ks);
+      for (int i = 0; i < C::TM; ++i)
+        fa[ks][i] = AMN ? read_f32_frag_mn<Tag>(pa, offA[i], ks) : read_f32_frag<Tag>(pa, offA[i], ks);
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) fb[ks][j] = read_f32_frag<Tag>(pb, offB[j], ks);
+      for (int j = 0; j < C::TN; ++j)
+        fb[ks][j] = BMN ? read_f32_frag_mn<Tag>(pb, offB[j], ks) : read_f32_frag<Tag>(pb, offB[j], ks);
     }
     if (group == 0) {
       if (s + 1 < KT) issue_b(s + 1, h >= 2 ? h - 2 : h + 3);  // B of s+1: (2s+3) % 5
@@ -152,20 +220,30 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_f32_kernel(const
   store_tile<C, EPI, false>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane);
 }
 
-template <class Tag>
-hipError_t launch_tag(const GemmArgs& a, hipStream_t s) {
+template <class Tag, bool AMN, bool BMN>
+hipError_t launch_layout(const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.tiles_m * a.tiles_n), block(PingPongCfg::THREADS);
-  if (a.epi == EPI_BETA0) return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_BETA0>, grid, block, s, a);
+  if (a.epi == EPI_BETA0)
+    return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_BETA0, AMN, BMN>, grid, block, s, a);
   if (a.epi == EPI_ACC_PLUS_C)
-    return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_ACC_PLUS_C>, grid, block, s, a);
-  return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_GENERAL>, grid, block, s, a);
+    return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_ACC_PLUS_C, AMN, BMN>, grid, block, s, a);
+  return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_GENERAL, AMN, BMN>, grid, block, s, a);
+}
+
+template <class Tag>
+hipError_t launch_tag(bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
+  // A is M-contiguous when stored transposed; B is N-contiguous when not.
+  if (!ta && tb) return launch_layout<Tag, false, false>(a, s);
+  if (!ta && !tb) return launch_layout<Tag, false, true>(a, s);
+  if (ta && tb) return launch_layout<Tag, true, false>(a, s);
+  return launch_layout<Tag, true, true>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_pp_f32(int dtype16, const GemmArgs& a, hipStream_t s) {
-  if (dtype16 == 0) return launch_tag<TagF16>(a, s);
-  return launch_tag<TagBF16>(a, s);
+hipError_t launch_pp_f32(int dtype16, bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
+  if (dtype16 == 0) return launch_tag<TagF16>(ta, tb, a, s);
+  return launch_tag<TagBF16>(ta, tb, a, s);
 }
 
 int pp_f32_slice() { return 32; }

@@ -240,22 +240,26 @@ def test_k16_tail_is_named(lib):
 
 
 def test_f32_operand_dtypes(lib, monkeypatch):
-    # whole 256x256 NT tiles, K a multiple of 32: the two-group kernel rounds
-    # fragments as it reads them
+    # whole 256x256 tiles in any layout, K a multiple of 32: the two-group
+    # kernel rounds fragments as it reads them
     assert _v(lib, M=8192, N=8192, K=8192, tB=1, dtype=lib.GEMM_DTYPE_F32_BF16) == lib.GEMM_OK
     assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 pingpong f32->bf16"
     assert _v(lib, M=4096, N=4096, K=4096 + 32, tB=1, dtype=2, beta=1.0, C=D0) == lib.GEMM_OK
     assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 NT epi=acc+c pingpong f32->f16"
-    # otherwise (other layouts, K not a multiple of 32, rows not 16-byte
-    # aligned) the 128x128 ring kernel stages both operands through registers
-    # and rounds them there; a K tail makes it masked
-    for kw in (dict(tB=0), dict(tA=1, tB=1), dict(tB=1, K=8192 + 16),
-               dict(tB=1, lda=8192 + 2)):
+    for tA, tB, ops in ((0, 0, "NN"), (1, 0, "TN"), (1, 1, "TT")):
+        assert _v(lib, M=4096, N=4096, K=4096, tA=tA, tB=tB, dtype=3) == lib.GEMM_OK
+        assert lib.gemm_last_path() == \
+            f"mfma t256x256x64 w2x4 a32x32x16 {ops} epi=beta0 pingpong f32->bf16"
+    # otherwise (edges, K not a multiple of 32, rows not 16-byte aligned) the
+    # 128x128 ring kernel stages both operands through registers and rounds
+    # them there; a K tail makes it masked
+    for kw in (dict(tB=0, M=8192 + 256 + 8), dict(tA=1, tB=1, N=8192 - 8),
+               dict(tB=1, K=8192 + 16), dict(tB=1, lda=8192 + 2)):
         args = dict(M=8192, N=8192, K=8192, dtype=lib.GEMM_DTYPE_F32_BF16)
         args.update(kw)
         assert _v(lib, **args) == lib.GEMM_OK
         path = lib.gemm_last_path()
-        masked = " masked" if "K" in kw else ""
+        masked = " masked" if ("K" in kw or "M" in kw or "N" in kw) else ""
         assert path.startswith("mfma t128x128x64 w2x2 a32x32x16") and path.endswith(
             f" ring{masked} f32->bf16 staged (A, B: float32 values rounded in registers)"), (kw, path)
     # large pitches (64-bit addressing) keep the masked general kernel

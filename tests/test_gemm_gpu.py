@@ -222,23 +222,28 @@ def test_f32_operands_equal_prerounded_16bit_bitwise(dtype):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_f32_operands_pingpong(dtype, monkeypatch):
-    """Whole 256x256 NT tiles of float32 operands take the two-group kernel,
-    which rounds each fragment as it reads it from LDS: one slice of 32, two,
-    an odd count, and many; every epilogue; against the oracle."""
+    """Whole 256x256 tiles of float32 operands take the two-group kernel in
+    every layout, which rounds each fragment as it reads it from LDS: one
+    slice of 32, two, an odd count, and many; every epilogue; padded leading
+    dimensions; against the oracle."""
     monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
     seed = 6500
-    for K in (32, 64, 96, 1056):
-        for alpha, beta in [(1.0, 0.0), (1.0, 1.0), (1.5, -0.5)]:
-            seed += 1
-            cfg = workloads.Config(f"f32pp{seed}", 512, 256, K, "f32_" + dtype, 0, 1, alpha,
-                                   beta, "uniform", seed, ldd=256 + 4 * (seed % 2))
-            r = run(cfg)
-            assert "pingpong f32->" + dtype in r.path and "masked" not in r.path, r.path
-            r.check()
-            r.check_padding_untouched()
-    # other layouts, K not a multiple of 32, or 8-byte rows: the 128x128 ring
+    for (tA, tB) in [(0, 1), (0, 0), (1, 1), (1, 0)]:
+        for K in (32, 64, 96, 1056):
+            for alpha, beta in [(1.0, 0.0), (1.0, 1.0), (1.5, -0.5)]:
+                seed += 1
+                pad = 4 * (seed % 3)
+                cfg = workloads.Config(f"f32pp{seed}", 512, 256, K, "f32_" + dtype, tA, tB, alpha,
+                                       beta, "uniform", seed, ldd=256 + 4 * (seed % 2),
+                                       lda=(512 if tA else K) + pad,
+                                       ldb=(K if tB else 256) + pad)
+                r = run(cfg)
+                assert "pingpong f32->" + dtype in r.path and "masked" not in r.path, r.path
+                r.check()
+                r.check_padding_untouched()
+    # M or N edges, K not a multiple of 32, or 8-byte rows: the 128x128 ring
     # kernel, both operands staged and rounded in registers
-    for (tA, tB, K, ldb) in [(0, 0, 64, None), (1, 1, 64, None), (0, 1, 48, None),
+    for (tA, tB, K, ldb) in [(0, 0, 48, None), (1, 1, 40, None), (0, 1, 48, None),
                              (0, 1, 64, 66)]:
         seed += 1
         cfg = workloads.Config(f"f32pp{seed}", 512, 256, K, "f32_" + dtype, tA, tB, 1.0, 0.0,
@@ -307,26 +312,29 @@ def _tie_heavy_f32(shape, dtype, rng):
     return torch.tensor(x.astype(np.float32).reshape(shape))
 
 
+@pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 1), (1, 0)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_f32_pingpong_rounding_bitwise(dtype, monkeypatch):
+def test_f32_pingpong_rounding_bitwise(dtype, tA, tB, monkeypatch):
     """In-register rounding of the two-group kernel against the oracle's
-    rounding: D from float32 operands must equal, bitwise, D of the 16-bit
-    kernel fed the operands the oracle rounds (same tile, same sum order)."""
+    rounding, in every layout (M/N-contiguous operands are read down their
+    float32 K-rows): D from float32 operands must equal, bitwise, D of the
+    16-bit kernel fed the operands the oracle rounds (same tile, same sum
+    order)."""
     monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
-    rng = np.random.default_rng(44)
+    rng = np.random.default_rng(44 + 2 * tA + tB)
     M, N, K = 256, 512, 192  # K whole 64-slices: both sides on the two-group design
-    A32 = _tie_heavy_f32((M, K), dtype, rng)
-    B32 = _tie_heavy_f32((N, K), dtype, rng)
+    A32 = _tie_heavy_f32((K, M) if tA else (M, K), dtype, rng)
+    B32 = _tie_heavy_f32((N, K) if tB else (K, N), dtype, rng)
     code = 0 if dtype == "f16" else 1
 
     def oracle_rounded(x):
         bits = oracle.round_f32_bits(x.numpy().reshape(-1), code)
         return torch.tensor(oracle.decode_bits(bits, code).astype(np.float32).reshape(x.shape))
 
-    cfg32 = workloads.Config("f32tie", M, N, K, "f32_" + dtype, 0, 1, 1.0, 0.0, "uniform", 1)
+    cfg32 = workloads.Config("f32tie", M, N, K, "f32_" + dtype, tA, tB, 1.0, 0.0, "uniform", 1)
     r32 = run(cfg32, workloads.make_inputs(cfg32, A_src=A32, B_src=B32))
     assert "pingpong f32->" + dtype in r32.path, r32.path
-    cfg16 = workloads.Config("f32tie16", M, N, K, dtype, 0, 1, 1.0, 0.0, "uniform", 1)
+    cfg16 = workloads.Config("f32tie16", M, N, K, dtype, tA, tB, 1.0, 0.0, "uniform", 1)
     r16 = run(cfg16, workloads.make_inputs(cfg16, A_src=oracle_rounded(A32),
                                            B_src=oracle_rounded(B32)))
     # Same tile and slice order; the 16-bit kernel multiplies on 16x16x32
