@@ -69,7 +69,7 @@ struct GemmByteArgs {
   int a_vec16, b_vec16;    // base and row pitch multiples of 16 bytes
   int cd_vec16;            // D (and C when read): base and row pitch multiples of 16 bytes
   int tiles_m, tiles_n, group_m;
-  int pingpong;  // whole 256x256 NT tiles with 16-byte C/D rows: the two-group kernel
+  int pingpong;  // the two-group kernel: 1 on whole 256x256 tiles, 2 with edge tiles
 };
 enum ByteKind : int { BYTE_I8 = 0, BYTE_F8E4M3 = 1, BYTE_F8E5M2 = 2 };
 

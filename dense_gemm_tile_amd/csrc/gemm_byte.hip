@@ -29,7 +29,7 @@
 //    into their K-contiguous LDS rows byte by byte;
 //  * out-of-range elements are staged as zeros (their products are zero), C
 //    loads and D stores are predicated.
-#include "gemm_mfma_pingpong.h"
+#include "gemm_ring.h"
 
 #include <cstdint>
 #include <type_traits>
@@ -127,6 +127,7 @@ __device__ inline v2i ds_read_tr8(const char* p) {
 // 128-byte LDS row holds two sub-steps (chunk 4 ks + l / 16).
 struct KindI8x16 {
   static constexpr int ATOM = 16;
+  static constexpr int KIND_ID = 1;  // distinct per two-group kind (template tags)
   using acc_t = i32x4;
   using frag_t = i32x4;
   static constexpr int KATOM = 64;
@@ -157,6 +158,7 @@ struct KindI8x16 {
 template <int FMT>
 struct KindF8x16 {
   static constexpr int ATOM = 16;
+  static constexpr int KIND_ID = 2 + FMT;
   using acc_t = f32x4;
   using frag_t = i32x8;
   static constexpr int KATOM = 128;
@@ -194,7 +196,9 @@ struct KindF8x16 {
 // row per atom; lanes l and l^1 swap one chunk so that every store
 // instruction writes whole 128-byte rows. All C values of a row of atoms are
 // read before its first D store (C may be D).
-template <class Kind, class C>
+// MASK (edge tiles, N a multiple of 4): C is read and D written only at rows
+// below M and column quads below N.
+template <class Kind, class C, bool MASK = false>
 __device__ inline void byte_store_pairs16(const GemmByteArgs& p, int r0, int c0,
                                           typename Kind::acc_t (&acc)[C::TM][C::TN], int lane) {
   static_assert(Kind::ATOM == 16 && C::TN % 2 == 0, "pairs of 16x16 atoms");
@@ -213,9 +217,10 @@ __device__ inline void byte_store_pairs16(const GemmByteArgs& p, int r0, int c0,
     for (int q = 0; q < NP; ++q)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        cv[q][h] = p.read_c ? *reinterpret_cast<const u32x4_t*>(Cb + (int64_t)(r + h) * p.ldc + c0 +
-                                                                  32 * q + col)
-                            : u32x4_t{0u, 0u, 0u, 0u};
+        cv[q][h] = p.read_c && (!MASK || (r + h < p.M && c0 + 32 * q + col < p.N))
+                       ? *reinterpret_cast<const u32x4_t*>(Cb + (int64_t)(r + h) * p.ldc + c0 +
+                                                           32 * q + col)
+                       : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
       // (whole-vector casts: a bit cast of one element of a vector reference
@@ -240,6 +245,7 @@ __device__ inline void byte_store_pairs16(const GemmByteArgs& p, int r0, int c0,
           const float v = h == 0 ? (odd ? w[k] : x[k]) : (odd ? y[k] : w[k]);
           o[k] = Kind::combine(p, __builtin_bit_cast(unsigned, v), cv[q][h][k]);
         }
+        if (MASK && !(r + h < p.M && c0 + 32 * q + col < p.N)) continue;
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(Db + (int64_t)(r + h) * p.ldd + c0 + 32 * q + col);
         if (c_is_d) *dst = o;
         else __builtin_nontemporal_store(o, dst);
@@ -428,28 +434,62 @@ __global__ void __launch_bounds__(kThreads) gemm_byte_kernel(const GemmByteArgs 
 // those 8 rows, and the next group's, on all 64 banks. Instruction i of wave
 // lw fills K-rows 32 lw + 4i .. +3, lane l chunk slot l % 16 of row
 // 32 lw + 4i + l / 16.
-template <int NFRAG>
+// MASK (edge tiles): pieces whose columns start at or past the operand's
+// M (or N), or whose K-row is at or past K, read as zeros (out-of-range
+// offset from a resource that ends at the operand's last byte); M (or N)
+// must then be a multiple of 16. TAG is unused: it gives each masked kernel
+// its own specialization (this compiler's host pass dropped the kernels
+// that shared one with an earlier kernel).
+template <int NFRAG, bool MASK = false, int TAG = 0>
 struct PpByteMN {
   const char* base;  // tile's first column (M or N index), K = 0
   int64_t ld;        // row pitch in bytes
   int voff[4];       // by i & 1 and i >= 4 (they set r & 7 and bit 4 of r)
   int off[NFRAG];    // transposed-read offset of each atom, sub-step 0
+  int ccol[4];       // (MASK) first column of the piece of voff[q], from the tile's
+  int crem, krem0;   // (MASK) columns left from the tile's first column; K-rows
+                     //    left from this lane's first K-row of slice 0 (K - 32 lw - l/16)
+  int klim;          // (MASK) K
 
   __device__ static inline int swz(int r) { return (r & 7) ^ (8 * ((r >> 4) & 1)); }
-  __device__ inline void init_load(const void* X, int64_t ld_, int c0, int lw, int lane) {
+  __device__ inline void init_load(const void* X, int64_t ld_, int c0, int lw, int lane,
+                                   int clim = 0, int K = 0) {
     base = static_cast<const char*>(X) + c0;
     ld = ld_;
     const int rsub = lane >> 4, p = lane & 15;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      voff[q] = (int)((32 * lw + rsub) * ld) + ((p ^ swz(4 * (q & 1) + rsub + 16 * (q >> 1))) << 4);
+    for (int q = 0; q < 4; ++q) {
+      const int chunk = p ^ swz(4 * (q & 1) + rsub + 16 * (q >> 1));
+      voff[q] = (int)((32 * lw + rsub) * ld) + (chunk << 4);
+      ccol[q] = chunk << 4;
+    }
+    crem = clim - c0;
+    krem0 = K - 32 * lw - rsub;
+    klim = K;
   }
   __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
     // the slice's first K-row is folded into the resource base
     const char* b = base + (int64_t)slice * 128 * ld;
     const int q = (i & 1) | ((i >= 4) << 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(b), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
-                                             16, voff[q], (int)(4 * i * ld), 0, 0);
+    if constexpr (!MASK) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(b), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
+                                               16, voff[q], (int)(4 * i * ld), 0, 0);
+    } else {
+      // This lane's K-row: slice*128 + 32 lw + 4 i + l/16; the record count
+      // ends at the operand's last byte (K-row K-1, column clim-1), counted
+      // from b, so the offsets stay in 32 bits with nothing in soffset.
+      const int krem = krem0 - slice * 128 - 4 * i;
+      const int voffm = (krem > 0 && ccol[q] < crem) ? voff[q] + (int)(4 * i * ld) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(b, nrec_slice(slice)),
+                                               (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024), 16, voffm,
+                                               0, 0, 0);
+    }
+  }
+  // Record count from the slice's base to the end of the operand's last
+  // K-row's valid columns.
+  __device__ inline unsigned nrec_slice(int slice) const {
+    const int64_t n = (int64_t)(klim - 1 - slice * 128) * ld + crem;
+    return n <= 0 ? 0u : (n > 0x7FFFFFFC ? 0x7FFFFFFCu : (unsigned)n);
   }
   // Lane l (group g = l / 16, t = l % 16) names K-row k = 16 g + t / 2,
   // columns col0 + 8 (t & 1) .. +7 of atom t's 16 columns.
@@ -461,6 +501,40 @@ struct PpByteMN {
       const int col = col0 + 16 * a;
       off[a] = k * 256 + (((col >> 4) ^ swz(k)) << 4) + 8 * (t & 1);
     }
+  }
+};
+
+// Masked loads of a K-contiguous 1-byte operand on edge tiles of the
+// two-group kernel: the LDS placement of PpOperand<false, N, 16> with 1-byte
+// elements (instruction i of wave lw: rows 64 lw + 8i .. +7 of the tile,
+// lane l chunk slot l % 8 of row 64 lw + 8i + l/8), but each piece addressed
+// through the voffset alone from the tile's first row, so that pieces in
+// rows at or past the operand's last, or starting at or past K, read as
+// zeros (out-of-range offset). K must be a multiple of 16.
+struct PpByteKMasked {
+  const char* base;  // tile's first row, K = 0
+  unsigned nrec;     // bytes from base to the operand's last byte
+  int ld, row, c0, c1, rrem, klim;
+
+  __device__ inline void init_load(const void* X, int64_t ld_, int r0, int rlim, int K, int lw,
+                                   int lane) {
+    base = static_cast<const char*>(X) + (int64_t)r0 * ld_;
+    ld = (int)ld_;
+    klim = K;
+    rrem = rlim - r0;
+    row = lw * 64 + (lane >> 3);
+    c0 = (lane & 7) ^ PpOperand<false, 1, 16>::swz(lane >> 3);
+    c1 = (lane & 7) ^ PpOperand<false, 1, 16>::swz(8 + (lane >> 3));
+    const int64_t n = rrem > 0 ? (int64_t)(rrem - 1) * ld_ + K : 0;
+    nrec = n > 0x7FFFFFFC ? 0x7FFFFFFCu : (unsigned)n;
+  }
+  __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
+    const int r = row + 8 * i;
+    const int k = slice * 128 + (((i & 1) ? c1 : c0) << 4);
+    const int voff = (r < rrem && k < klim) ? r * ld + k : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(base, nrec),
+                                             (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024), 16, voff, 0,
+                                             0, 0);
   }
 };
 
@@ -480,10 +554,15 @@ __device__ inline int pp_byte_frag_off(int row0, int lane) {
     return lds_off_b(row0 + (lane & 31), Kind::CHUNK0 * (lane >> 5));
 }
 
-// AMN / BMN: A stored [K][M] / B stored [K][N] (16-wide kinds only).
-template <class Kind, bool AMN, bool BMN>
+// AMN / BMN: A stored [K][M] / B stored [K][N] (16-wide kinds only). MASK:
+// edge tiles (M, N not multiples of 256, K of 128): pieces outside the
+// operands read as zeros, C and D accessed inside M x N only (K a multiple
+// of 16, N of 4, and the contiguous dimension of an M/N-contiguous operand
+// of 16).
+template <class Kind, bool AMN, bool BMN, bool MASK = false>
 __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(const GemmByteArgs p) {
   static_assert(Kind::ATOM == 16 || (!AMN && !BMN), "M/N-contiguous operands use 16-wide atoms");
+  static_assert(Kind::ATOM == 16 || !MASK, "edge tiles use 16-wide atoms");
   using C = PingPongCfgT<Kind::ATOM>;
   using At = typename C::At;
   using acc_t = typename Kind::acc_t;
@@ -497,28 +576,34 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
   schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
 
-  using OpA = std::conditional_t<AMN, PpByteMN<C::TM>, PpOperand<false, C::TM, Kind::ATOM>>;
-  using OpB = std::conditional_t<BMN, PpByteMN<C::TN>, PpOperand<false, C::TN, Kind::ATOM>>;
+  using OpKA = std::conditional_t<MASK, PpByteKMasked, PpOperand<false, C::TM, Kind::ATOM>>;
+  using OpKB = std::conditional_t<MASK, PpByteKMasked, PpOperand<false, C::TN, Kind::ATOM>>;
+  // (the tag: one specialization per masked kernel, see PpByteMN)
+  constexpr int TAG = MASK ? 4 * Kind::KIND_ID + 2 * AMN + BMN : 0;
+  using OpA = std::conditional_t<AMN, PpByteMN<C::TM, MASK, TAG>, OpKA>;
+  using OpB = std::conditional_t<BMN, PpByteMN<C::TN, MASK, TAG>, OpKB>;
   OpA a;
   OpB b;
   int offA[C::TM], offB[C::TN];  // fragment offsets within a slot, sub-step 0
   if constexpr (AMN) {
-    a.init_load(p.A, p.lda, m0, lw, lane);
+    a.init_load(p.A, p.lda, m0, lw, lane, p.M, p.K);
     a.init_read(wm * C::WTM, lane);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) offA[i] = a.off[i];
   } else {
-    a.init_load(p.A, p.lda, m0, lw, lane, 1);
+    if constexpr (MASK) a.init_load(p.A, p.lda, m0, p.M, p.K, lw, lane);
+    else a.init_load(p.A, p.lda, m0, lw, lane, 1);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) offA[i] = pp_byte_frag_off<Kind>(wm * C::WTM + At::M * i, lane);
   }
   if constexpr (BMN) {
-    b.init_load(p.B, p.ldb, n0, lw, lane);
+    b.init_load(p.B, p.ldb, n0, lw, lane, p.N, p.K);
     b.init_read(wn * C::WTN, lane);
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) offB[j] = b.off[j];
   } else {
-    b.init_load(p.B, p.ldb, n0, lw, lane, 1);
+    if constexpr (MASK) b.init_load(p.B, p.ldb, n0, p.N, p.K, lw, lane);
+    else b.init_load(p.B, p.ldb, n0, lw, lane, 1);
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) offB[j] = pp_byte_frag_off<Kind>(wn * C::WTN + At::N * j, lane);
   }
@@ -551,7 +636,7 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
   // Phases as in pp_mainloop: group 0 reads slice s in phase 2s+1 and
   // multiplies it in 2s+2, group 1 one phase later; A of slice t in slot
   // 2t % 5 (loaded by group 1), B in slot (2t+1) % 5 (loaded by group 0).
-  const int KT = p.K / 128;
+  const int KT = MASK ? (p.K + 127) / 128 : p.K / 128;
   if (group == 1) {
     issue(a, 0, 0);
     if (KT > 1) {
@@ -626,7 +711,7 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
   if (group == 0) pp_barrier();
 
   if constexpr (Kind::ATOM == 16) {
-    byte_store_pairs16<Kind, C>(p, m0 + wm * C::WTM, n0 + wn * C::WTN, acc, lane);
+    byte_store_pairs16<Kind, C, MASK>(p, m0 + wm * C::WTM, n0 + wn * C::WTN, acc, lane);
   } else {
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
@@ -641,6 +726,16 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_byte_kernel(cons
 template <class Kind, class KindPP>
 hipError_t launch_kind(bool ta, bool tb, const GemmByteArgs& a, hipStream_t s) {
   const dim3 grid(a.tiles_m * a.tiles_n);
+  if (a.pingpong == 2) {  // edge tiles
+    const dim3 block(PingPongCfg::THREADS);
+    if (!ta && tb)
+      return launch_kernel(gemm_pp_byte_kernel<KindPP, false, false, true>, grid, block, s, a);
+    if (!ta && !tb)
+      return launch_kernel(gemm_pp_byte_kernel<KindPP, false, true, true>, grid, block, s, a);
+    if (ta && tb)
+      return launch_kernel(gemm_pp_byte_kernel<KindPP, true, false, true>, grid, block, s, a);
+    return launch_kernel(gemm_pp_byte_kernel<KindPP, true, true, true>, grid, block, s, a);
+  }
   if (a.pingpong) {
     const dim3 block(PingPongCfg::THREADS);
     // A is M-contiguous when stored transposed; B is N-contiguous when not.

@@ -320,6 +320,26 @@ def test_byte_two_group_kernel_needs_16_byte_cd_rows(lib):
     assert "pingpong" not in lib.gemm_last_path()
 
 
+def test_byte_two_group_kernel_edge_tiles(lib):
+    # other shapes take the two-group kernel with edge tiles when K is a
+    # multiple of 16, N of 4, an M/N-contiguous operand's contiguous dimension
+    # of 16, and the grid has at least 4 tiles of 256x256
+    assert _v8(lib, M=1000, N=1000, K=1024, tB=1) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "i8 mfma t256x256x128 w2x4 a16x16x64 NT epi=beta0 pingpong masked"
+    assert _v(lib, M=1008, N=1008, K=1040, dtype=lib.GEMM_DTYPE_F8_E5M2) == lib.GEMM_OK
+    assert lib.gemm_last_path() == \
+        "fp8 e5m2 mfma t256x256x128 w2x4 a16x16x128 NN epi=beta0 pingpong masked"
+    for kw in (dict(K=1000, tB=1),            # K % 16 != 0
+               dict(N=1002, tB=1),            # N % 4 != 0
+               dict(N=1000),                  # B stored [K][N], N % 16 != 0
+               dict(M=1000, tA=1, tB=1),      # A stored [K][M], M % 16 != 0
+               dict(M=500, N=200, tB=1)):     # 2 tiles of 256x256
+        args = dict(M=1008, N=1008, K=1024)
+        args.update(kw)
+        assert _v8(lib, **args) == lib.GEMM_OK
+        assert lib.gemm_last_path().startswith("i8 mfma t128x128x128"), (kw, lib.gemm_last_path())
+
+
 def test_i8_form_checks_and_paths(lib):
     assert _v8(lib, tB=1) == lib.GEMM_OK
     assert lib.gemm_last_path() == "i8 mfma t128x128x128 w2x2 a32x32x32 NT epi=beta0"

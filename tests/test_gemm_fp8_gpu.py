@@ -171,3 +171,39 @@ def test_fp8_inplace_c_is_d(dt):
             assert "pingpong" not in path, path
         rep = oracle.check(D[:M, :N].astype(np.float64), D_ref, bound)
         assert rep["ok"], (dt, M, N, K, rep)
+
+
+@pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 1), (1, 0)])
+@pytest.mark.parametrize("dt", ["f8e4m3", "f8e5m2"])
+def test_fp8_pingpong_edge_tiles(dt, tA, tB):
+    """Shapes that do not tile 256x256 take the two-group kernel with edge
+    tiles (see the int8 test): edges on M and N, K tails, padded leading
+    dimensions, a general epilogue and C == D; against the oracle, D's
+    padding untouched; and small integers, exact in E4M3 with exact f32
+    sums, bitwise."""
+    seed = 1300 + 20 * (2 * tA + tB)
+    for (M, N, K) in [(608, 528, 400), (1040, 784, 272), (272, 1040, 1040)]:
+        seed += 1
+        lda = (M if tA else K) + (16 if seed % 2 else 0)
+        ldb = (K if tB else N) + 32
+        D, D_ref, bound, path = run_fp8(dt, M, N, K, tA, tB, 0.5, -1.0, seed=seed, lda=lda,
+                                        ldb=ldb, ldd=N + 4)
+        assert "pingpong masked" in path, path
+        assert oracle.check(D[:M, :N].astype(np.float64), D_ref, bound)["ok"], (dt, M, N, K)
+        assert np.all(D[:M, N:].view(np.uint32) == D_SENTINEL)
+    D, D_ref, bound, path = run_fp8(dt, 608, 528, 400, tA, tB, 1.5, -0.75, seed=seed + 1,
+                                    inplace=True)
+    assert "pingpong masked" in path, path
+    assert oracle.check(D[:608, :528].astype(np.float64), D_ref, bound)["ok"]
+    if dt == "f8e4m3":
+        rng = np.random.default_rng(18 + 2 * tA + tB)
+        M, N, K = 528, 784, 272
+        table = {-2: 0xC0, -1: 0xB8, 0: 0x00, 1: 0x38, 2: 0x40}
+        av = rng.integers(-2, 3, (M, K))
+        bv = rng.integers(-2, 3, (N, K))
+        enc = np.vectorize(lambda v: table[int(v)])
+        A = torch.from_numpy(np.ascontiguousarray(enc(av.T if tA else av).astype(np.uint8)))
+        B = torch.from_numpy(np.ascontiguousarray(enc(bv if tB else bv.T).astype(np.uint8)))
+        D, _, _, path = run_fp8("f8e4m3", M, N, K, tA, tB, 1.0, 0.0, A=A, B=B)
+        assert "pingpong masked" in path, path
+        assert np.array_equal(D[:M, :N], (av @ bv.T).astype(np.float32))

@@ -175,3 +175,27 @@ def test_i8_inplace_c_is_d_on_both_kernels():
     got, ref, path = run_i8(300, 200, 520, 1, 0, 5, -1, seed=932, inplace=True)
     assert "pingpong" not in path, path
     assert np.array_equal(got[:300, :200], ref)
+
+
+@pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 1), (1, 0)])
+def test_i8_pingpong_edge_tiles(tA, tB):
+    """Shapes that do not tile 256x256 (K a multiple of 16, N of 4, the
+    contiguous dimension of an M/N-contiguous operand of 16) take the
+    two-group kernel with edge tiles: pieces outside the operands read as
+    zeros, C and D accessed inside M x N only. Edges on M and N, K tails of
+    16 to 112 bytes past the last whole slice, padded leading dimensions,
+    both epilogues, C == D; bit-exact, D's padding untouched."""
+    seed = 1200 + 40 * (2 * tA + tB)
+    for (M, N, K) in [(608, 528, 400), (1040, 784, 272), (528, 784, 144), (272, 1040, 1040)]:
+        for alpha, beta in [(1, 0), (-7, 3)]:
+            seed += 1
+            lda = (M if tA else K) + (16 if seed % 2 else 0)
+            ldb = (K if tB else N) + (32 if seed % 3 == 0 else 0)
+            got, ref, path = run_i8(M, N, K, tA, tB, alpha, beta, seed=seed, lda=lda, ldb=ldb,
+                                    ldd=N + 4)
+            assert "pingpong masked" in path, path
+            assert np.array_equal(got[:M, :N], ref), (M, N, K, alpha, beta)
+            assert np.all(got[:M, N:] == SENTINEL)
+    got, ref, path = run_i8(608, 528, 400, tA, tB, -3, 2, seed=seed + 1, inplace=True)
+    assert "pingpong masked" in path, path
+    assert np.array_equal(got[:608, :528], ref)
