@@ -160,6 +160,9 @@ std::string pitch_reason(const char* name, const void* ptr, int64_t ld, int vw, 
 // Largest tile that still gives every CU work; grids that even 64x64 tiles
 // leave under-filled (fewer than 256 tiles) take 32x32 tiles with K split
 // over four wave groups once K holds a step of 64 for each group.
+// Tiles per round of the 256x256 grid (one workgroup per CU).
+constexpr int64_t kPpEdgeRound = 256;
+
 int choose_tile(int64_t M, int64_t N, int64_t K) {
   auto count = [&](int t) {
     const MfmaTileInfo& ti = mfma_tile_info(t);
@@ -437,11 +440,23 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     else if (a_elem || b_elem || src32) plan.masked = true;
   };
   plan_tile(tile);
-  // The 256x256 tile runs only whole tiles (the two-group kernel); a call
-  // that needs masking at that size takes the 128x128 masked kernel.
+  // The 256x256 tile runs on the two-group kernel: whole tiles, or edge
+  // tiles of 16-bit operands loaded in whole 16-byte pieces (16-byte rows,
+  // each operand's contiguous dimension a multiple of 8, 32-bit offsets)
+  // when the grid fills its last round of 256 CUs to at least 3/4 (forced
+  // 256x256 tiles skip that test); other calls that need masking at that
+  // size take the 128x128 kernels.
   if (tile == TILE_256x256 && plan.masked) {
-    tile = TILE_128x128;
-    plan_tile(tile);
+    const MfmaTileInfo& t256 = mfma_tile_info(TILE_256x256);
+    const int64_t n256 = ((M + t256.bm - 1) / t256.bm) * ((N + t256.bn - 1) / t256.bn);
+    const int64_t rounds = (n256 + kPpEdgeRound - 1) / kPpEdgeRound;
+    const bool fills = g_env.force_tile || 4 * n256 >= 3 * rounds * kPpEdgeRound;
+    const bool edges = !src32 && !a_elem && !b_elem && !big_pitch &&
+                       (transA ? M % 8 == 0 : K % 8 == 0) && (transB ? K % 8 == 0 : N % 8 == 0);
+    if (!(edges && fills)) {
+      tile = TILE_128x128;
+      plan_tile(tile);
+    }
   }
   const MfmaTileInfo& ti = mfma_tile_info(tile);
   plan.mfma = true;
@@ -452,9 +467,9 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   a.tiles_n = (int)((N + ti.bn - 1) / ti.bn);
   if ((int64_t)a.tiles_m * a.tiles_n > 0x7fffffff)
     return fail(GEMM_ERR_UNSUPPORTED, "too many output tiles for one launch");
-  // Whole 256x256 tiles (any operand layout) take the kernel with two wave
-  // groups (2x4 waves) and direct global->LDS loads.
-  const bool pingpong = tile == TILE_256x256 && !plan.masked;  // includes plan.pp_f32
+  // 256x256 tiles (any operand layout) take the kernel with two wave groups
+  // (2x4 waves) and direct global->LDS loads.
+  const bool pingpong = tile == TILE_256x256;  // includes plan.pp_f32
   // 128x128 tiles of 16-bit operands take the direct-to-LDS ring kernel,
   // edges, K tails and unaligned rows included; each operand is loaded
   // straight into LDS when its base and row pitch are multiples of 16 bytes

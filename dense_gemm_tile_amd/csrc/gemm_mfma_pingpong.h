@@ -107,22 +107,51 @@ __device__ __forceinline__ void pp_barrier() {
 }
 
 using pp_lds_ptr_t = __attribute__((address_space(3))) void*;
+
+// Out-of-range buffer offset: loads through it read zeros.
+constexpr int kOutOfRange = (int)0x80000000u;
+
+// A buffer resource over `base` whose record count is `nrec` bytes: offsets
+// at or past it read as zero.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, unsigned nrec) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nrec,
+                                           0x00020000);
+}
+
+// Record count for a resource based at `b` over an operand that starts at
+// `X` and whose stored extent is `ext` bytes: up to the end of the dword
+// (in memory, 4-byte aligned) that holds the operand's last byte, at most
+// 2^31 - 4 bytes.
+__device__ inline unsigned nrec_from(const char* X, int64_t ext, const char* b) {
+  const uintptr_t end = ((uintptr_t)X + (uintptr_t)ext + 3) & ~(uintptr_t)3;
+  const int64_t n = (int64_t)(end - (uintptr_t)b);
+  if (n <= 0) return 0u;
+  return n > 0x7FFFFFFC ? 0x7FFFFFFCu : (unsigned)n;
+}
+
 typedef short pp_i16x4 __attribute__((ext_vector_type(4)));
 
 // One operand's loads (by the wave group that loads it) and fragment reads
 // (by every wave). MN: the operand is stored with M (or N) contiguous.
 // NFRAG atoms of ATOM rows/columns per wave, starting at row0 of the tile.
-template <bool MN, int NFRAG, int ATOM = 32>
+// MASK (edge tiles, 16-bit elements): every piece is addressed through the
+// voffset alone from a resource that ends at the operand's last byte, and
+// pieces in rows (K-rows) past the operand or starting past its contiguous
+// dimension get an out-of-range offset, so they read as zeros; the
+// contiguous dimension must be a multiple of 8 (whole 16-byte pieces).
+template <bool MN, int NFRAG, int ATOM = 32, bool MASK = false>
 struct PpOperand;
 
-template <int NFRAG, int ATOM>
-struct PpOperand<false, NFRAG, ATOM> {
+template <int NFRAG, int ATOM, bool MASK>
+struct PpOperand<false, NFRAG, ATOM, MASK> {
   using C = PingPongCfgT<ATOM>;
   using At = typename C::At;
   // Load side: this lane's byte offset for instruction 0 and its chunk (for
   // the 16-wide atom, c1 for the odd instructions).
   const char* base;      // tile's first row (M or N index), K = 0
   int ld2, row, c0, c1;  // ld2: row pitch in bytes
+  int rmask, klim;       // (MASK) bit i: instruction i's row is inside the operand; K;
+  unsigned nrec;         //    bytes from base to the operand's end
   // Read side: byte offset of each atom's fragment within a slot, sub-step 0.
   int off[NFRAG];
 
@@ -152,12 +181,32 @@ struct PpOperand<false, NFRAG, ATOM> {
       c1 = 0;
     }
   }
+  // (MASK) the operand's extent from this tile: rlim rows (M or N), K.
+  __device__ inline void set_limits(int r0, int rlim, int K, int lw, int lane) {
+    const int rix = lw * 64 + (lane >> 3), rrem = rlim - r0;
+    rmask = 0;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) rmask |= (rix + 8 * i < rrem) << i;
+    klim = K;
+    const int64_t n = rrem > 0 ? (int64_t)(rrem - 1) * ld2 + 2 * (int64_t)K : 0;
+    nrec = n > 0x7FFFFFFC ? 0x7FFFFFFCu : (unsigned)n;
+  }
   __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
     const int chunk = ATOM == 16 ? ((i & 1) ? c1 : c0) : c0 ^ i;
-    const int voff = row + (chunk << 4);
-    const int soff = slice * 128 + i * 8 * ld2;  // a slice is 128 bytes of each row
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
-                                             16, voff, soff, 0, 0);
+    if constexpr (!MASK) {
+      const int voff = row + (chunk << 4);
+      const int soff = slice * 128 + i * 8 * ld2;  // a slice is 128 bytes of each row
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
+                                               16, voff, soff, 0, 0);
+    } else {
+      const int k = slice * 64 + chunk * 8;  // the piece's first K (16-bit elements)
+      const int voff = ((rmask >> i) & 1) && k < klim
+                           ? row + i * 8 * ld2 + slice * 128 + (chunk << 4)
+                           : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(base, nrec),
+                                               (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024), 16, voff,
+                                               0, 0, 0);
+    }
   }
   __device__ inline void init_read(int row0, int lane) {
     // The chunk of sub-step ks is (K / 8) * ks + koct, whose sub-step term
@@ -173,14 +222,17 @@ struct PpOperand<false, NFRAG, ATOM> {
   }
 };
 
-template <int NFRAG, int ATOM>
-struct PpOperand<true, NFRAG, ATOM> {
+template <int NFRAG, int ATOM, bool MASK>
+struct PpOperand<true, NFRAG, ATOM, MASK> {
   using C = PingPongCfgT<ATOM>;
   static constexpr int NV = ATOM == 16 ? 4 : 2;  // distinct load offsets
   const uint16_t* base;  // tile's first column (M or N index), K = 0
   int64_t ld;
   int voff[NV];          // by instruction i: i & 1 (and i >= 4 for the 16-wide atom)
   int off[NFRAG];
+  int cmask;             // (MASK) bit q: the piece of voff[q] starts inside the operand;
+  int crem, krem0, klim; //    columns left from the tile's first; K - this lane's first
+                         //    K row of slice 0; K
 
   // Chunk swizzle of K row r of a slot.
   __device__ static inline int swz(int r) {
@@ -198,13 +250,40 @@ struct PpOperand<true, NFRAG, ATOM> {
     for (int q = 0; q < NV; ++q)
       voff[q] = (int)((lw * 16 + hi) * ld * 2) + ((p ^ swz(2 * (q & 1) + hi + 8 * (q >> 1))) << 4);
   }
+  // (MASK) the operand's extent from this tile: clim columns (M or N), K.
+  __device__ inline void set_limits(int c0, int clim, int K, int lw, int lane) {
+    const int hi = lane >> 5, p = lane & 31;
+    crem = clim - c0;
+    cmask = 0;
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+      cmask |= (8 * (p ^ swz(2 * (q & 1) + hi + 8 * (q >> 1))) < crem) << q;
+    krem0 = K - 16 * lw - hi;
+    klim = K;
+  }
+  // (MASK) record count from the slice's base to the end of the operand's
+  // last K row's valid columns.
+  __device__ inline unsigned nrec_slice(int slice) const {
+    const int64_t n = 2 * ((int64_t)(klim - 1 - slice * C::BK) * ld + crem);
+    return n <= 0 ? 0u : (n > 0x7FFFFFFC ? 0x7FFFFFFCu : (unsigned)n);
+  }
   __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
     // The slice's first K row is folded into the resource base so that the
     // 32-bit offsets stay within 16 rows of the operand.
     const uint16_t* b = base + (int64_t)slice * C::BK * ld;
     const int q = ATOM == 16 ? (i & 1) | ((i >= 4) << 1) : (i & 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(b), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
-                                             16, voff[q], (int)(2 * i * ld * 2), 0, 0);
+    if constexpr (!MASK) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(b), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
+                                               16, voff[q], (int)(2 * i * ld * 2), 0, 0);
+    } else {
+      // This lane's K row is slice*64 + 16 lw + 2 i + l/32.
+      const int krem = krem0 - slice * C::BK - 2 * i;
+      const int voffm = (krem > 0 && ((cmask >> q) & 1)) ? voff[q] + (int)(2 * i * ld * 2)
+                                                         : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(b, nrec_slice(slice)),
+                                               (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024), 16, voffm,
+                                               0, 0, 0);
+    }
   }
   __device__ inline void init_read(int col0, int lane) {
     // Lane l (group g = l/16, s = l%16) of the first transposed read of
@@ -268,13 +347,13 @@ __device__ __forceinline__ void pp_multiply(typename C::At::acc_t (&acc)[C::TM][
   }
 }
 
-template <bool AMN, bool BMN, int ATOM>
+template <bool AMN, bool BMN, int ATOM, bool MASK = false>
 struct PingPongPipe {
   using C = PingPongCfgT<ATOM>;
   char* smem;
   int lw;  // wave index within its group
-  PpOperand<AMN, C::TM, ATOM> a;
-  PpOperand<BMN, C::TN, ATOM> b;
+  PpOperand<AMN, C::TM, ATOM, MASK> a;
+  PpOperand<BMN, C::TN, ATOM, MASK> b;
 
   __device__ inline void init(const GemmArgs& p, char* smem_, int m0, int n0, int group, int wave,
                               int lane, int wm, int wn) {
@@ -284,6 +363,10 @@ struct PingPongPipe {
     // every register the loop keeps is defined.
     a.init_load(static_cast<const uint16_t*>(p.A), p.lda, m0, lw, lane);
     b.init_load(static_cast<const uint16_t*>(p.B), p.ldb, n0, lw, lane);
+    if constexpr (MASK) {
+      a.set_limits(m0, p.M, p.K, lw, lane);
+      b.set_limits(n0, p.N, p.K, lw, lane);
+    }
     a.init_read(wm * C::WTM, lane);
     b.init_read(wn * C::WTN, lane);
   }
@@ -324,9 +407,11 @@ struct PingPongPipe {
     if constexpr (MN) {
 #pragma unroll
       for (int q = 0; q < Op::NV; ++q) asm volatile("" : "+v"(x.voff[q]));
+      if constexpr (MASK) asm volatile("" : "+v"(x.cmask), "+v"(x.krem0));
     } else {
       asm volatile("" : "+v"(x.row), "+v"(x.c0));
       if constexpr (ATOM == 16) asm volatile("" : "+v"(x.c1));
+      if constexpr (MASK) asm volatile("" : "+v"(x.rmask));
     }
   }
 };
@@ -340,11 +425,12 @@ struct PingPongPipe {
 // this compiler's host pass rejects a second kernel (same Tag, other
 // epilogue) calling a device function template specialization already
 // instantiated for the first one.
-template <class C, class Tag, int EPI, bool AMN, bool BMN>
+template <class C, class Tag, int EPI, bool AMN, bool BMN, bool MASK>
 __device__ __forceinline__ void pp_mainloop(typename C::At::acc_t (&acc)[C::TM][C::TN],
-                                            const PingPongPipe<AMN, BMN, C::At::M>& pipe, int K,
-                                            int group) {
-  const int KT = K / C::BK;  // whole slices (unmasked kernel)
+                                            const PingPongPipe<AMN, BMN, C::At::M, MASK>& pipe,
+                                            int K, int group) {
+  // Slices: whole ones, or (edge tiles) the last one cut short and zero-filled.
+  const int KT = MASK ? (K + C::BK - 1) / C::BK : K / C::BK;
   // Prologue: group 1 requests A of slices 0 and 1, group 0 B of slice 0.
   if (group == 1) {
     pipe.issue_a(0, 0);
@@ -365,7 +451,7 @@ __device__ __forceinline__ void pp_mainloop(typename C::At::acc_t (&acc)[C::TM][
   }
 
   Frags<C> f[C::KSTEPS];
-  PingPongPipe<AMN, BMN, C::At::M> pp = pipe;
+  PingPongPipe<AMN, BMN, C::At::M, MASK> pp = pipe;
   int h = 0;  // (2s) % 5: the slot of A of slice s
   for (int s = 0; s < KT; ++s) {
     pp.launder();
@@ -399,7 +485,10 @@ __device__ __forceinline__ void pp_mainloop(typename C::At::acc_t (&acc)[C::TM][
   if (group == 0) pp_barrier();  // matches group 1's idle phase: same barrier count
 }
 
-template <class Tag, int EPI, bool AMN, bool BMN>
+// MASK: edge tiles (M, N, K need not be multiples of the tile) for 16-bit
+// operands whose contiguous dimension is a multiple of 8: loads past the
+// operand read zeros and the epilogue stores only inside M x N.
+template <class Tag, int EPI, bool AMN, bool BMN, bool MASK = false>
 __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_mfma_pingpong_kernel(const GemmArgs p) {
   using C = PingPongCfgT<AMN ? 32 : 16>;  // the atom: see the notes at the top
   using At = typename C::At;
@@ -417,7 +506,7 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_mfma_pingpong_kerne
   const int m0 = tm * C::BM;
   const int n0 = tn * C::BN;
 
-  PingPongPipe<AMN, BMN, C::At::M> pipe;
+  PingPongPipe<AMN, BMN, C::At::M, MASK> pipe;
   pipe.init(p, smem, m0, n0, group, wave, lane, wm, wn);
 
   acc_t acc[C::TM][C::TN];
@@ -428,8 +517,8 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_mfma_pingpong_kerne
 #pragma unroll
       for (int v = 0; v < At::NACC; ++v) acc[i][j][v] = 0.0f;
 
-  pp_mainloop<C, Tag, EPI, AMN, BMN>(acc, pipe, p.K, group);
-  store_tile<C, EPI, false>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane);
+  pp_mainloop<C, Tag, EPI, AMN, BMN, MASK>(acc, pipe, p.K, group);
+  store_tile<C, EPI, MASK>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane);
 }
 
 }  // namespace dgt

@@ -61,26 +61,6 @@ struct RingCfg {
 };
 using Ring128Cfg = RingCfg<128>;
 
-constexpr int kOutOfRange = (int)0x80000000u;
-
-// A buffer resource over `base` whose record count is `nrec` bytes: offsets
-// at or past it read as zero.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, unsigned nrec) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nrec,
-                                           0x00020000);
-}
-
-// Record count for a resource based at `b` over an operand that starts at
-// `X` and whose stored extent is `ext` bytes: up to the end of the dword
-// (in memory, 4-byte aligned) that holds the operand's last byte, at most
-// 2^31 - 4 bytes.
-__device__ inline unsigned nrec_from(const char* X, int64_t ext, const char* b) {
-  const uintptr_t end = ((uintptr_t)X + (uintptr_t)ext + 3) & ~(uintptr_t)3;
-  const int64_t n = (int64_t)(end - (uintptr_t)b);
-  if (n <= 0) return 0u;
-  return n > 0x7FFFFFFC ? 0x7FFFFFFCu : (unsigned)n;
-}
-
 // Zero the 16-bit elements of a 16-byte piece from index nv (0..8) on.
 __device__ inline u32x4 keep_first(u32x4 v, int nv) {
 #pragma unroll

@@ -387,6 +387,34 @@ def test_tile_and_epilogue_choice(lib):
     assert lib.gemm_last_path() == "mfma t32x32x64k4 w1x1 a32x32x16 NN epi=general ksplit4"
 
 
+def test_two_group_kernel_edge_tiles(lib, monkeypatch):
+    # 256x256 tiles that need masking stay on the two-group kernel when the
+    # operands load in whole 16-byte pieces and the grid fills its last round
+    # of 256 CUs to at least 3/4
+    assert _v(lib, M=4000, N=4000, K=4096, tB=1, dtype=1) == lib.GEMM_OK  # 256 tiles
+    assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a16x16x32 NT epi=beta0 pingpong masked"
+    assert _v(lib, M=8000, N=8000, K=8200, beta=1.0, C=D0) == lib.GEMM_OK  # 1024 tiles
+    assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a16x16x32 NN epi=acc+c pingpong masked"
+    assert _v(lib, M=4000, N=3904, K=4100, tA=1) == lib.GEMM_OK  # K tail: both M/N-contiguous
+    assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 TN epi=beta0 pingpong masked"
+    for kw in (dict(M=4097, N=4097),           # 289 tiles: the second round 13 % full
+               dict(K=4100),                   # K-contiguous operand, K % 8 != 0
+               dict(M=4004, tA=1),             # A stored [K][M], M % 8 != 0
+               dict(N=4004, tB=0),             # B stored [K][N], N % 8 != 0
+               dict(A=A0 + 2),                 # A not 16-byte aligned
+               dict(dtype=2)):                 # float32 operands
+        args = dict(M=4000, N=4000, K=4096, tB=1)
+        args.update(kw)
+        assert _v(lib, **args) == lib.GEMM_OK
+        assert lib.gemm_last_path().startswith("mfma t128x128x64"), (kw, lib.gemm_last_path())
+    # a forced 256x256 tile skips the fill test
+    monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
+    assert _v(lib, M=4097, N=4097, K=4096, tB=1) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" pingpong masked"), lib.gemm_last_path()
+    assert _v(lib, M=96, N=40, K=20, tA=1, tB=0) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" pingpong masked"), lib.gemm_last_path()
+
+
 def test_k_split_tile_choice(lib):
     # 64x64 tiles would leave CUs idle: 32x32 tiles, K split over 4 wave groups
     assert _v(lib, M=1000, N=500, K=256) == lib.GEMM_OK

@@ -613,6 +613,76 @@ def test_pingpong_path_slice_counts(dtype, layout, monkeypatch):
             r.check_padding_untouched()
 
 
+PP_EDGE_SHAPES = {
+    # (M, N, K, C == D); every layout's contiguous dimensions are multiples of 8
+    "any": [(520, 264, 1000, False), (264, 776, 72, True), (8, 520, 8, False),
+            (768, 40, 200, False), (1032, 1288, 136, True), (256, 256, 24, False)],
+    # edges that only the layout's M/N-contiguous operands allow
+    (0, 1): [(301, 299, 136, False)],
+    (0, 0): [(301, 264, 200, True)],
+    (1, 1): [(264, 299, 200, False)],
+    (1, 0): [(264, 264, 137, False), (264, 520, 3, True)],
+}
+
+
+@pytest.mark.parametrize("layout", [(0, 1), (0, 0), (1, 1), (1, 0)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_pingpong_edge_tiles(dtype, layout, monkeypatch):
+    """Edge tiles on the two-group kernel: M and N edges inside a wave's
+    block and ones that leave whole waves or a whole wave group outside,
+    K tails inside a 64-deep slice and K shorter than one slice (pieces past
+    the operand read as zeros; each 16-byte piece is whole because the
+    operand's contiguous dimension is a multiple of 8), every epilogue,
+    C == D, padded leading dimensions; D untouched outside M x N."""
+    monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
+    tA, tB = layout
+    seed = 4700 + 100 * (2 * tA + tB) + (50 if dtype == "bf16" else 0)
+    for (M, N, K, inplace) in PP_EDGE_SHAPES["any"] + PP_EDGE_SHAPES[layout]:
+        for alpha, beta in [(1.0, 0.0), (1.0, 1.0), (-1.5, 0.5)]:
+            seed += 1
+            lda = _pad8(M if tA else K) + (8 if seed % 2 else 0)
+            ldb = _pad8(K if tB else N) + (16 if seed % 3 == 0 else 0)
+            ip = inplace and beta != 0.0  # C == D needs an epilogue that reads C
+            ld = N + (0 if ip else 4)
+            cfg = workloads.Config(f"ppedge{seed}", M, N, K, dtype, tA, tB, alpha, beta,
+                                   "uniform", seed, lda=lda, ldb=ldb, ldc=ld, ldd=ld,
+                                   inplace=ip)
+            r = run(cfg)
+            assert r.path.startswith("mfma t256x256x64") and r.path.endswith(" pingpong masked"), \
+                r.path
+            r.check()
+            r.check_padding_untouched()
+
+
+@pytest.mark.parametrize("layout", [(0, 1), (0, 0), (1, 1), (1, 0)])
+def test_pingpong_edge_tiles_integer_inputs_bitwise(layout, monkeypatch):
+    """Integer-valued operands make every partial sum exact: with edge tiles
+    on M, N and a K tail, D must equal the exact product bitwise (zeros read
+    past the operands add nothing; a piece read from the wrong place or a
+    lost slice shows up)."""
+    monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
+    tA, tB = layout
+    rng = np.random.default_rng(61 + 2 * tA + tB)
+    M, N, K = 520, 776, 1000
+    A = rng.integers(-2, 3, (M, K)).astype(np.float32)
+    B = rng.integers(-2, 3, (K, N)).astype(np.float32)
+    _exact_case("bf16", tA, tB, M, N, K, A, B, "mfma t256x256x64")
+
+
+@pytest.mark.parametrize("shape", [(4000, 4000, 4096, 0, 1, 0.0), (4000, 3904, 4100, 1, 0, 1.0)])
+def test_pingpong_edge_tiles_full_size_sampled(shape):
+    """A 256-tile grid of edge tiles at full size, planned without forcing:
+    4000^2 x 4096 NT, and TN with an N edge and a K tail reading C; rows that
+    touch every 256-row tile band and one element in every 64x64 block."""
+    M, N, K, tA, tB, beta = shape
+    cfg = workloads.Config(f"ppedge{M}x{N}x{K}", M, N, K, "bf16", tA, tB, 1.0, beta, "uniform",
+                           77 + tA)
+    r = run(cfg)
+    assert r.path.startswith("mfma t256x256x64") and r.path.endswith(" pingpong masked"), r.path
+    r.check(rows=sample_rows(cfg.M, 256, 1))
+    r.check_elements(block=64, seed=cfg.seed)
+
+
 @pytest.mark.parametrize("layout", [(0, 1), (0, 0), (1, 1)])
 def test_wide_and_scalar_epilogues_agree(layout):
     """Whole tiles store D with 16-byte accesses when D (and C) allow it and
