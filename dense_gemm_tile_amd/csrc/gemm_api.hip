@@ -168,7 +168,14 @@ int choose_tile(int64_t M, int64_t N, int64_t K) {
     const MfmaTileInfo& ti = mfma_tile_info(t);
     return ((M + ti.bm - 1) / ti.bm) * ((N + ti.bn - 1) / ti.bn);
   };
-  if (count(TILE_256x256) >= 256) return TILE_256x256;
+  // 256x256 tiles also on grids that leave CUs idle, once K is long enough
+  // for their twice larger work per loaded byte to outweigh the idle CUs
+  // (measured against the 128x128 two-group form, same box, bf16: 192
+  // tiles 1.41x faster at K = 2048, 1.53-1.61x at K = 4096-8192; 128 tiles
+  // 1.03-1.11x at K = 2048-8192, 0.96x at K = 1024).
+  const int64_t n256 = count(TILE_256x256);
+  if (n256 >= 256 || (n256 >= 192 && K >= 1024) || (n256 >= 128 && K >= 2048))
+    return TILE_256x256;
   if (count(TILE_128x128) >= 128) return TILE_128x128;
   if (M <= 16 && N <= 16) return TILE_16x16;
   const MfmaTileInfo& k4 = mfma_tile_info(TILE_32x32K4);

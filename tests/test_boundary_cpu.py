@@ -191,31 +191,31 @@ def test_ring_modes(lib, monkeypatch):
         "mfma t128x128x64 w2x2 a32x32x16 NN epi=beta0 ring ksplit2 staged (A: row pitch")
     # more tiles than CUs: two workgroups per CU, of two wave groups taking
     # turns (both operands direct) or of one group (a staged operand)
-    assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_OK
+    assert _v(lib, M=4096, N=2048, K=1024, dtype=1) == lib.GEMM_OK
     assert lib.gemm_last_path() == "mfma t128x128x64 w2x4 a32x32x16 NN epi=beta0 ring two-group"
-    assert _v(lib, M=4096, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_OK
+    assert _v(lib, M=4096, N=2048, K=1024, dtype=1, lda=1025) == lib.GEMM_OK
     assert lib.gemm_last_path().startswith(
         "mfma t128x128x64 w2x2 a32x32x16 NN epi=beta0 ring staged (A: row pitch")
     monkeypatch.setenv("GEMM_RING_MODE", "shared")
     assert _v(lib, M=2048, N=2048, K=2048, dtype=1) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" ring")
     monkeypatch.setenv("GEMM_RING_MODE", "ksplit2")
-    assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_OK
+    assert _v(lib, M=4096, N=2048, K=1024, dtype=1) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" ring ksplit2")
     monkeypatch.setenv("GEMM_RING_MODE", "deep")
-    assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_OK
+    assert _v(lib, M=4096, N=2048, K=1024, dtype=1) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" ring deep")
     assert _v(lib, M=2048, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_ERR_UNSUPPORTED
     monkeypatch.setenv("GEMM_RING_MODE", "pp")
-    assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_OK
+    assert _v(lib, M=4096, N=2048, K=1024, dtype=1) == lib.GEMM_OK
     assert lib.gemm_last_path() == "mfma t128x128x64 w2x4 a32x32x16 NN epi=beta0 ring two-group"
     monkeypatch.setenv("GEMM_RING_MODE", "ppdeep")
-    assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_OK
+    assert _v(lib, M=4096, N=2048, K=1024, dtype=1) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" ring two-group deep")
     assert _v(lib, M=2048, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_ERR_UNSUPPORTED
     assert _v(lib, M=2048, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_ERR_UNSUPPORTED
     monkeypatch.setenv("GEMM_RING_MODE", "wide")
-    assert _v(lib, M=4096, N=2048, K=2048, dtype=1) == lib.GEMM_ERR_INVALID_ARG
+    assert _v(lib, M=4096, N=2048, K=1024, dtype=1) == lib.GEMM_ERR_INVALID_ARG
 
 
 def test_ragged_dims_stay_on_mfma_masked(lib):
@@ -383,6 +383,13 @@ def test_tile_and_epilogue_choice(lib):
     # A stored [K][M]: the two-group kernel keeps the 32x32x16 atom
     assert _v(lib, M=4096, N=4096, K=4096, tA=1, dtype=1) == lib.GEMM_OK
     assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 TN epi=beta0 pingpong"
+    # fewer 256x256 tiles than CUs: that tile still, once K is long enough
+    for M, N, K, tile in [(3072, 4096, 1024, 256), (3072, 4096, 512, 128),
+                          (1024, 8192, 2048, 256), (4096, 2048, 1024, 128),
+                          (2048, 2048, 8192, 128)]:
+        assert _v(lib, M=M, N=N, K=K, tB=1, dtype=1) == lib.GEMM_OK
+        assert lib.gemm_last_path().startswith(f"mfma t{tile}x{tile}x64"), \
+            (M, N, K, lib.gemm_last_path())
     assert _v(lib, M=512, N=512, K=512, alpha=1.5, beta=0.5) == lib.GEMM_OK
     assert lib.gemm_last_path() == "mfma t32x32x64k4 w1x1 a32x32x16 NN epi=general ksplit4"
 
