@@ -164,10 +164,11 @@ int byte_tile_m();
 int byte_tile_n();
 int byte_pp_tile();
 hipError_t launch_scale_c(const GemmArgs& a, hipStream_t stream);
-// Whole 256x256 tiles of float32 A and B (src32 calls, any layout), rounded
-// to f16 (dtype16 0) or bf16 (1) as fragments are read; K a multiple of
-// pp_f32_slice().
-hipError_t launch_pp_f32(int dtype16, bool transA, bool transB, const GemmArgs& a,
+// 256x256 tiles of float32 A and B (src32 calls, any layout), rounded to
+// f16 (dtype16 0) or bf16 (1) as fragments are read: whole tiles with K a
+// multiple of pp_f32_slice(), or (masked) edge tiles and K tails when each
+// operand's contiguous dimension is a multiple of 4.
+hipError_t launch_pp_f32(int dtype16, bool transA, bool transB, bool masked, const GemmArgs& a,
                          hipStream_t stream);
 int pp_f32_slice();
 

@@ -448,19 +448,22 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   };
   plan_tile(tile);
   // The 256x256 tile runs on the two-group kernel: whole tiles, or edge
-  // tiles of 16-bit operands loaded in whole 16-byte pieces (16-byte rows,
-  // each operand's contiguous dimension a multiple of 8, 32-bit offsets)
-  // when the grid fills its last round of 256 CUs to at least 3/4 (forced
-  // 256x256 tiles skip that test); other calls that need masking at that
-  // size take the 128x128 kernels.
+  // tiles whose operands load in whole 16-byte pieces (16-byte rows, each
+  // operand's contiguous dimension a multiple of 8 16-bit or 4 float32
+  // values, 32-bit offsets) when the grid fills its last round of 256 CUs to
+  // at least 3/4 (forced 256x256 tiles skip that test); other calls that
+  // need masking at that size take the 128x128 kernels.
   if (tile == TILE_256x256 && plan.masked) {
     const MfmaTileInfo& t256 = mfma_tile_info(TILE_256x256);
     const int64_t n256 = ((M + t256.bm - 1) / t256.bm) * ((N + t256.bn - 1) / t256.bn);
     const int64_t rounds = (n256 + kPpEdgeRound - 1) / kPpEdgeRound;
     const bool fills = g_env.force_tile || 4 * n256 >= 3 * rounds * kPpEdgeRound;
-    const bool edges = !src32 && !a_elem && !b_elem && !big_pitch &&
-                       (transA ? M % 8 == 0 : K % 8 == 0) && (transB ? K % 8 == 0 : N % 8 == 0);
-    if (!(edges && fills)) {
+    const int64_t q = 16 / esz;  // elements per 16-byte piece
+    const bool edges = !a_elem && !b_elem && !big_pitch &&
+                       (transA ? M % q == 0 : K % q == 0) && (transB ? K % q == 0 : N % q == 0);
+    if (edges && fills) {
+      plan.pp_f32 = src32;  // float32 operands: the f32 form of the kernel, masked
+    } else {
       tile = TILE_128x128;
       plan_tile(tile);
     }
@@ -679,7 +682,8 @@ hipError_t launch_plan(const Plan& plan, int dtype, int transA, int transB, hipS
   if (plan.noop) return hipSuccess;
   if (plan.scale_only) return launch_scale_c(plan.args, s);
   if (plan.byte8) return launch_byte(plan.byte_kind, transA != 0, transB != 0, plan.bargs, s);
-  if (plan.pp_f32) return launch_pp_f32(dtype & 1, transA != 0, transB != 0, plan.args, s);
+  if (plan.pp_f32)
+    return launch_pp_f32(dtype & 1, transA != 0, transB != 0, plan.masked, plan.args, s);
   if (plan.ring) return launch_ring128(dtype & 1, transA != 0, transB != 0, plan.args, s);
   if (plan.mfma)
     return launch_mfma(plan.tile, dtype & 1, transA != 0, transB != 0, plan.masked, plan.args, s);

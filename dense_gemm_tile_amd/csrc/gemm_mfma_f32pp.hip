@@ -1,5 +1,7 @@
-// Whole 256x256 tiles of float32 operands, in any of the four layouts, on the
-// two-group direct-to-LDS design of the 16-bit kernel. The operands reach
+// 256x256 tiles of float32 operands, in any of the four layouts, on the
+// two-group direct-to-LDS design of the 16-bit kernel: whole tiles, or edge
+// tiles (MASK) when each operand's contiguous dimension is a multiple of 4
+// (whole 16-byte pieces; pieces past the operand read as zeros, as there). The operands reach
 // LDS as float32 and are rounded to f16 or bf16
 // (nearest, ties to even) in registers as each fragment is read, so an f32
 // call moves no more than its own operand bytes through HBM and the matrix
@@ -53,22 +55,43 @@ __device__ __forceinline__ u32x4 read_f32_frag(const char* slot, int off, int ks
 }
 
 // An M/N-contiguous float32 operand of the two-group kernel (see above).
+template <bool MASK>
 struct PpF32MN {
   const float* base;  // tile's first column (M or N index), K = 0
   int64_t ld;         // row pitch in elements
   int voff;           // this lane's byte offset within the wave's first row
+  int cin, krem0;     // (MASK) this lane's piece starts inside the operand; K - 8 lw
+  int klim, crem;     //    K; columns left from the tile's first
   __device__ inline void init_load(const void* X, int64_t ld_, int c0, int lw, int lane) {
     base = static_cast<const float*>(X) + c0;
     ld = ld_;
     // rows 8 lw .. 8 lw + 7 all have r3 = lw & 1
     voff = (int)((int64_t)(8 * lw) * ld * 4) + ((lane ^ (8 * (lw & 1))) << 4);
   }
+  // (MASK) the operand's extent from this tile: clim columns (M or N), K.
+  __device__ inline void set_limits(int c0, int clim, int K, int lw, int lane) {
+    crem = clim - c0;
+    cin = 4 * (lane ^ (8 * (lw & 1))) < crem;
+    krem0 = K - 8 * lw;
+    klim = K;
+  }
   __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
     // The slice's first K row is folded into the resource base, so the
     // 32-bit offsets stay within its 32 rows.
     const float* b = base + (int64_t)slice * 32 * ld;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(b), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
-                                             16, voff, (int)(i * ld * 4), 0, 0);
+    if constexpr (!MASK) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(b), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
+                                               16, voff, (int)(i * ld * 4), 0, 0);
+    } else {
+      // This instruction's K row is slice*32 + 8 lw + i; the record count
+      // ends at the last K row's last valid column, counted from b.
+      const int64_t n = 4 * ((int64_t)(klim - 1 - slice * 32) * ld + crem);
+      const unsigned nrec = n <= 0 ? 0u : (n > 0x7FFFFFFC ? 0x7FFFFFFCu : (unsigned)n);
+      const int voffm = (cin && krem0 - slice * 32 - i > 0) ? voff + (int)(i * ld * 4) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(b, nrec),
+                                               (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024), 16, voffm,
+                                               0, 0, 0);
+    }
   }
   // Sub-step-0 byte offset of lane l's fragment of the 32x32 atom whose
   // first column is col0 (within the tile): column col0 + l%32, rows
@@ -91,16 +114,16 @@ __device__ __forceinline__ u32x4 read_f32_frag_mn(const char* slot, int off, int
                cvt_pk(Tag{}, v[6], v[7])};
 }
 
-template <bool MN, int NFRAG>
+template <bool MN, int NFRAG, bool MASK>
 struct PpF32Op {
-  using type = PpOperand<false, NFRAG>;
+  using type = PpOperand<false, NFRAG, 32, MASK>;
 };
-template <int NFRAG>
-struct PpF32Op<true, NFRAG> {
-  using type = PpF32MN;
+template <int NFRAG, bool MASK>
+struct PpF32Op<true, NFRAG, MASK> {
+  using type = PpF32MN<MASK>;
 };
 
-template <class Tag, int EPI, bool AMN, bool BMN>
+template <class Tag, int EPI, bool AMN, bool BMN, bool MASK>
 __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_f32_kernel(const GemmArgs p) {
   using C = PingPongCfg;
   using At = typename C::At;
@@ -116,21 +139,27 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_f32_kernel(const
   schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
 
-  typename PpF32Op<AMN, C::TM>::type a;
-  typename PpF32Op<BMN, C::TN>::type b;
+  typename PpF32Op<AMN, C::TM, MASK>::type a;
+  typename PpF32Op<BMN, C::TN, MASK>::type b;
   if constexpr (AMN) a.init_load(p.A, p.lda, m0, lw, lane);
   else a.init_load(p.A, p.lda, m0, lw, lane, 4);
   if constexpr (BMN) b.init_load(p.B, p.ldb, n0, lw, lane);
   else b.init_load(p.B, p.ldb, n0, lw, lane, 4);
+  if constexpr (MASK) {
+    if constexpr (AMN) a.set_limits(m0, p.M, p.K, lw, lane);
+    else a.set_limits(m0, p.M, 4 * p.K, lw, lane);
+    if constexpr (BMN) b.set_limits(n0, p.N, p.K, lw, lane);
+    else b.set_limits(n0, p.N, 4 * p.K, lw, lane);
+  }
   int offA[C::TM], offB[C::TN];  // fragment offsets within a slot, sub-step 0
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
-    offA[i] = AMN ? PpF32MN::frag_off(wm * C::WTM + 32 * i, lane)
+    offA[i] = AMN ? PpF32MN<MASK>::frag_off(wm * C::WTM + 32 * i, lane)
                   : PpOperand<false, C::TM>::lds_off(wm * C::WTM + 32 * i + (lane & 31),
                                                      2 * (lane >> 5));
 #pragma unroll
   for (int j = 0; j < C::TN; ++j)
-    offB[j] = BMN ? PpF32MN::frag_off(wn * C::WTN + 32 * j, lane)
+    offB[j] = BMN ? PpF32MN<MASK>::frag_off(wn * C::WTN + 32 * j, lane)
                   : PpOperand<false, C::TN>::lds_off(wn * C::WTN + 32 * j + (lane & 31),
                                                      2 * (lane >> 5));
 
@@ -154,7 +183,8 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_f32_kernel(const
   // Phases as in the 16-bit kernel: group 0 reads slice s in phase 2s+1 and
   // multiplies it in 2s+2, group 1 one phase later; A of slice t in slot
   // 2t % 5 (loaded by group 1), B in slot (2t+1) % 5 (loaded by group 0).
-  const int KT = p.K / KSL;
+  // Slices: whole ones, or (edge tiles) the last one cut short and zero-filled.
+  const int KT = MASK ? (p.K + KSL - 1) / KSL : p.K / KSL;
   if (group == 1) {
     issue_a(0, 0);
     if (KT > 1) {
@@ -179,6 +209,12 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_f32_kernel(const
     else asm volatile("" : "+v"(a.row), "+v"(a.c0));
     if constexpr (BMN) asm volatile("" : "+v"(b.voff));
     else asm volatile("" : "+v"(b.row), "+v"(b.c0));
+    if constexpr (MASK) {
+      if constexpr (AMN) asm volatile("" : "+v"(a.cin), "+v"(a.krem0));
+      else asm volatile("" : "+v"(a.rmask));
+      if constexpr (BMN) asm volatile("" : "+v"(b.cin), "+v"(b.krem0));
+      else asm volatile("" : "+v"(b.rmask));
+    }
     asm volatile("" : "+v"(offA[0]), "+v"(offA[1]), "+v"(offA[2]), "+v"(offA[3]),
                  "+v"(offB[0]), "+v"(offB[1]));
     const int sa = h, sb = h == 4 ? 0 : h + 1;
@@ -217,33 +253,39 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_pp_f32_kernel(const
   }
   if (group == 0) pp_barrier();  // matches group 1's idle phase: same barrier count
 
-  store_tile<C, EPI, false>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane);
+  store_tile<C, EPI, MASK>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane);
 }
 
-template <class Tag, bool AMN, bool BMN>
+template <class Tag, bool AMN, bool BMN, bool MASK>
 hipError_t launch_layout(const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.tiles_m * a.tiles_n), block(PingPongCfg::THREADS);
   if (a.epi == EPI_BETA0)
-    return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_BETA0, AMN, BMN>, grid, block, s, a);
+    return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_BETA0, AMN, BMN, MASK>, grid, block, s, a);
   if (a.epi == EPI_ACC_PLUS_C)
-    return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_ACC_PLUS_C, AMN, BMN>, grid, block, s, a);
-  return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_GENERAL, AMN, BMN>, grid, block, s, a);
+    return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_ACC_PLUS_C, AMN, BMN, MASK>, grid, block, s,
+                         a);
+  return launch_kernel(gemm_pp_f32_kernel<Tag, EPI_GENERAL, AMN, BMN, MASK>, grid, block, s, a);
 }
 
-template <class Tag>
+template <class Tag, bool MASK>
 hipError_t launch_tag(bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
   // A is M-contiguous when stored transposed; B is N-contiguous when not.
-  if (!ta && tb) return launch_layout<Tag, false, false>(a, s);
-  if (!ta && !tb) return launch_layout<Tag, false, true>(a, s);
-  if (ta && tb) return launch_layout<Tag, true, false>(a, s);
-  return launch_layout<Tag, true, true>(a, s);
+  if (!ta && tb) return launch_layout<Tag, false, false, MASK>(a, s);
+  if (!ta && !tb) return launch_layout<Tag, false, true, MASK>(a, s);
+  if (ta && tb) return launch_layout<Tag, true, false, MASK>(a, s);
+  return launch_layout<Tag, true, true, MASK>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_pp_f32(int dtype16, bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
-  if (dtype16 == 0) return launch_tag<TagF16>(ta, tb, a, s);
-  return launch_tag<TagBF16>(ta, tb, a, s);
+hipError_t launch_pp_f32(int dtype16, bool ta, bool tb, bool masked, const GemmArgs& a,
+                         hipStream_t s) {
+  if (masked) {
+    if (dtype16 == 0) return launch_tag<TagF16, true>(ta, tb, a, s);
+    return launch_tag<TagBF16, true>(ta, tb, a, s);
+  }
+  if (dtype16 == 0) return launch_tag<TagF16, false>(ta, tb, a, s);
+  return launch_tag<TagBF16, false>(ta, tb, a, s);
 }
 
 int pp_f32_slice() { return 32; }

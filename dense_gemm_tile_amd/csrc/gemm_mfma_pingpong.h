@@ -134,11 +134,12 @@ typedef short pp_i16x4 __attribute__((ext_vector_type(4)));
 // One operand's loads (by the wave group that loads it) and fragment reads
 // (by every wave). MN: the operand is stored with M (or N) contiguous.
 // NFRAG atoms of ATOM rows/columns per wave, starting at row0 of the tile.
-// MASK (edge tiles, 16-bit elements): every piece is addressed through the
-// voffset alone from a resource that ends at the operand's last byte, and
-// pieces in rows (K-rows) past the operand or starting past its contiguous
-// dimension get an out-of-range offset, so they read as zeros; the
-// contiguous dimension must be a multiple of 8 (whole 16-byte pieces).
+// MASK (edge tiles): every piece is addressed through the voffset alone
+// from a resource that ends at the operand's last byte, and pieces in rows
+// (K-rows) past the operand or starting past its contiguous dimension get an
+// out-of-range offset, so they read as zeros; the contiguous dimension must
+// fill whole 16-byte pieces (the M/N-contiguous form: 16-bit elements, a
+// multiple of 8).
 template <bool MN, int NFRAG, int ATOM = 32, bool MASK = false>
 struct PpOperand;
 
@@ -150,8 +151,8 @@ struct PpOperand<false, NFRAG, ATOM, MASK> {
   // the 16-wide atom, c1 for the odd instructions).
   const char* base;      // tile's first row (M or N index), K = 0
   int ld2, row, c0, c1;  // ld2: row pitch in bytes
-  int rmask, klim;       // (MASK) bit i: instruction i's row is inside the operand; K;
-  unsigned nrec;         //    bytes from base to the operand's end
+  int rmask, kbytes;     // (MASK) bit i: instruction i's row is inside the operand; bytes
+  unsigned nrec;         //    of K in a row; bytes from base to the operand's end
   // Read side: byte offset of each atom's fragment within a slot, sub-step 0.
   int off[NFRAG];
 
@@ -181,14 +182,15 @@ struct PpOperand<false, NFRAG, ATOM, MASK> {
       c1 = 0;
     }
   }
-  // (MASK) the operand's extent from this tile: rlim rows (M or N), K.
-  __device__ inline void set_limits(int r0, int rlim, int K, int lw, int lane) {
+  // (MASK) the operand's extent from this tile: rlim rows (M or N), kb
+  // bytes of K values per row (a multiple of 16).
+  __device__ inline void set_limits(int r0, int rlim, int kb, int lw, int lane) {
     const int rix = lw * 64 + (lane >> 3), rrem = rlim - r0;
     rmask = 0;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) rmask |= (rix + 8 * i < rrem) << i;
-    klim = K;
-    const int64_t n = rrem > 0 ? (int64_t)(rrem - 1) * ld2 + 2 * (int64_t)K : 0;
+    kbytes = kb;
+    const int64_t n = rrem > 0 ? (int64_t)(rrem - 1) * ld2 + kb : 0;
     nrec = n > 0x7FFFFFFC ? 0x7FFFFFFCu : (unsigned)n;
   }
   __device__ __forceinline__ void issue(char* slot, int lw, int i, int slice) const {
@@ -199,10 +201,8 @@ struct PpOperand<false, NFRAG, ATOM, MASK> {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024),
                                                16, voff, soff, 0, 0);
     } else {
-      const int k = slice * 64 + chunk * 8;  // the piece's first K (16-bit elements)
-      const int voff = ((rmask >> i) & 1) && k < klim
-                           ? row + i * 8 * ld2 + slice * 128 + (chunk << 4)
-                           : kOutOfRange;
+      const int kb = slice * 128 + (chunk << 4);  // the piece's first byte in its row
+      const int voff = ((rmask >> i) & 1) && kb < kbytes ? row + i * 8 * ld2 + kb : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(base, nrec),
                                                (pp_lds_ptr_t)(slot + (lw * 8 + i) * 1024), 16, voff,
                                                0, 0, 0);
@@ -364,8 +364,10 @@ struct PingPongPipe {
     a.init_load(static_cast<const uint16_t*>(p.A), p.lda, m0, lw, lane);
     b.init_load(static_cast<const uint16_t*>(p.B), p.ldb, n0, lw, lane);
     if constexpr (MASK) {
-      a.set_limits(m0, p.M, p.K, lw, lane);
-      b.set_limits(n0, p.N, p.K, lw, lane);
+      if constexpr (AMN) a.set_limits(m0, p.M, p.K, lw, lane);
+      else a.set_limits(m0, p.M, 2 * p.K, lw, lane);
+      if constexpr (BMN) b.set_limits(n0, p.N, p.K, lw, lane);
+      else b.set_limits(n0, p.N, 2 * p.K, lw, lane);
     }
     a.init_read(wm * C::WTM, lane);
     b.init_read(wn * C::WTN, lane);

@@ -240,8 +240,8 @@ def test_k16_tail_is_named(lib):
 
 
 def test_f32_operand_dtypes(lib, monkeypatch):
-    # whole 256x256 tiles in any layout, K a multiple of 32: the two-group
-    # kernel rounds fragments as it reads them
+    # 256x256 tiles in any layout: the two-group kernel rounds fragments as
+    # it reads them (whole tiles: K a multiple of 32)
     assert _v(lib, M=8192, N=8192, K=8192, tB=1, dtype=lib.GEMM_DTYPE_F32_BF16) == lib.GEMM_OK
     assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 pingpong f32->bf16"
     assert _v(lib, M=4096, N=4096, K=4096 + 32, tB=1, dtype=2, beta=1.0, C=D0) == lib.GEMM_OK
@@ -250,11 +250,20 @@ def test_f32_operand_dtypes(lib, monkeypatch):
         assert _v(lib, M=4096, N=4096, K=4096, tA=tA, tB=tB, dtype=3) == lib.GEMM_OK
         assert lib.gemm_last_path() == \
             f"mfma t256x256x64 w2x4 a32x32x16 {ops} epi=beta0 pingpong f32->bf16"
-    # otherwise (edges, K not a multiple of 32, rows not 16-byte aligned) the
-    # 128x128 ring kernel stages both operands through registers and rounds
-    # them there; a K tail makes it masked
+    # edge tiles and K tails too, when every operand's contiguous dimension
+    # is a multiple of 4 (whole 16-byte pieces)
     for kw in (dict(tB=0, M=8192 + 256 + 8), dict(tA=1, tB=1, N=8192 - 8),
-               dict(tB=1, K=8192 + 16), dict(tB=1, lda=8192 + 2)):
+               dict(tB=1, K=8192 + 16), dict(tA=1, tB=0, K=8192 + 3)):
+        args = dict(M=8192, N=8192, K=8192, dtype=lib.GEMM_DTYPE_F32_BF16)
+        args.update(kw)
+        assert _v(lib, **args) == lib.GEMM_OK
+        path = lib.gemm_last_path()
+        assert path.startswith("mfma t256x256x64 w2x4 a32x32x16") and path.endswith(
+            " pingpong masked f32->bf16"), (kw, path)
+    # otherwise (a contiguous dimension cut inside a piece, rows not 16-byte
+    # aligned) the 128x128 ring kernel stages both operands through registers
+    # and rounds them there; edges or a K tail make it masked
+    for kw in (dict(tA=1, M=8192 - 2), dict(tB=1, K=8192 + 2), dict(tB=1, lda=8192 + 2)):
         args = dict(M=8192, N=8192, K=8192, dtype=lib.GEMM_DTYPE_F32_BF16)
         args.update(kw)
         assert _v(lib, **args) == lib.GEMM_OK
@@ -409,11 +418,15 @@ def test_two_group_kernel_edge_tiles(lib, monkeypatch):
                dict(M=4004, tA=1),             # A stored [K][M], M % 8 != 0
                dict(N=4004, tB=0),             # B stored [K][N], N % 8 != 0
                dict(A=A0 + 2),                 # A not 16-byte aligned
-               dict(dtype=2)):                 # float32 operands
+               dict(dtype=2, K=4098)):         # float32 operands, K % 4 != 0
         args = dict(M=4000, N=4000, K=4096, tB=1)
         args.update(kw)
         assert _v(lib, **args) == lib.GEMM_OK
         assert lib.gemm_last_path().startswith("mfma t128x128x64"), (kw, lib.gemm_last_path())
+    # float32 operands: the contiguous dimensions in multiples of 4
+    assert _v(lib, M=4000, N=4000, K=4100, tB=1, dtype=2) == lib.GEMM_OK
+    assert lib.gemm_last_path() == \
+        "mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 pingpong masked f32->f16"
     # a forced 256x256 tile skips the fill test
     monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
     assert _v(lib, M=4097, N=4097, K=4096, tB=1) == lib.GEMM_OK

@@ -241,10 +241,24 @@ def test_f32_operands_pingpong(dtype, monkeypatch):
                 assert "pingpong f32->" + dtype in r.path and "masked" not in r.path, r.path
                 r.check()
                 r.check_padding_untouched()
-    # M or N edges, K not a multiple of 32, or 8-byte rows: the 128x128 ring
-    # kernel, both operands staged and rounded in registers
-    for (tA, tB, K, ldb) in [(0, 0, 48, None), (1, 1, 40, None), (0, 1, 48, None),
-                             (0, 1, 64, 66)]:
+    # M or N edges and K tails (K-contiguous operands: K a multiple of 4; an
+    # M/N-contiguous operand: its M or N): the same kernel with edge tiles,
+    # pieces past the operands reading as zeros; C == D
+    for (tA, tB, M, N, K) in [(0, 0, 300, 260, 48), (1, 1, 516, 200, 40), (0, 1, 301, 299, 44),
+                              (1, 0, 260, 516, 37), (1, 0, 8, 4, 3)]:
+        for alpha, beta in [(1.0, 0.0), (-1.5, 0.5)]:
+            seed += 1
+            ip = beta != 0.0
+            cfg = workloads.Config(f"f32pp{seed}", M, N, K, "f32_" + dtype, tA, tB, alpha, beta,
+                                   "uniform", seed, ldc=N + (0 if ip else 4),
+                                   ldd=N + (0 if ip else 4), inplace=ip)
+            r = run(cfg)
+            assert r.path.endswith("pingpong masked f32->" + dtype), r.path
+            r.check()
+            r.check_padding_untouched()
+    # a contiguous dimension cut inside a 16-byte piece, or 8-byte rows: the
+    # 128x128 ring kernel, both operands staged and rounded in registers
+    for (tA, tB, K, ldb) in [(0, 1, 42, None), (0, 1, 64, 66)]:
         seed += 1
         cfg = workloads.Config(f"f32pp{seed}", 512, 256, K, "f32_" + dtype, tA, tB, 1.0, 0.0,
                                "uniform", seed, ldb=ldb)
@@ -312,17 +326,18 @@ def _tie_heavy_f32(shape, dtype, rng):
     return torch.tensor(x.astype(np.float32).reshape(shape))
 
 
+@pytest.mark.parametrize("shape", [(256, 512, 192), (264, 520, 200)])
 @pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 1), (1, 0)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_f32_pingpong_rounding_bitwise(dtype, tA, tB, monkeypatch):
+def test_f32_pingpong_rounding_bitwise(dtype, tA, tB, shape, monkeypatch):
     """In-register rounding of the two-group kernel against the oracle's
     rounding, in every layout (M/N-contiguous operands are read down their
-    float32 K-rows): D from float32 operands must equal, bitwise, D of the
-    16-bit kernel fed the operands the oracle rounds (same tile, same sum
-    order)."""
+    float32 K-rows), whole tiles and edge tiles: D from float32 operands must
+    equal, bitwise, D of the 16-bit kernel fed the operands the oracle rounds
+    (same tile, same sum order; zeros past the operands add nothing)."""
     monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
-    rng = np.random.default_rng(44 + 2 * tA + tB)
-    M, N, K = 256, 512, 192  # K whole 64-slices: both sides on the two-group design
+    rng = np.random.default_rng(44 + 2 * tA + tB + shape[2])
+    M, N, K = shape  # both sides on the two-group design
     A32 = _tie_heavy_f32((K, M) if tA else (M, K), dtype, rng)
     B32 = _tie_heavy_f32((N, K) if tB else (K, N), dtype, rng)
     code = 0 if dtype == "f16" else 1
@@ -333,7 +348,7 @@ def test_f32_pingpong_rounding_bitwise(dtype, tA, tB, monkeypatch):
 
     cfg32 = workloads.Config("f32tie", M, N, K, "f32_" + dtype, tA, tB, 1.0, 0.0, "uniform", 1)
     r32 = run(cfg32, workloads.make_inputs(cfg32, A_src=A32, B_src=B32))
-    assert "pingpong f32->" + dtype in r32.path, r32.path
+    assert r32.path.endswith(("pingpong f32->" + dtype, "pingpong masked f32->" + dtype)), r32.path
     cfg16 = workloads.Config("f32tie16", M, N, K, dtype, tA, tB, 1.0, 0.0, "uniform", 1)
     r16 = run(cfg16, workloads.make_inputs(cfg16, A_src=oracle_rounded(A32),
                                            B_src=oracle_rounded(B32)))
