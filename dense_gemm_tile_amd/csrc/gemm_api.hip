@@ -439,8 +439,9 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     if (big_pitch) plan.masked = true;
     // Float32 operands with 16-byte rows, whole 256x256 tiles and K a
     // multiple of its 32-deep slices, any layout: the two-group kernel rounds
-    // them as it reads fragments. Every other float32 call is rounded while
-    // it is staged (ring kernel, or the masked kernel for 64-bit pitches).
+    // them as it reads fragments (edge tiles: see below). Every other float32
+    // call is rounded while it is staged (ring kernel, or the masked kernel
+    // for 64-bit pitches).
     plan.pp_f32 = src32 && t == TILE_256x256 && !a_elem && !b_elem &&
                   !big_pitch && M % ti.bm == 0 && N % ti.bn == 0 && K % pp_f32_slice() == 0;
     if (plan.pp_f32) plan.masked = false;

@@ -1,7 +1,8 @@
-// Matrix-core GEMM for whole 256x256 output tiles: direct global->LDS staging
-// and two wave groups that take turns on the matrix cores. Each operand may be
+// Matrix-core GEMM for 256x256 output tiles: direct global->LDS staging and
+// two wave groups that take turns on the matrix cores. Each operand may be
 // K-contiguous (A stored [M][K], B stored [N][K]) or M/N-contiguous (A stored
-// [K][M], B stored [K][N]).
+// [K][M], B stored [K][N]). Whole tiles, or (MASK) edge tiles and K tails
+// whose operands still load in whole 16-byte pieces.
 //
 // Same contraction and atom nest as the general kernel (TVM TIRx `gemm`:
 // "Algorithm" steps 1-3), with the Phobos `@pipeline` idea of asynchronous

@@ -29,7 +29,9 @@
  * allocates, frees and synchronises nothing. Work is enqueued on `stream`
  * (a hipStream_t; NULL means the default stream) and gemm() returns before it
  * completes. Error and path strings are thread-local; concurrent calls on
- * different threads are safe.
+ * different threads are safe. A call enqueues kernel launches only (no
+ * memset, copy or event), so calls on a stream under capture are recorded
+ * into the HIP graph and replay like the eager calls.
  */
 #ifndef DENSE_GEMM_TILE_H
 #define DENSE_GEMM_TILE_H
