@@ -413,7 +413,7 @@ def test_two_group_kernel_edge_tiles(lib, monkeypatch):
     assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a16x16x32 NN epi=acc+c pingpong masked"
     assert _v(lib, M=4000, N=3904, K=4100, tA=1) == lib.GEMM_OK  # K tail: both M/N-contiguous
     assert lib.gemm_last_path() == "mfma t256x256x64 w2x4 a32x32x16 TN epi=beta0 pingpong masked"
-    for kw in (dict(M=4097, N=4097),           # 289 tiles: the second round 13 % full
+    for kw in (dict(M=4353, N=4353),           # 324 tiles: the second round 27 % full
                dict(K=4100),                   # K-contiguous operand, K % 8 != 0
                dict(M=4004, tA=1),             # A stored [K][M], M % 8 != 0
                dict(N=4004, tB=0),             # B stored [K][N], N % 8 != 0
@@ -432,6 +432,36 @@ def test_two_group_kernel_edge_tiles(lib, monkeypatch):
     assert _v(lib, M=4097, N=4097, K=4096, tB=1) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" pingpong masked"), lib.gemm_last_path()
     assert _v(lib, M=96, N=40, K=20, tA=1, tB=0) == lib.GEMM_OK
+    assert lib.gemm_last_path().endswith(" pingpong masked"), lib.gemm_last_path()
+
+
+def test_split_past_a_multiple_of_the_tile(lib, monkeypatch):
+    # at most 32 rows and columns past the last whole 256x256 tile that add a
+    # round of tiles: whole tiles, remainder rows, remainder columns, each
+    # planned on its own and launched in that order
+    assert _v(lib, M=4097, N=4097, K=4096, tB=1, dtype=1) == lib.GEMM_OK
+    path = lib.gemm_last_path()
+    assert path.startswith("split core 4096x4096: mfma t256x256x64 w2x4 a16x16x32 NT epi=beta0 "
+                           "pingpong; rows 1x4097: mfma ") and "; cols 4096x1: mfma " in path, path
+    assert _v(lib, M=4128, N=8192, K=1024, tA=1, dtype=0, beta=1.0, C=D0) == lib.GEMM_OK
+    path = lib.gemm_last_path()
+    assert path.startswith("split core 4096x8192: mfma t256x256x64 w2x4 a32x32x16 TN epi=acc+c "
+                           "pingpong; rows 32x8192: mfma ") and "cols" not in path, path
+    assert _v(lib, M=4096, N=4100, K=512, tB=1, dtype=3) == lib.GEMM_OK
+    path = lib.gemm_last_path()
+    assert path.startswith("split core 4096x4096: mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 "
+                           "pingpong f32->bf16; cols 4096x4: mfma ") and "rows" not in path, path
+    for kw in (dict(M=4353, N=4353),           # the remainder adds no round
+               dict(M=4096 + 33),              # more than 32 remainder rows
+               dict(N=4097, tB=0),             # B [K][N] with an unaligned row pitch
+               dict(N=4097, K=0, beta=1.0, lda=1, ldb=1),  # D = beta*C
+               dict(M=3841, N=4097)):          # fewer than 256 whole tiles
+        args = dict(M=4097, N=4096, K=4096, tB=1, dtype=1)
+        args.update(kw)
+        assert _v(lib, **args) == lib.GEMM_OK
+        assert not lib.gemm_last_path().startswith("split"), (kw, lib.gemm_last_path())
+    monkeypatch.setenv("GEMM_FORCE_TILE", "t256x256x64")
+    assert _v(lib, M=4097, N=4097, K=4096, tB=1, dtype=1) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith(" pingpong masked"), lib.gemm_last_path()
 
 

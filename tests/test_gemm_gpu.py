@@ -698,6 +698,49 @@ def test_pingpong_edge_tiles_full_size_sampled(shape):
     r.check_elements(block=64, seed=cfg.seed)
 
 
+SPLIT_CASES = [
+    # (M, N, K, dtype, tA, tB, alpha, beta, C == D): remainder rows and
+    # columns, rows only, columns only; every layout; float32 operands
+    (4097, 4097, 256, "bf16", 0, 1, 1.5, -0.5, False),
+    (4128, 4100, 192, "f16", 0, 0, 1.0, 1.0, True),
+    (4104, 4096, 136, "bf16", 1, 0, 1.0, 0.0, False),
+    (4096, 4127, 320, "f16", 1, 1, -2.0, 0.5, False),
+    (4097, 4100, 96, "f32_bf16", 0, 1, 1.0, 0.0, False),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_{c[3]}_{c[4]}{c[5]}")
+def test_split_past_a_multiple_of_the_tile(case, monkeypatch):
+    """Up to 32 rows and columns past the last whole 256x256 tile that would
+    add a round of tiles: the call runs as the whole tiles, the remainder
+    rows and the remainder columns, three launches on one stream. Rows that
+    touch every tile band (the remainder rows included) against the oracle
+    over all columns, one element in every 64x64 block, D untouched outside
+    M x N; the same path from gemm_validate."""
+    monkeypatch.delenv("GEMM_FORCE_TILE", raising=False)
+    M, N, K, dtype, tA, tB, alpha, beta, inplace = case
+    pad8 = lambda x: (x + 7) // 8 * 8  # 16-byte rows for every operand
+    lda = pad8(M if tA else K)
+    ldb = pad8(K if tB else N)
+    ld = N + (0 if inplace else 4)
+    cfg = workloads.Config(f"split{M}x{N}x{K}", M, N, K, dtype, tA, tB, alpha, beta, "uniform",
+                           M + N + K, lda=lda, ldb=ldb, ldc=ld, ldd=ld, inplace=inplace)
+    r = run(cfg)
+    assert r.path.startswith("split core "), r.path
+    assert (f"; rows {M % 256}x{N}:" in r.path) == (M % 256 > 0), r.path
+    assert (f"; cols {M - M % 256}x{N % 256}:" in r.path) == (N % 256 > 0), r.path
+    rows = np.unique(np.concatenate([sample_rows(M, 256, 1), np.arange(M - 40, M)]))
+    r.check(rows=rows)
+    if not dtype.startswith("f32"):  # the per-element oracle takes 16-bit operands
+        r.check_elements(block=64, seed=cfg.seed)
+    r.check_padding_untouched()
+    import dense_gemm_tile_amd as dgt
+    st = dgt.gemm_validate(M, N, K, dtype, tA, tB, alpha, beta, 1 << 32, lda, 2 << 32, ldb,
+                           (3 << 32) if beta else None, ld, (3 << 32) if inplace else 4 << 32,
+                           ld)
+    assert st == dgt.GEMM_OK and dgt.gemm_last_path() == r.path, dgt.gemm_last_path()
+
+
 @pytest.mark.parametrize("layout", [(0, 1), (0, 0), (1, 1)])
 def test_wide_and_scalar_epilogues_agree(layout):
     """Whole tiles store D with 16-byte accesses when D (and C) allow it and
