@@ -700,8 +700,10 @@ hipError_t launch_plan(const Plan& plan, int dtype, int transA, int transB, hipS
 // Every element of D is computed once, by one of the three. Measured, same
 // box, bf16 NT: 4097^2 x 4096 one launch on 128x128 tiles 193 us, the
 // pieces 103.5 + 15.0 + 18.5 us; 8193^2 x 8192 masked 256x256 tiles 932 us,
-// the pieces 733 + 28.5 + 33.9 us.
-constexpr int64_t kSplitMaxRem = 32;
+// the pieces 733 + 28.5 + 33.9 us; with 64, 104 and 128 remainder rows and
+// columns (K = 4096) one launch takes 198 us against 107 us for the whole
+// tiles plus 32, 50 and 43 us for the two strips.
+constexpr int64_t kSplitMaxRem = 128;
 
 struct SplitPart {
   const char* what;  // "core", "rows" or "cols"

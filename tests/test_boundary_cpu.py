@@ -436,7 +436,7 @@ def test_two_group_kernel_edge_tiles(lib, monkeypatch):
 
 
 def test_split_past_a_multiple_of_the_tile(lib, monkeypatch):
-    # at most 32 rows and columns past the last whole 256x256 tile that add a
+    # at most 128 rows and columns past the last whole 256x256 tile that add a
     # round of tiles: whole tiles, remainder rows, remainder columns, each
     # planned on its own and launched in that order
     assert _v(lib, M=4097, N=4097, K=4096, tB=1, dtype=1) == lib.GEMM_OK
@@ -452,7 +452,7 @@ def test_split_past_a_multiple_of_the_tile(lib, monkeypatch):
     assert path.startswith("split core 4096x4096: mfma t256x256x64 w2x4 a32x32x16 NT epi=beta0 "
                            "pingpong f32->bf16; cols 4096x4: mfma ") and "rows" not in path, path
     for kw in (dict(M=4353, N=4353),           # the remainder adds no round
-               dict(M=4096 + 33),              # more than 32 remainder rows
+               dict(M=4096 + 129),             # more than 128 remainder rows
                dict(N=4097, tB=0),             # B [K][N] with an unaligned row pitch
                dict(N=4097, K=0, beta=1.0, lda=1, ldb=1),  # D = beta*C
                dict(M=3841, N=4097)):          # fewer than 256 whole tiles

@@ -706,12 +706,13 @@ SPLIT_CASES = [
     (4104, 4096, 136, "bf16", 1, 0, 1.0, 0.0, False),
     (4096, 4127, 320, "f16", 1, 1, -2.0, 0.5, False),
     (4097, 4100, 96, "f32_bf16", 0, 1, 1.0, 0.0, False),
+    (4200, 4224, 200, "bf16", 0, 1, 1.0, 1.0, True),
 ]
 
 
 @pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_{c[3]}_{c[4]}{c[5]}")
 def test_split_past_a_multiple_of_the_tile(case, monkeypatch):
-    """Up to 32 rows and columns past the last whole 256x256 tile that would
+    """Up to 128 rows and columns past the last whole 256x256 tile that would
     add a round of tiles: the call runs as the whole tiles, the remainder
     rows and the remainder columns, three launches on one stream. Rows that
     touch every tile band (the remainder rows included) against the oracle
