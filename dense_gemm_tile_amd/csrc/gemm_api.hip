@@ -179,7 +179,16 @@ int choose_tile(int64_t M, int64_t N, int64_t K) {
   if (count(TILE_128x128) >= 128) return TILE_128x128;
   if (M <= 16 && N <= 16) return TILE_16x16;
   const MfmaTileInfo& k4 = mfma_tile_info(TILE_32x32K4);
-  if (count(TILE_64x64) < 256 && K >= (int64_t)k4.bk * k4.kg) return TILE_32x32K4;
+  if (count(TILE_64x64) < 256 && K >= (int64_t)k4.bk * k4.kg) {
+    // Eight K groups when the 32x32 tiles fit one round (the eight-group
+    // workgroup takes 128 KiB of LDS, so one per CU) and each group still
+    // walks at least four slices: the shorter chain of dependent slice loads
+    // per wave measured 1x4097x4096 15.1 -> 11.6 us, 4096x1x4096 18.4 ->
+    // 12.2, 256x1024x4096 10.8 -> 9.7; past one round (1x8193x8192: 257
+    // tiles) four groups stay faster (28.4 against 39.2 us).
+    if (count(TILE_32x32K8) <= 256 && K >= 2048) return TILE_32x32K8;
+    return TILE_32x32K4;
+  }
   return TILE_64x64;
 }
 

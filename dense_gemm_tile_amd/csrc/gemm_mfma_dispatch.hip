@@ -14,6 +14,7 @@ const MfmaTileInfo kTiles[NUM_MFMA_TILES] = {
     info<Cfg64>("t64x64x64"),
     info<Cfg16>("t16x16x64"),
     info<Cfg32k4>("t32x32x64k4"),
+    info<Cfg32k8>("t32x32x64k8"),
 };
 }  // namespace
 
@@ -27,6 +28,7 @@ hipError_t launch_mfma(int tile, int dtype, bool ta, bool tb, bool masked, const
     case TILE_64x64: return launch_mfma_64(dtype, ta, tb, masked, a, s);
     case TILE_16x16: return launch_mfma_16(dtype, ta, tb, masked, a, s);
     case TILE_32x32K4: return launch_mfma_32k4(dtype, ta, tb, masked, a, s);
+    case TILE_32x32K8: return launch_mfma_32k8(dtype, ta, tb, masked, a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -918,13 +918,16 @@ using Cfg256 = TileCfg<256, 256, 2, 2, 32>;
 using Cfg128 = TileCfg<128, 128, 2, 2, 32>;
 using Cfg64 = TileCfg<64, 64, 2, 2, 16>;
 using Cfg16 = TileCfg<16, 16, 1, 1, 16>;
-// Under-filled grids: 32x32 tiles, K split over four one-wave groups.
+// Under-filled grids: 32x32 tiles, K split over four (or, for long K, eight)
+// one-wave groups.
 using Cfg32k4 = TileCfg<32, 32, 1, 1, 32, 4>;
+using Cfg32k8 = TileCfg<32, 32, 1, 1, 32, 8>;
 
 hipError_t launch_mfma_256(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mfma_128(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mfma_64(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mfma_16(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mfma_32k4(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_32k8(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 
 }  // namespace dgt

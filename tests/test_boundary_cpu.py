@@ -465,6 +465,19 @@ def test_split_past_a_multiple_of_the_tile(lib, monkeypatch):
     assert lib.gemm_last_path().endswith(" pingpong masked"), lib.gemm_last_path()
 
 
+def test_k_split_eight_ways(lib):
+    # one round of 32x32 tiles and K >= 2048: K split over eight one-wave groups
+    for M, N, K in [(1, 4097, 4096), (4096, 1, 4096), (256, 1024, 4096)]:
+        assert _v(lib, M=M, N=N, K=K, tB=1, dtype=1) == lib.GEMM_OK
+        assert lib.gemm_last_path().startswith("mfma t32x32x64k8 w1x1 a32x32x16 NT"), \
+            (M, N, K, lib.gemm_last_path())
+        assert " ksplit8" in lib.gemm_last_path()
+    # more than one round, or a shorter K: four groups
+    for M, N, K in [(1, 8193, 8192), (64, 4160, 4096), (512, 512, 512), (256, 1024, 1024)]:
+        assert _v(lib, M=M, N=N, K=K, tB=1, dtype=1) == lib.GEMM_OK
+        assert lib.gemm_last_path().startswith("mfma t32x32x64k4 "), (M, N, K, lib.gemm_last_path())
+
+
 def test_k_split_tile_choice(lib):
     # 64x64 tiles would leave CUs idle: 32x32 tiles, K split over 4 wave groups
     assert _v(lib, M=1000, N=500, K=256) == lib.GEMM_OK

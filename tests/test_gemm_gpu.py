@@ -102,7 +102,7 @@ def test_full_size_workload_forced_fma_sampled(name, monkeypatch):
 SHAPES = [(16, 8, 16), (1, 1, 1), (32, 32, 16), (48, 40, 24), (64, 64, 64), (100, 130, 70),
           (257, 129, 200), (128, 256, 96), (300, 17, 33), (5, 300, 8), (513, 65, 130),
           (256, 256, 256), (96, 160, 1000), (64, 96, 768)]
-TILES = ["t16x16x64", "t64x64x64", "t128x128x64", "t256x256x64", "t32x32x64k4"]
+TILES = ["t16x16x64", "t64x64x64", "t128x128x64", "t256x256x64", "t32x32x64k4", "t32x32x64k8"]
 
 
 def _on_tile(path, tile):
@@ -472,15 +472,17 @@ def test_exact_ones_closed_form():
     assert np.all(r.D.numpy() == float(K))
 
 
-def test_k_split_is_deterministic_and_exact():
-    """The four K groups' partial sums are added in a fixed order: two runs agree
+@pytest.mark.parametrize("kg", [4, 8])
+def test_k_split_is_deterministic_and_exact(kg, monkeypatch):
+    """The K groups' partial sums are added in a fixed order: two runs agree
     bitwise; with integer inputs every partial sum is exact, so D is the exact
     product. K = 2120 leaves the groups unequal numbers of steps and a ragged tail."""
+    monkeypatch.setenv("GEMM_FORCE_TILE", f"t32x32x64k{kg}")
     M, N, K = 512, 512, 2120
     cfg = workloads.Config("ksplit", M, N, K, "bf16", 0, 0, 1.5, 0.5, "normal", 77)
     r1 = run(cfg)
     r2 = run(cfg)
-    assert " ksplit4 masked" in r1.path, r1.path
+    assert f" ksplit{kg} masked" in r1.path, r1.path
     assert torch.equal(r1.D, r2.D)
     r1.check()
     rng = np.random.default_rng(5)
@@ -491,7 +493,7 @@ def test_k_split_is_deterministic_and_exact():
         inp = workloads.make_inputs(cfg, A_src=torch.tensor(A.T.copy() if tA else A),
                                     B_src=torch.tensor(B.T.copy() if tB else B))
         r = run(cfg, inp)
-        assert " ksplit4" in r.path, r.path
+        assert f" ksplit{kg}" in r.path, r.path
         assert np.array_equal(r.D[:, :N].numpy(), (A @ B).astype(np.float32)), (tA, tB)
 
 
