@@ -36,6 +36,9 @@ struct GemmArgs {
   int b_direct;  //    (16-byte rows, edges of its contiguous dimension on
                  //    multiples of 8 elements), 0 if staged through registers
   int ring_mode; // 128x128 ring kernel: RingMode below
+  int stage_depth; // 128x128 ring kernel with exactly one staged 16-bit operand:
+                   //    2 requests its loads three slices ahead (two register
+                   //    sets), 1 two slices ahead (one set)
   int mfold;     // 128x128 ring kernel (two K groups, 16-bit operands):
                  //    rows M - mfold .. M - 1 (0 < mfold <= 4) lie past the
                  //    tiles_m whole tile rows and are computed by the last of

@@ -81,6 +81,7 @@ struct EnvSwitches {
   const char* force_tile = nullptr;  // GEMM_FORCE_TILE
   const char* log = nullptr;         // GEMM_LOG
   const char* ring_mode = nullptr;   // GEMM_RING_MODE: form of the 128x128 ring kernel
+  const char* stage_depth = nullptr; // GEMM_STAGE_DEPTH: slices of staged loads ahead (1 or 2)
 };
 thread_local EnvSwitches g_env;
 
@@ -94,11 +95,13 @@ void read_env() {
     else if (std::strncmp(v, "FORCE_TILE=", 11) == 0) g_env.force_tile = v + 11;
     else if (std::strncmp(v, "LOG=", 4) == 0) g_env.log = v + 4;
     else if (std::strncmp(v, "RING_MODE=", 10) == 0) g_env.ring_mode = v + 10;
+    else if (std::strncmp(v, "STAGE_DEPTH=", 12) == 0) g_env.stage_depth = v + 12;
   }
   if (g_env.force_path && !*g_env.force_path) g_env.force_path = nullptr;
   if (g_env.force_tile && !*g_env.force_tile) g_env.force_tile = nullptr;
   if (g_env.log && !*g_env.log) g_env.log = nullptr;
   if (g_env.ring_mode && !*g_env.ring_mode) g_env.ring_mode = nullptr;
+  if (g_env.stage_depth && !*g_env.stage_depth) g_env.stage_depth = nullptr;
 }
 
 // Largest dimension the int32 index arithmetic in the kernels supports.
@@ -577,6 +580,15 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     if (a.mfold > 0 && a.ring_mode != RING_KSPLIT2) {  // a forced form: no folded rows
       a.mfold = 0;
       a.tiles_m = (int)((M + ti.bm - 1) / ti.bm);
+    }
+    // One staged 16-bit operand (shared ring or two K groups): its loads go
+    // three slices ahead into two register sets (GEMM_STAGE_DEPTH=1: two
+    // slices ahead, one set).
+    a.stage_depth = 2;
+    if (const char* sd = g_env.stage_depth) {
+      if (std::strcmp(sd, "1") == 0) a.stage_depth = 1;
+      else if (std::strcmp(sd, "2") != 0)
+        return fail(GEMM_ERR_INVALID_ARG, std::string("GEMM_STAGE_DEPTH must be 1 or 2, got ") + sd);
     }
   }
   // A last K step whose valid part ends within the first half of a 16x16x32

@@ -307,18 +307,20 @@ hipError_t launch_ring_deep(const GemmArgs& a, hipStream_t s) {
   return launch_kernel(gemm_ring128_deep_kernel<Tag, EPI_GENERAL, AMN, BMN>, grid, block, s, a);
 }
 
-template <class Tag, bool AMN, bool BMN, int KG, bool SRC32, bool FOLD = false>
+template <class Tag, bool AMN, bool BMN, int KG, bool SRC32, bool FOLD = false, bool STG2 = false>
 hipError_t launch_ring_kg_src(const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.tiles_m * a.tiles_n), block(Ring128Cfg::THREADS * KG);
   if (a.epi == EPI_BETA0)
-    return launch_kernel(gemm_ring_kernel<128, Tag, EPI_BETA0, AMN, BMN, KG, true, SRC32, FOLD>,
-                         grid, block, s, a);
+    return launch_kernel(
+        gemm_ring_kernel<128, Tag, EPI_BETA0, AMN, BMN, KG, true, SRC32, FOLD, STG2>, grid, block,
+        s, a);
   if (a.epi == EPI_ACC_PLUS_C)
     return launch_kernel(
-        gemm_ring_kernel<128, Tag, EPI_ACC_PLUS_C, AMN, BMN, KG, true, SRC32, FOLD>, grid, block,
-        s, a);
-  return launch_kernel(gemm_ring_kernel<128, Tag, EPI_GENERAL, AMN, BMN, KG, true, SRC32, FOLD>,
-                       grid, block, s, a);
+        gemm_ring_kernel<128, Tag, EPI_ACC_PLUS_C, AMN, BMN, KG, true, SRC32, FOLD, STG2>, grid,
+        block, s, a);
+  return launch_kernel(
+      gemm_ring_kernel<128, Tag, EPI_GENERAL, AMN, BMN, KG, true, SRC32, FOLD, STG2>, grid, block,
+      s, a);
 }
 
 // Float32 operands (a.src32: rounded to Tag's type as they are staged) take
@@ -326,11 +328,17 @@ hipError_t launch_ring_kg_src(const GemmArgs& a, hipStream_t s) {
 template <class Tag, bool AMN, bool BMN, int KG>
 hipError_t launch_ring_kg(const GemmArgs& a, hipStream_t s) {
   if (a.src32) return launch_ring_kg_src<Tag, AMN, BMN, KG, true>(a, s);
+  // Exactly one operand staged: its loads three slices ahead (two sets).
+  const bool stg2 = a.stage_depth == 2 && (a.a_direct != 0) != (a.b_direct != 0);
   if constexpr (KG == 2) {
     // Rows past the last whole tile row, computed by that row's workgroups.
-    if (a.mfold > 0) return launch_ring_kg_src<Tag, AMN, BMN, KG, false, true>(a, s);
+    if (a.mfold > 0) {
+      if (stg2) return launch_ring_kg_src<Tag, AMN, BMN, KG, false, true, true>(a, s);
+      return launch_ring_kg_src<Tag, AMN, BMN, KG, false, true>(a, s);
+    }
   }
   if (a.mfold > 0) return hipErrorInvalidValue;  // never planned
+  if (stg2) return launch_ring_kg_src<Tag, AMN, BMN, KG, false, false, true>(a, s);
   return launch_ring_kg_src<Tag, AMN, BMN, KG, false>(a, s);
 }
 

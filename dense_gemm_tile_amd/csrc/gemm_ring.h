@@ -39,6 +39,8 @@
 
 #include "gemm_mfma_pingpong.h"
 
+#include <type_traits>
+
 namespace dgt {
 
 template <int ROWS>
@@ -384,8 +386,12 @@ struct RingFold {
 // to Tag's type with mode p.src32).
 // FOLD: the instantiation for p.mfold > 0 (two K groups, 16-bit operands),
 // which leaves out the early C requests to make room for the folded rows.
+// STG2: exactly one operand staged (16-bit values; which one is uniform at
+// run time): its loads are requested three slices ahead into two register
+// sets taken in turn, instead of two slices ahead into one, so each staged
+// load has two iterations to land instead of one.
 template <int ROWS, class Tag, int EPI, bool AMN, bool BMN, int KG, bool STAGING, bool SRC32 = false,
-          bool FOLD = false>
+          bool FOLD = false, bool STG2 = false>
 __global__ void __launch_bounds__(RingCfg<ROWS>::THREADS * KG, RingCfg<ROWS>::MIN_WG / KG)
 gemm_ring_kernel(const GemmArgs p) {
   using C = RingCfg<ROWS>;
@@ -459,139 +465,229 @@ gemm_ring_kernel(const GemmArgs p) {
   // (row grp). On interior tiles that read C it requests those C values
   // right after the prologue's loads, so they arrive while the K loop runs
   // instead of after it (32 registers per lane).
-  constexpr bool PRE_C = KG == 2 && EPI != EPI_BETA0 && !FOLD;
+  constexpr bool PRE_C = KG == 2 && EPI != EPI_BETA0 && !FOLD && !STG2;
   const bool inner = m0 + C::BM <= p.M && n0 + C::BN <= p.N;
   const bool pre_c = PRE_C && p.wide_epi && inner;
   WideC<RingRow<C>> cpre;
 
-  // Prologue: local slice 0 into slots 0 and 1, then A of local slice 1
-  // (direct) into slot 2, or local slice 1 (staged) into registers. The
-  // folded rows' A of slice 0 goes first.
-  if constexpr (FOLD) {
-    if (fold && NJ > 0)
-      RingFold<AMN, ROWS>::load_pairs(fpc, static_cast<const uint16_t*>(p.A), p.lda, frow0,
-                                      fnrows, p.M, p.K, gs(0), lane);
-  }
-  if (NJ > 0) {
-    if (a_dir) {
-      if constexpr (!SRC32) a.issue_direct(slot(0), gs(0), w, lane);
-    } else {
-      a.load_staged(ra, gs(0), w, lane);
+  // Multiply local slice j (edge waves: only their atoms that hold outputs
+  // inside M x N; the branch is uniform per wave), and the folded rows.
+  auto multiply = [&](int j) {
+    const char* sa = slot(2 * j);
+    const char* sb = slot(2 * j + 1);
+  #pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      u32x4 fa[C::TM], fb[C::TN];
+  #pragma unroll
+      for (int i = 0; i < C::TM; ++i) fa[i] = a.read(sa, i, ks);
+  #pragma unroll
+      for (int jj = 0; jj < C::TN; ++jj) fb[jj] = b.read(sb, jj, ks);
+  #pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+  #pragma unroll
+        for (int jj = 0; jj < C::TN; ++jj)
+          if (full_wave || (i < nvi && jj < nvj))
+            acc[i][jj] = At::mma(Tag{}, fa[i], fb[jj], acc[i][jj]);
     }
-    if (b_dir) {
-      if constexpr (!SRC32) b.issue_direct(slot(1), gs(0), w, lane);
-    } else {
-      b.load_staged(rb, gs(0), w, lane);
-    }
-    if constexpr (!SRC32) { if (a_dir && NJ > 1) a.issue_direct(slot(2), gs(1), w, lane); }
-  }
-  if constexpr (PRE_C) {
-    if (pre_c)
-      load_wide_c<RingRow<C>>(cpre, p, m0 + wm * C::WTM + grp * At::M, n0 + wn * C::WTN, lane);
-  }
-  constexpr int NC = PRE_C ? C::TN * At::NACC / 4 : 0;  // C loads per lane
-  if (NJ > 0) {
-    if (staged) {
-      pp_wait_vm<0>();
-      if (!a_dir) a.store_staged(slot(0), ra, gs(0), w, lane, a_edge, mode);
-      if (!b_dir) b.store_staged(slot(1), rb, gs(0), w, lane, b_edge, mode);
-      if (NJ > 1) {
-        if (!a_dir) a.load_staged(ra, gs(1), w, lane);
-        if (!b_dir) b.load_staged(rb, gs(1), w, lane);
+    if constexpr (FOLD) {
+      if (fold) {
+  #pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 fa16 = RingFold<AMN, ROWS>::gather(fpc, fnrows, ks, lane);
+  #pragma unroll
+          for (int t = 0; t < 2; ++t)
+            facc[0][t] = A16::mma(Tag{}, fa16,
+                                  RingFold<BMN, ROWS>::read_b(sb, 32 * w + 16 * t, ks, lane),
+                                  facc[0][t]);
+        }
       }
-      pp_wait_lgkm0();
-    } else if (NJ > 1) {
-      // A of local slice 1 (and the C requests) may stay in flight
-      if (pre_c) pp_wait_vm_lgkm0<C::LOADS + NC>();
-      else pp_wait_vm_lgkm0<C::LOADS>();
-    } else {
-      if (pre_c) pp_wait_vm_lgkm0<NC>();
+    }
+  };
+
+  if constexpr (STG2) {
+    static_assert(STAGING && !SRC32, "two-deep staging takes 16-bit values");
+    // X: the staged operand (A when !a_dir, else B); X of local slice s sits
+    // in register set s % 2 from its request (three slices ahead) until its
+    // LDS write (one slice ahead).
+    using Stg = typename RingOperand<AMN, ROWS, false>::Staged;
+    static_assert(std::is_same<Stg, typename RingOperand<BMN, ROWS, false>::Staged>::value,
+                  "both operands stage through the same register set type");
+    Stg st0, st1;
+    const bool xa = !a_dir;
+    auto x_load = [&](Stg& r, int j) {
+      if (xa) a.load_staged(r, gs(j), w, lane);
+      else b.load_staged(r, gs(j), w, lane);
+    };
+    auto x_store = [&](const Stg& r, int j) {
+      if (xa) a.store_staged(slot(2 * j), r, gs(j), w, lane, a_edge, 0);
+      else b.store_staged(slot(2 * j + 1), r, gs(j), w, lane, b_edge, 0);
+    };
+    if constexpr (FOLD) {
+      if (fold && NJ > 0)
+        RingFold<AMN, ROWS>::load_pairs(fpc, static_cast<const uint16_t*>(p.A), p.lda, frow0,
+                                        fnrows, p.M, p.K, gs(0), lane);
+    }
+    if (NJ > 0) {
+      if (xa) {
+        x_load(st0, 0);
+        if constexpr (!SRC32) b.issue_direct(slot(1), gs(0), w, lane);
+      } else {
+        if constexpr (!SRC32) a.issue_direct(slot(0), gs(0), w, lane);
+        x_load(st0, 0);
+        if constexpr (!SRC32) { if (NJ > 1) a.issue_direct(slot(2), gs(1), w, lane); }
+      }
+      pp_wait_vm<0>();
+      x_store(st0, 0);
+      if (NJ > 1) x_load(st1, 1);
+      if (NJ > 2) x_load(st0, 2);
+      // X of local slice 1 is written in iteration 0; slice 2 may stay in flight.
+      if (NJ > 2) pp_wait_vm_lgkm0<2 * C::LOADS>();
       else pp_wait_vm_lgkm0<0>();
     }
-  }
-  pp_barrier();
-
-  for (int j = 0; j < JT; ++j) {
-    if (j < NJ) {
-      // Folded rows: A of local slice j+1, before this iteration's other
-      // loads.
-      if constexpr (FOLD) {
-        if (fold && j + 1 < NJ)
-          RingFold<AMN, ROWS>::load_pairs(fpn, static_cast<const uint16_t*>(p.A), p.lda, frow0,
-                                          fnrows, p.M, p.K, gs(j + 1), lane);
+    pp_barrier();
+    // Iteration j writes X of local slice j+1 from `sx` and requests X of
+    // j+3 into the same set; the direct operand's loads are as in the
+    // one-deep loop. At its end every load but the newest requests (X of
+    // j+3, and a direct A of j+2) has landed: the slice read next and X of
+    // j+2, which the next iteration writes.
+    auto iter = [&](int j, Stg& sx) {
+      if (j < NJ) {
+        if constexpr (FOLD) {
+          if (fold && j + 1 < NJ)
+            RingFold<AMN, ROWS>::load_pairs(fpn, static_cast<const uint16_t*>(p.A), p.lda, frow0,
+                                            fnrows, p.M, p.K, gs(j + 1), lane);
+        }
+        if (j + 1 < NJ) x_store(sx, j + 1);
+        if constexpr (!SRC32) {
+          if (xa) {
+            if (j + 1 < NJ) b.issue_direct(slot(2 * j + 3), gs(j + 1), w, lane);
+          } else {
+            if (j + 2 < NJ) a.issue_direct(slot(2 * j + 4), gs(j + 2), w, lane);
+          }
+        }
+        if (j + 3 < NJ) x_load(sx, j + 3);
+        multiply(j);
+        if (xa) {
+          if (j + 3 < NJ) pp_wait_vm_lgkm0<2 * C::LOADS>();
+          else pp_wait_vm_lgkm0<0>();
+        } else {
+          if (j + 3 < NJ) pp_wait_vm_lgkm0<3 * C::LOADS>();
+          else if (j + 2 < NJ) pp_wait_vm_lgkm0<C::LOADS>();
+          else pp_wait_vm_lgkm0<0>();
+        }
       }
-      // Staged operands: local slice j+1 arrived in registers during the
-      // previous iteration (this waits for every older load); write it into
-      // its slots (A: 2j+2, left by B of j-2; B: 2j+3, left by A of j-1),
-      // then request local slice j+2 into the same registers.
-      if (staged && j + 1 < NJ) {
-        pp_wait_vm<0>();
-        if (!a_dir) a.store_staged(slot(2 * j + 2), ra, gs(j + 1), w, lane, a_edge, mode);
-        if (!b_dir) b.store_staged(slot(2 * j + 3), rb, gs(j + 1), w, lane, b_edge, mode);
-      }
-      // Direct loads into the slots local slice j-1 has left: B of j+1
-      // first, then A of j+2 (slot 2j+4, left by B of j-1).
-      if constexpr (!SRC32) {
-        if (b_dir && j + 1 < NJ) b.issue_direct(slot(2 * j + 3), gs(j + 1), w, lane);
-        if (a_dir && j + 2 < NJ) a.issue_direct(slot(2 * j + 4), gs(j + 2), w, lane);
-      }
-      if (staged && j + 2 < NJ) {
-        if (!a_dir) a.load_staged(ra, gs(j + 2), w, lane);
-        if (!b_dir) b.load_staged(rb, gs(j + 2), w, lane);
-      }
-
-      // Multiply local slice j (edge waves: only their atoms that hold
-      // outputs inside M x N; the branch is uniform per wave).
-      const char* sa = slot(2 * j);
-      const char* sb = slot(2 * j + 1);
-#pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks) {
-        u32x4 fa[C::TM], fb[C::TN];
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i) fa[i] = a.read(sa, i, ks);
-#pragma unroll
-        for (int jj = 0; jj < C::TN; ++jj) fb[jj] = b.read(sb, jj, ks);
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-          for (int jj = 0; jj < C::TN; ++jj)
-            if (full_wave || (i < nvi && jj < nvj))
-              acc[i][jj] = At::mma(Tag{}, fa[i], fb[jj], acc[i][jj]);
-      }
+      pp_barrier();
       if constexpr (FOLD) {
         if (fold) {
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const u32x4 fa16 = RingFold<AMN, ROWS>::gather(fpc, fnrows, ks, lane);
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-              facc[0][t] = A16::mma(Tag{}, fa16,
-                                    RingFold<BMN, ROWS>::read_b(sb, 32 * w + 16 * t, ks, lane),
-                                    facc[0][t]);
-          }
+          for (int i = 0; i < kMaxFold; ++i) fpc[i] = fpn[i];
         }
       }
-
-      // Local slice j+1 must be in LDS by the next barrier. A direct B of
-      // j+1 was issued first in this iteration, so at most the one
-      // half-slice request that followed it (A of j+2: 4 direct loads or 8
-      // staged ones) may stay in flight; a direct A of j+1 is older still.
-      // Without a direct B, the staged wait at the top of this iteration
-      // already covered every older load. LDS reads and staged writes must
-      // be complete.
-      if (b_dir) {
-        if (j + 2 < NJ && a_dir) pp_wait_vm_lgkm0<C::LOADS>();
-        else if (j + 2 < NJ) pp_wait_vm_lgkm0<2 * C::LOADS>();  // staged: two loads per piece
-        else pp_wait_vm_lgkm0<0>();
+    };
+    for (int j = 0; j < JT; j += 2) {
+      iter(j, st1);
+      if (j + 1 < JT) iter(j + 1, st0);
+    }
+  } else {
+    // Prologue: local slice 0 into slots 0 and 1, then A of local slice 1
+    // (direct) into slot 2, or local slice 1 (staged) into registers. The
+    // folded rows' A of slice 0 goes first.
+    if constexpr (FOLD) {
+      if (fold && NJ > 0)
+        RingFold<AMN, ROWS>::load_pairs(fpc, static_cast<const uint16_t*>(p.A), p.lda, frow0,
+                                        fnrows, p.M, p.K, gs(0), lane);
+    }
+    if (NJ > 0) {
+      if (a_dir) {
+        if constexpr (!SRC32) a.issue_direct(slot(0), gs(0), w, lane);
       } else {
+        a.load_staged(ra, gs(0), w, lane);
+      }
+      if (b_dir) {
+        if constexpr (!SRC32) b.issue_direct(slot(1), gs(0), w, lane);
+      } else {
+        b.load_staged(rb, gs(0), w, lane);
+      }
+      if constexpr (!SRC32) { if (a_dir && NJ > 1) a.issue_direct(slot(2), gs(1), w, lane); }
+    }
+    if constexpr (PRE_C) {
+      if (pre_c)
+        load_wide_c<RingRow<C>>(cpre, p, m0 + wm * C::WTM + grp * At::M, n0 + wn * C::WTN, lane);
+    }
+    constexpr int NC = PRE_C ? C::TN * At::NACC / 4 : 0;  // C loads per lane
+    if (NJ > 0) {
+      if (staged) {
+        pp_wait_vm<0>();
+        if (!a_dir) a.store_staged(slot(0), ra, gs(0), w, lane, a_edge, mode);
+        if (!b_dir) b.store_staged(slot(1), rb, gs(0), w, lane, b_edge, mode);
+        if (NJ > 1) {
+          if (!a_dir) a.load_staged(ra, gs(1), w, lane);
+          if (!b_dir) b.load_staged(rb, gs(1), w, lane);
+        }
         pp_wait_lgkm0();
+      } else if (NJ > 1) {
+        // A of local slice 1 (and the C requests) may stay in flight
+        if (pre_c) pp_wait_vm_lgkm0<C::LOADS + NC>();
+        else pp_wait_vm_lgkm0<C::LOADS>();
+      } else {
+        if (pre_c) pp_wait_vm_lgkm0<NC>();
+        else pp_wait_vm_lgkm0<0>();
       }
     }
     pp_barrier();
-    if constexpr (FOLD) {
-      if (fold) {
+
+    for (int j = 0; j < JT; ++j) {
+      if (j < NJ) {
+        // Folded rows: A of local slice j+1, before this iteration's other
+        // loads.
+        if constexpr (FOLD) {
+          if (fold && j + 1 < NJ)
+            RingFold<AMN, ROWS>::load_pairs(fpn, static_cast<const uint16_t*>(p.A), p.lda, frow0,
+                                            fnrows, p.M, p.K, gs(j + 1), lane);
+        }
+        // Staged operands: local slice j+1 arrived in registers during the
+        // previous iteration (this waits for every older load); write it into
+        // its slots (A: 2j+2, left by B of j-2; B: 2j+3, left by A of j-1),
+        // then request local slice j+2 into the same registers.
+        if (staged && j + 1 < NJ) {
+          pp_wait_vm<0>();
+          if (!a_dir) a.store_staged(slot(2 * j + 2), ra, gs(j + 1), w, lane, a_edge, mode);
+          if (!b_dir) b.store_staged(slot(2 * j + 3), rb, gs(j + 1), w, lane, b_edge, mode);
+        }
+        // Direct loads into the slots local slice j-1 has left: B of j+1
+        // first, then A of j+2 (slot 2j+4, left by B of j-1).
+        if constexpr (!SRC32) {
+          if (b_dir && j + 1 < NJ) b.issue_direct(slot(2 * j + 3), gs(j + 1), w, lane);
+          if (a_dir && j + 2 < NJ) a.issue_direct(slot(2 * j + 4), gs(j + 2), w, lane);
+        }
+        if (staged && j + 2 < NJ) {
+          if (!a_dir) a.load_staged(ra, gs(j + 2), w, lane);
+          if (!b_dir) b.load_staged(rb, gs(j + 2), w, lane);
+        }
+
+        multiply(j);
+
+        // Local slice j+1 must be in LDS by the next barrier. A direct B of
+        // j+1 was issued first in this iteration, so at most the one
+        // half-slice request that followed it (A of j+2: 4 direct loads or 8
+        // staged ones) may stay in flight; a direct A of j+1 is older still.
+        // Without a direct B, the staged wait at the top of this iteration
+        // already covered every older load. LDS reads and staged writes must
+        // be complete.
+        if (b_dir) {
+          if (j + 2 < NJ && a_dir) pp_wait_vm_lgkm0<C::LOADS>();
+          else if (j + 2 < NJ) pp_wait_vm_lgkm0<2 * C::LOADS>();  // staged: two loads per piece
+          else pp_wait_vm_lgkm0<0>();
+        } else {
+          pp_wait_lgkm0();
+        }
+      }
+      pp_barrier();
+      if constexpr (FOLD) {
+        if (fold) {
 #pragma unroll
-        for (int i = 0; i < kMaxFold; ++i) fpc[i] = fpn[i];
+          for (int i = 0; i < kMaxFold; ++i) fpc[i] = fpn[i];
+        }
       }
     }
   }
