@@ -216,6 +216,11 @@ def test_ring_modes(lib, monkeypatch):
     assert _v(lib, M=2048, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_ERR_UNSUPPORTED
     monkeypatch.setenv("GEMM_RING_MODE", "wide")
     assert _v(lib, M=4096, N=2048, K=1024, dtype=1) == lib.GEMM_ERR_INVALID_ARG
+    monkeypatch.delenv("GEMM_RING_MODE")
+    monkeypatch.setenv("GEMM_STAGE_DEPTH", "1")
+    assert _v(lib, M=2048, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_OK
+    monkeypatch.setenv("GEMM_STAGE_DEPTH", "3")
+    assert _v(lib, M=2048, N=2048, K=2048, dtype=1, lda=2049) == lib.GEMM_ERR_INVALID_ARG
 
 
 def test_ragged_dims_stay_on_mfma_masked(lib):

@@ -180,3 +180,36 @@ def test_ring_fold_rows_past_the_last_tile_row(tA, tB, monkeypatch):
         monkeypatch.delenv("GEMM_RING_MODE")
         assert " ring" in r2.path and "fold" not in r2.path, r2.path
         r2.check(rows=rows)
+
+
+@pytest.mark.parametrize("kg", ["shared", "ksplit2"])
+@pytest.mark.parametrize("tA,tB", LAYOUTS)
+def test_single_staged_operand_depths_agree_bitwise(tA, tB, kg, monkeypatch):
+    """One operand staged through registers: requested three slices ahead
+    into two register sets (default) or two slices ahead into one
+    (GEMM_STAGE_DEPTH=1). Slice counts of 1 to 6 per K group (the two-set
+    loop runs in pairs of iterations), edges on M and N, a K tail; both
+    against the oracle and bitwise equal to each other (same sums, same
+    order)."""
+    monkeypatch.setenv("GEMM_RING_MODE", kg)
+    seed = 9900 + 10 * LAYOUTS.index((tA, tB)) + (5 if kg == "shared" else 0)
+    # every contiguous dimension a multiple of 8, so only the operand with
+    # the odd row pitch is staged
+    for (M, N, K) in [(296, 264, 64), (264, 296, 136), (136, 264, 200), (264, 136, 392),
+                      (200, 200, 704), (128, 128, 768)]:
+        for stage_a in (True, False):
+            seed += 1
+            lda = _ld(M if tA else K, not stage_a)
+            ldb = _ld(K if tB else N, stage_a)
+            cfg = workloads.Config(f"depth{seed}", M, N, K, "bf16" if seed % 2 else "f16", tA, tB,
+                                   1.5, -0.5, "uniform", seed, lda=lda, ldb=ldb)
+            inp = workloads.make_inputs(cfg)
+            r2 = run(cfg, inp)
+            assert ("staged (A:" in r2.path) == stage_a and " ring" in r2.path, r2.path
+            monkeypatch.setenv("GEMM_STAGE_DEPTH", "1")
+            r1 = run(cfg, inp)
+            monkeypatch.delenv("GEMM_STAGE_DEPTH")
+            assert r1.path == r2.path
+            assert torch.equal(r1.D, r2.D)
+            r2.check()
+
