@@ -71,6 +71,8 @@ struct GemmByteArgs {
   int read_c;              // beta != 0
   int a_vec16, b_vec16;    // base and row pitch multiples of 16 bytes
   int cd_vec16;            // D (and C when read): base and row pitch multiples of 16 bytes
+  int cd_scalar;           // two-group kernel with edge tiles: C and D accessed element by
+                           //    element (D or C rows not 16-byte aligned, or N % 4 != 0)
   int tiles_m, tiles_n, group_m;
   int pingpong;  // the two-group kernel: 1 on whole 256x256 tiles, 2 with edge tiles
 };

@@ -207,11 +207,12 @@ bool byte_pingpong(const GemmByteArgs& b) {
 
 // Other 1-byte-operand calls also take the two-group kernel, with edge tiles
 // (pieces outside the operands read as zeros, C and D accessed inside
-// M x N only), when K is a multiple of 16, N of 4, an M/N-contiguous
-// operand's contiguous dimension of 16 (whole 16-byte pieces and column
-// quads), operand and C/D rows are 16-byte aligned, and the grid has at
-// least kBytePpMaskedMinTiles tiles of 256x256 (smaller grids keep the
-// 128x128 kernel, which spreads them over more CUs). Measured against the
+// M x N only), when K is a multiple of 16, an M/N-contiguous operand's
+// contiguous dimension of 16 (whole 16-byte pieces), operand rows are
+// 16-byte aligned, and the grid has at least kBytePpMaskedMinTiles tiles of
+// 256x256 (smaller grids keep the 128x128 kernel, which spreads them over
+// more CUs). C and D go by column quads when their rows are 16-byte aligned
+// and N is a multiple of 4, else element by element. Measured against the
 // 128x128 kernel, same box: fp8 4000^2 x 4096 NT 111 -> 56 us, TN 181 ->
 // 58 us, int8 106 -> 59 us, 8000^2 x 8192 740 -> 379 us, 1008^2 x 1024 NN
 // 24.5 -> 19.2 us; 512^3 (4 tiles) equal.
@@ -220,13 +221,14 @@ bool byte_pingpong_masked(const GemmByteArgs& b, int transA, int transB) {
   const int64_t t = byte_pp_tile();
   const int64_t ldmax = b.lda > b.ldb ? b.lda : b.ldb;
   const int64_t tiles = ((b.M + t - 1) / t) * ((b.N + t - 1) / t);
-  return b.K > 0 && b.K % 16 == 0 && b.N % 4 == 0 && (!transA || b.M % 16 == 0) &&
-         (transB || b.N % 16 == 0) && b.a_vec16 && b.b_vec16 && b.cd_vec16 &&
+  return b.K > 0 && b.K % 16 == 0 && (!transA || b.M % 16 == 0) &&
+         (transB || b.N % 16 == 0) && b.a_vec16 && b.b_vec16 &&
          ldmax * t + 4096 < (int64_t{1} << 31) && tiles >= kBytePpMaskedMinTiles;
 }
 
 void set_byte_tiles(GemmByteArgs& b, int transA, int transB) {
   b.pingpong = byte_pingpong(b) ? 1 : byte_pingpong_masked(b, transA, transB) ? 2 : 0;
+  b.cd_scalar = b.pingpong == 2 && !(b.cd_vec16 && b.N % 4 == 0);
   const int tm = b.pingpong ? byte_pp_tile() : byte_tile_m();
   const int tn = b.pingpong ? byte_pp_tile() : byte_tile_n();
   b.tiles_m = (int)((b.M + tm - 1) / tm);
@@ -382,10 +384,11 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
     plan.byte_kind = dtype == GEMM_DTYPE_F8_E4M3 ? BYTE_F8E4M3 : BYTE_F8E5M2;
     const char* ops8 = transA ? (transB ? "TT" : "TN") : (transB ? "NT" : "NN");
     const int t8 = b.pingpong ? byte_pp_tile() : byte_tile_m();
-    std::snprintf(buf, sizeof buf, "fp8 %s mfma t%dx%dx128 %s %s %s epi=%s%s%s",
+    std::snprintf(buf, sizeof buf, "fp8 %s mfma t%dx%dx128 %s %s %s epi=%s%s%s%s",
                   dtype == GEMM_DTYPE_F8_E4M3 ? "e4m3" : "e5m2", t8, t8,
                   b.pingpong ? "w2x4" : "w2x2", b.pingpong ? "a16x16x128" : "a32x32x64", ops8,
                   epi_name, b.pingpong == 2 ? " pingpong masked" : b.pingpong ? " pingpong" : "",
+                  b.cd_scalar ? " elementwise C/D" : "",
                   (!b.a_vec16 || !b.b_vec16) ? " bytewise staging" : "");
     g_path = buf;
     return GEMM_OK;
@@ -689,10 +692,11 @@ int plan_i8(int64_t M, int64_t N, int64_t K, int transA, int transB, int32_t alp
     return fail(GEMM_ERR_UNSUPPORTED, "too many output tiles for one launch");
   const char* ops = transA ? (transB ? "TT" : "TN") : (transB ? "NT" : "NN");
   const int t8 = a.pingpong ? byte_pp_tile() : byte_tile_m();
-  std::snprintf(buf, sizeof buf, "i8 mfma t%dx%dx128 %s %s %s epi=%s%s%s%s", t8, t8,
+  std::snprintf(buf, sizeof buf, "i8 mfma t%dx%dx128 %s %s %s epi=%s%s%s%s%s", t8, t8,
                 a.pingpong ? "w2x4" : "w2x2", a.pingpong ? "a16x16x64" : "a32x32x32", ops,
                 reads_c ? "general" : "beta0",
                 a.pingpong == 2 ? " pingpong masked" : a.pingpong ? " pingpong" : "",
+                a.cd_scalar ? " elementwise C/D" : "",
                 reads_ab ? "" : " (K == 0 or alpha == 0: D = beta*C)",
                 (reads_ab && (!a.a_vec16 || !a.b_vec16)) ? " bytewise staging" : "");
   g_path = buf;

@@ -209,6 +209,8 @@ __device__ inline void byte_store_pairs16(const GemmByteArgs& p, int r0, int c0,
   const bool c_is_d = p.read_c && p.C == static_cast<const void*>(p.D);
   const unsigned* Cb = static_cast<const unsigned*>(p.C);
   unsigned* Db = static_cast<unsigned*>(p.D);
+  // (MASK) C and D element by element: rows not 16-byte aligned, or N % 4 != 0
+  const bool scalar = MASK && p.cd_scalar;  // uniform
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
     const int r = r0 + 16 * i + rl;
@@ -216,11 +218,20 @@ __device__ inline void byte_store_pairs16(const GemmByteArgs& p, int r0, int c0,
 #pragma unroll
     for (int q = 0; q < NP; ++q)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        cv[q][h] = p.read_c && (!MASK || (r + h < p.M && c0 + 32 * q + col < p.N))
-                       ? *reinterpret_cast<const u32x4_t*>(Cb + (int64_t)(r + h) * p.ldc + c0 +
-                                                           32 * q + col)
-                       : u32x4_t{0u, 0u, 0u, 0u};
+      for (int h = 0; h < 2; ++h) {
+        const int cc = c0 + 32 * q + col;
+        if (scalar) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            cv[q][h][k] = p.read_c && r + h < p.M && cc + k < p.N
+                              ? Cb[(int64_t)(r + h) * p.ldc + cc + k]
+                              : 0u;
+        } else {
+          cv[q][h] = p.read_c && (!MASK || (r + h < p.M && cc < p.N))
+                         ? *reinterpret_cast<const u32x4_t*>(Cb + (int64_t)(r + h) * p.ldc + cc)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
       // (whole-vector casts: a bit cast of one element of a vector reference
@@ -244,6 +255,15 @@ __device__ inline void byte_store_pairs16(const GemmByteArgs& p, int r0, int c0,
         for (int k = 0; k < 4; ++k) {
           const float v = h == 0 ? (odd ? w[k] : x[k]) : (odd ? y[k] : w[k]);
           o[k] = Kind::combine(p, __builtin_bit_cast(unsigned, v), cv[q][h][k]);
+        }
+        if (scalar) {
+          const int cc = c0 + 32 * q + col;
+          if (r + h < p.M) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (cc + k < p.N) Db[(int64_t)(r + h) * p.ldd + cc + k] = o[k];
+          }
+          continue;
         }
         if (MASK && !(r + h < p.M && c0 + 32 * q + col < p.N)) continue;
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(Db + (int64_t)(r + h) * p.ldd + c0 + 32 * q + col);

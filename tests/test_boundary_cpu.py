@@ -319,32 +319,37 @@ def test_fp8_dtypes_take_the_byte_kernel(lib, monkeypatch):
     assert _v(lib, dtype=5) == lib.GEMM_ERR_UNSUPPORTED
 
 
-def test_byte_two_group_kernel_needs_16_byte_cd_rows(lib):
+def test_byte_two_group_kernel_cd_rows(lib):
     # whole 256x256 NT tiles take the two-group kernel on 16-wide atoms, whose
-    # epilogue stores 16 bytes per lane: D (and C when read) need 16-byte rows
+    # epilogue stores 16 bytes per lane when D (and C when read) have 16-byte
+    # rows; otherwise the edge-tile form accesses C and D element by element
     assert _v8(lib, M=512, N=512, K=256, tB=1) == lib.GEMM_OK
     assert lib.gemm_last_path() == "i8 mfma t256x256x128 w2x4 a16x16x64 NT epi=beta0 pingpong"
     assert _v(lib, M=512, N=512, K=256, tB=1, dtype=lib.GEMM_DTYPE_F8_E4M3) == lib.GEMM_OK
     assert lib.gemm_last_path() == "fp8 e4m3 mfma t256x256x128 w2x4 a16x16x128 NT epi=beta0 pingpong"
     assert _v8(lib, M=512, N=512, K=256, tB=1, ldd=514) == lib.GEMM_OK
-    assert lib.gemm_last_path() == "i8 mfma t128x128x128 w2x2 a32x32x32 NT epi=beta0"
+    assert lib.gemm_last_path() == \
+        "i8 mfma t256x256x128 w2x4 a16x16x64 NT epi=beta0 pingpong masked elementwise C/D"
     assert _v8(lib, M=512, N=512, K=256, tB=1, beta=1, C=D0, ldc=512) == lib.GEMM_OK
-    assert "pingpong" in lib.gemm_last_path()
+    assert lib.gemm_last_path().endswith(" pingpong"), lib.gemm_last_path()
     assert _v8(lib, M=512, N=512, K=256, tB=1, beta=1, C=C0 + 4, ldc=512) == lib.GEMM_OK
-    assert "pingpong" not in lib.gemm_last_path()
+    assert lib.gemm_last_path().endswith(" pingpong masked elementwise C/D"), lib.gemm_last_path()
+    # fewer than 4 tiles of 256x256: the 128x128 kernel
+    assert _v8(lib, M=256, N=512, K=256, tB=1, ldd=514) == lib.GEMM_OK
+    assert lib.gemm_last_path() == "i8 mfma t128x128x128 w2x2 a32x32x32 NT epi=beta0"
 
 
 def test_byte_two_group_kernel_edge_tiles(lib):
     # other shapes take the two-group kernel with edge tiles when K is a
-    # multiple of 16, N of 4, an M/N-contiguous operand's contiguous dimension
-    # of 16, and the grid has at least 4 tiles of 256x256
+    # multiple of 16, an M/N-contiguous operand's contiguous dimension of 16,
+    # and the grid has at least 4 tiles of 256x256 (C and D element by
+    # element when N % 4 != 0)
     assert _v8(lib, M=1000, N=1000, K=1024, tB=1) == lib.GEMM_OK
     assert lib.gemm_last_path() == "i8 mfma t256x256x128 w2x4 a16x16x64 NT epi=beta0 pingpong masked"
     assert _v(lib, M=1008, N=1008, K=1040, dtype=lib.GEMM_DTYPE_F8_E5M2) == lib.GEMM_OK
     assert lib.gemm_last_path() == \
         "fp8 e5m2 mfma t256x256x128 w2x4 a16x16x128 NN epi=beta0 pingpong masked"
     for kw in (dict(K=1000, tB=1),            # K % 16 != 0
-               dict(N=1002, tB=1),            # N % 4 != 0
                dict(N=1000),                  # B stored [K][N], N % 16 != 0
                dict(M=1000, tA=1, tB=1),      # A stored [K][M], M % 16 != 0
                dict(M=500, N=200, tB=1)):     # 2 tiles of 256x256
@@ -352,6 +357,15 @@ def test_byte_two_group_kernel_edge_tiles(lib):
         args.update(kw)
         assert _v8(lib, **args) == lib.GEMM_OK
         assert lib.gemm_last_path().startswith("i8 mfma t128x128x128"), (kw, lib.gemm_last_path())
+
+
+def test_byte_two_group_kernel_elementwise_cd(lib):
+    assert _v8(lib, M=1008, N=1002, K=1024, tB=1) == lib.GEMM_OK
+    assert lib.gemm_last_path() == \
+        "i8 mfma t256x256x128 w2x4 a16x16x64 NT epi=beta0 pingpong masked elementwise C/D"
+    assert _v(lib, M=4097, N=4097, K=4096, tB=1, dtype=lib.GEMM_DTYPE_F8_E5M2) == lib.GEMM_OK
+    assert lib.gemm_last_path() == ("fp8 e5m2 mfma t256x256x128 w2x4 a16x16x128 NT epi=beta0 "
+                                    "pingpong masked elementwise C/D")
 
 
 def test_i8_form_checks_and_paths(lib):

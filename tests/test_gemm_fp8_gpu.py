@@ -207,3 +207,24 @@ def test_fp8_pingpong_edge_tiles(dt, tA, tB):
         D, _, _, path = run_fp8("f8e4m3", M, N, K, tA, tB, 1.0, 0.0, A=A, B=B)
         assert "pingpong masked" in path, path
         assert np.array_equal(D[:M, :N], (av @ bv.T).astype(np.float32))
+
+
+@pytest.mark.parametrize("dt", ["f8e4m3", "f8e5m2"])
+@pytest.mark.parametrize("tA,tB", [(0, 1), (1, 0)])
+def test_fp8_pingpong_elementwise_cd(dt, tA, tB):
+    """Odd leading dimensions of C and D, or N % 4 != 0: the two-group kernel
+    with edge tiles reads C and writes D element by element; a general
+    epilogue and C == D; against the oracle, D's padding untouched."""
+    seed = 1700 + 20 * (2 * tA + tB) + FMT[dt]
+    cases = [(608, 528, 400, 529)] + ([(1040, 1025, 272, 1027)] if tB else [(1040, 784, 272, 785)])
+    for (M, N, K, ldd) in cases:
+        seed += 1
+        D, D_ref, bound, path = run_fp8(dt, M, N, K, tA, tB, 0.5, -1.0, seed=seed, ldd=ldd)
+        assert path.endswith("pingpong masked elementwise C/D"), path
+        assert oracle.check(D[:M, :N].astype(np.float64), D_ref, bound)["ok"], (dt, M, N, K)
+        assert np.all(D[:M, N:].view(np.uint32) == D_SENTINEL)
+    D, D_ref, bound, path = run_fp8(dt, 608, 528, 400, tA, tB, 1.5, -0.75, seed=seed + 1,
+                                    ldd=531, inplace=True)
+    assert path.endswith("pingpong masked elementwise C/D"), path
+    assert oracle.check(D[:608, :528].astype(np.float64), D_ref, bound)["ok"]
+

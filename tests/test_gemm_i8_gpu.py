@@ -199,3 +199,27 @@ def test_i8_pingpong_edge_tiles(tA, tB):
     got, ref, path = run_i8(608, 528, 400, tA, tB, -3, 2, seed=seed + 1, inplace=True)
     assert "pingpong masked" in path, path
     assert np.array_equal(got[:608, :528], ref)
+
+
+@pytest.mark.parametrize("tA,tB", [(0, 1), (0, 0), (1, 1), (1, 0)])
+def test_i8_pingpong_elementwise_cd(tA, tB):
+    """C and D rows not 16-byte aligned (odd leading dimension) or N % 4 != 0
+    (where B is K-contiguous): the two-group kernel with edge tiles reads C
+    and writes D element by element; both epilogues, C == D; bit-exact, D's
+    padding untouched."""
+    seed = 1500 + 40 * (2 * tA + tB)
+    cases = [(608, 528, 400, 529), (1040, 784, 272, 787)]
+    if tB:
+        cases += [(528, 1030, 144, 1030), (1040, 1025, 272, 1027)]
+    for (M, N, K, ldd) in cases:
+        for alpha, beta in [(1, 0), (-7, 3)]:
+            seed += 1
+            lda = (M if tA else K) + (16 if seed % 2 else 0)
+            got, ref, path = run_i8(M, N, K, tA, tB, alpha, beta, seed=seed, lda=lda, ldd=ldd)
+            assert path.endswith("pingpong masked elementwise C/D"), path
+            assert np.array_equal(got[:M, :N], ref), (M, N, K, ldd, alpha, beta)
+            assert np.all(got[:M, N:] == SENTINEL)
+    got, ref, path = run_i8(608, 528, 400, tA, tB, -3, 2, seed=seed + 1, ldd=531, inplace=True)
+    assert path.endswith("pingpong masked elementwise C/D"), path
+    assert np.array_equal(got[:608, :528], ref)
+
