@@ -719,7 +719,7 @@ hipError_t launch_plan(const Plan& plan, int dtype, int transA, int transB, hipS
 // Ragged shapes just past a multiple of the 256x256 tile: when at most
 // kSplitMaxRem rows and columns past the last whole tile push a grid of at
 // least one round of 256 whole tiles into one more round, the call runs as
-// three: the whole tiles (two-group kernel, unmasked), the remainder rows
+// three: the whole tiles (two-group kernel), the remainder rows
 // under all columns, and the remainder columns beside the whole rows, each
 // planned like a call of its own and launched in that order on the stream.
 // Every element of D is computed once, by one of the three. Measured, same
@@ -741,9 +741,9 @@ struct SplitPart {
 
 // The parts (core, then rows, then columns; empty parts left out) if the
 // call is split, else 0 parts. `full` is the plan of the whole call.
-int plan_split(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB,
-               const void* A, int64_t lda, const void* B, int64_t ldb, const float* C,
-               int64_t ldc, const float* D, int64_t ldd, const Plan& full, SplitPart (&part)[3]) {
+int plan_split(int64_t M, int64_t N, int dtype, int transA, int transB, const void* A,
+               int64_t lda, const void* B, int64_t ldb, const float* C, int64_t ldc,
+               const float* D, int64_t ldd, const Plan& full, SplitPart (&part)[3]) {
   if (g_env.force_path || g_env.force_tile || g_env.ring_mode) return 0;
   if (full.noop || full.scale_only || full.byte8 || !full.mfma) return 0;
   const bool src32 = dtype >= GEMM_DTYPE_F32_F16;
@@ -770,7 +770,6 @@ int plan_split(int64_t M, int64_t N, int64_t K, int dtype, int transA, int trans
   if (rn > 0)
     part[n++] = SplitPart{"cols", Mc, rn, A, transB ? b + Nc * ldb * esz : b + Nc * esz,
                           C ? C + Nc : nullptr, D + Nc};
-  (void)K;
   return n;
 }
 
@@ -785,7 +784,7 @@ int plan_and_launch(int64_t M, int64_t N, int64_t K, int dtype, int transA, int 
                      plan);
   if (st != GEMM_OK) return st;
   SplitPart part[3];
-  const int np = plan_split(M, N, K, dtype, transA, transB, A, lda, B, ldb, C, ldc, D, ldd, plan,
+  const int np = plan_split(M, N, dtype, transA, transB, A, lda, B, ldb, C, ldc, D, ldd, plan,
                             part);
   if (np > 0) {
     Plan pp[3];
