@@ -182,7 +182,14 @@ int choose_tile(int64_t M, int64_t N, int64_t K) {
   if (count(TILE_128x128) >= 128) return TILE_128x128;
   if (M <= 16 && N <= 16) return TILE_16x16;
   const MfmaTileInfo& k4 = mfma_tile_info(TILE_32x32K4);
-  if (count(TILE_64x64) < 256 && K >= (int64_t)k4.bk * k4.kg) {
+  // K split over one-wave groups when 64x64 tiles would leave CUs idle, or
+  // fill exactly one round with a K long enough that each 64x64 tile's chain
+  // of dependent slices dominates (measured, same box, 256 tiles of 64x64:
+  // 1024^2 x 4096 NT 34.8 -> 27.9 us, 128x8192x8192 NT 64 -> 49 us, 96 x
+  // 8192 x 8192 99 -> 48 us; at K = 1024-2048 the 64x64 tile was as fast or
+  // faster).
+  const int64_t n64 = count(TILE_64x64);
+  if ((n64 < 256 || (n64 == 256 && K >= 4096)) && K >= (int64_t)k4.bk * k4.kg) {
     // Eight K groups when the 32x32 tiles fit one round (the eight-group
     // workgroup takes 128 KiB of LDS, so one per CU) and each group still
     // walks at least four slices: the shorter chain of dependent slice loads

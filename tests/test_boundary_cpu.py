@@ -505,9 +505,11 @@ def test_k_split_tile_choice(lib):
     # too little K for four groups of 64
     assert _v(lib, M=512, N=512, K=255) == lib.GEMM_OK
     assert lib.gemm_last_path().startswith("mfma t64x64x64 ")
-    # 256 tiles of 64x64 already fill the chip
-    assert _v(lib, M=1024, N=1024, K=4096) == lib.GEMM_OK
+    # 256 tiles of 64x64 already fill the chip (unless K is long)
+    assert _v(lib, M=1024, N=1024, K=2048) == lib.GEMM_OK
     assert lib.gemm_last_path().startswith("mfma t64x64x64 ")
+    assert _v(lib, M=1024, N=1024, K=4096) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma t32x32x64k4 ")
     # whole tiles, but K not a multiple of 4 x 64: the groups' last steps are masked
     assert _v(lib, M=512, N=512, K=512 + 64) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith("ksplit4 masked"), lib.gemm_last_path()
