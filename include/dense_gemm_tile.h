@@ -98,14 +98,20 @@ extern "C" {
  * stream    hipStream_t cast to void*.
  *
  * Path: every call runs on the matrix cores. An operand whose base address or
- * row pitch is not a multiple of 16 bytes is read by the masked kernel with
- * the widest loads both allow (8, 4 or 2 bytes; slower, same result up to
- * rounding order); the VALU FMA path computes the same contraction with f32
+ * row pitch is not a multiple of 16 bytes is staged through registers with
+ * dword-aligned loads (or, on the small-tile kernels, read with the widest
+ * loads both allow); slower, same result up to rounding order. A call just
+ * past a multiple of the 256x256 tile may run as three launches (whole
+ * tiles, remainder rows, remainder columns); each element of D is still
+ * computed once. The VALU FMA path computes the same contraction with f32
  * FMAs and runs only when forced.
  *
  * Environment: GEMM_LOG=debug prints one line per call to stderr (path, tile,
  * reason); GEMM_FORCE_PATH=mfma|fma forces the matrix-core or the VALU path;
- * GEMM_FORCE_TILE=<tile name> picks a matrix-core tile configuration.
+ * GEMM_FORCE_TILE=<tile name> picks a matrix-core tile configuration;
+ * GEMM_RING_MODE=shared|ksplit2|deep|pp|ppdeep picks the form of the 128x128
+ * kernel; GEMM_STAGE_DEPTH=1|2 sets how far ahead a single staged operand is
+ * requested. Any forcing switch also keeps a call in one launch.
  */
 GEMM_API int gemm(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB,
          float alpha, float beta,
