@@ -12,9 +12,15 @@ namespace dgt {
 
 namespace {
 
+// Whole tiles: at most one workgroup per CU (one fits, by its LDS), each
+// walking its tiles in turn; edge tiles: one workgroup per tile.
+constexpr int kPingPongGrid = 256;
+
 template <class TAG, bool AMN, bool BMN, bool MASK>
 hipError_t launch_pingpong(const GemmArgs& a, hipStream_t s) {
-  const dim3 grid(a.tiles_m * a.tiles_n), block(PingPongCfg::THREADS);
+  const int ntiles = a.tiles_m * a.tiles_n;
+  const dim3 grid(MASK || ntiles < kPingPongGrid ? ntiles : kPingPongGrid),
+      block(PingPongCfg::THREADS);
   if (a.epi == EPI_BETA0)
     return launch_kernel(gemm_mfma_pingpong_kernel<TAG, EPI_BETA0, AMN, BMN, MASK>, grid, block,
                          s, a);

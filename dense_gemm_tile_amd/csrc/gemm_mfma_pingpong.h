@@ -504,24 +504,46 @@ __global__ void __launch_bounds__(PingPongCfg::THREADS) gemm_mfma_pingpong_kerne
   const int group = wave >> 2;
   const int wm = group, wn = wave & 3;
 
-  int tm, tn;
-  schedule_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-  const int m0 = tm * C::BM;
-  const int n0 = tn * C::BN;
+  // One tile: its loads, K loop and epilogue.
+  auto tile = [&](int t, int ln) {
+    int tm, tn;
+    schedule_tile(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int m0 = tm * C::BM;
+    const int n0 = tn * C::BN;
 
-  PingPongPipe<AMN, BMN, C::At::M, MASK> pipe;
-  pipe.init(p, smem, m0, n0, group, wave, lane, wm, wn);
+    PingPongPipe<AMN, BMN, C::At::M, MASK> pipe;
+    pipe.init(p, smem, m0, n0, group, wave, ln, wm, wn);
 
-  acc_t acc[C::TM][C::TN];
+    acc_t acc[C::TM][C::TN];
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
+      for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-      for (int v = 0; v < At::NACC; ++v) acc[i][j][v] = 0.0f;
+        for (int v = 0; v < At::NACC; ++v) acc[i][j][v] = 0.0f;
 
-  pp_mainloop<C, Tag, EPI, AMN, BMN, MASK>(acc, pipe, p.K, group);
-  store_tile<C, EPI, MASK>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, lane);
+    pp_mainloop<C, Tag, EPI, AMN, BMN, MASK>(acc, pipe, p.K, group);
+    store_tile<C, EPI, MASK>(acc, p, m0 + wm * C::WTM, n0 + wn * C::WTN, ln);
+  };
+  if constexpr (MASK) {
+    tile(blockIdx.x, lane);  // edge tiles: one tile per workgroup
+  } else {
+    // Whole tiles t = blockIdx.x, + gridDim.x, ...: one per workgroup when
+    // the grid has a workgroup per tile; with a grid of one workgroup per CU
+    // each workgroup walks its tiles in turn, so the next tile's first loads
+    // are requested right after this tile's D stores are issued instead of
+    // after they drain (a multiple of 8 workgroups keeps every tile on the
+    // XCD the scheduler's order assigns it).
+    const int ntiles = p.tiles_m * p.tiles_n;
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+      // The lane index, opaque to loop-invariant code motion: what depends
+      // on it is formed inside each tile's iteration, not held in registers
+      // across the K loop.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      tile(t, ln);
+    }
+  }
 }
 
 }  // namespace dgt
