@@ -665,7 +665,6 @@ __device__ inline void store_tile(typename Cfg::At::acc_t (&acc)[Cfg::TM][Cfg::T
                                   const GemmArgs& p, int r0, int c0, int lane,
                                   const WideC<Cfg>& pre = WideC<Cfg>{}, bool use_pre = false) {
   using At = typename Cfg::At;
-  constexpr int NG = At::NACC / 4;  // groups of 4 rows per atom and lane
   const float alpha = p.alpha, beta = p.beta;
   const int col_l = At::acc_col(lane);
   // The 16-byte form also serves masked tiles when N is a multiple of 4:
@@ -901,12 +900,12 @@ hipError_t launch_mfma_cfg(int dtype, bool ta, bool tb, bool masked, const GemmA
   if constexpr (MASKED_ONLY) return launch_epi<Cfg, TAG, TA_, TB_, true>(a, s);       \
   else return masked ? launch_epi<Cfg, TAG, TA_, TB_, true>(a, s)                     \
                      : launch_epi<Cfg, TAG, TA_, TB_, false>(a, s)
-#define DGT_LAUNCH_T(TAG)                          \
-  do {                                             \
-    if (!ta && !tb) DGT_LAUNCH_MASK(TAG, false, false); \
-    if (!ta && tb) DGT_LAUNCH_MASK(TAG, false, true);   \
-    if (ta && !tb) DGT_LAUNCH_MASK(TAG, true, false);   \
-    DGT_LAUNCH_MASK(TAG, true, true);                   \
+#define DGT_LAUNCH_T(TAG)                                   \
+  do {                                                      \
+    if (!ta && !tb) { DGT_LAUNCH_MASK(TAG, false, false); } \
+    if (!ta && tb) { DGT_LAUNCH_MASK(TAG, false, true); }   \
+    if (ta && !tb) { DGT_LAUNCH_MASK(TAG, true, false); }   \
+    DGT_LAUNCH_MASK(TAG, true, true);                       \
   } while (0)
   if (dtype == 0) DGT_LAUNCH_T(TagF16);
   DGT_LAUNCH_T(TagBF16);
