@@ -150,7 +150,8 @@ struct MfmaTileInfo {
 
 // Matrix-core tile configurations, largest first.
 enum MfmaTile : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x64 = 2, TILE_16x16 = 3,
-                      TILE_32x32K4 = 4, TILE_32x32K8 = 5, NUM_MFMA_TILES = 6 };
+                      TILE_32x32K4 = 4, TILE_32x32K8 = 5, TILE_64x64K4 = 6,
+                      NUM_MFMA_TILES = 7 };
 const MfmaTileInfo& mfma_tile_info(int tile);
 
 hipError_t launch_mfma(int tile, int dtype, bool transA, bool transB, bool masked,

@@ -166,7 +166,8 @@ std::string pitch_reason(const char* name, const void* ptr, int64_t ld, int vw, 
 // Tiles per round of the 256x256 grid (one workgroup per CU).
 constexpr int64_t kPpEdgeRound = 256;
 
-int choose_tile(int64_t M, int64_t N, int64_t K) {
+// whole64k4: the 64x64 four-group tile may be chosen (it runs whole tiles only).
+int choose_tile(int64_t M, int64_t N, int64_t K, bool whole64k4 = true) {
   auto count = [&](int t) {
     const MfmaTileInfo& ti = mfma_tile_info(t);
     return ((M + ti.bm - 1) / ti.bm) * ((N + ti.bn - 1) / ti.bn);
@@ -189,6 +190,13 @@ int choose_tile(int64_t M, int64_t N, int64_t K) {
   // 8192 x 8192 99 -> 48 us; at K = 1024-2048 the 64x64 tile was as fast or
   // faster).
   const int64_t n64 = count(TILE_64x64);
+  // One round of 64x64 tiles (192-256) with K >= 2048: those tiles with K
+  // split over four groups of 2x2 waves, when the call needs no masking
+  // (measured, same box: 128x8192x8192 NT 49.0 -> 36.6 us against 32x32
+  // tiles in four K groups, NN 63.2 -> 40.5; 1024^2 x 4096 27.9 -> 21.2;
+  // 1024^2 x 2048 16.4 -> 13.1 against 64x64 tiles; with 128 tiles of 64x64
+  // the 32x32 tiles stay faster: 64x8192x8192 28.7 against 36.4 us).
+  if (whole64k4 && n64 >= 192 && n64 <= 256 && K >= 2048) return TILE_64x64K4;
   if ((n64 < 256 || (n64 == 256 && K >= 4096)) && K >= (int64_t)k4.bk * k4.kg) {
     // Eight K groups when the 32x32 tiles fit one round (the eight-group
     // workgroup takes 128 KiB of LDS, so one per CU) and each group still
@@ -476,6 +484,12 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB
   // values, 32-bit offsets) when the grid fills its last round of 256 CUs to
   // at least 3/4 (forced 256x256 tiles skip that test); other calls that
   // need masking at that size take the 128x128 kernels.
+  // The 64x64 four-group tile runs whole tiles only; a call that needs
+  // masking takes the tile chosen without it.
+  if (tile == TILE_64x64K4 && plan.masked) {
+    tile = choose_tile(M, N, K, false);
+    plan_tile(tile);
+  }
   if (tile == TILE_256x256 && plan.masked) {
     const MfmaTileInfo& t256 = mfma_tile_info(TILE_256x256);
     const int64_t n256 = ((M + t256.bm - 1) / t256.bm) * ((N + t256.bn - 1) / t256.bn);

@@ -8,7 +8,7 @@ namespace dgt {
 
 hipError_t launch_mfma_128(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a,
                          hipStream_t s) {
-  return launch_mfma_cfg<Cfg128, true>(dtype, ta, tb, masked, a, s);
+  return launch_mfma_cfg<Cfg128, FORMS_MASKED>(dtype, ta, tb, masked, a, s);
 }
 
 }  // namespace dgt

@@ -15,6 +15,7 @@ const MfmaTileInfo kTiles[NUM_MFMA_TILES] = {
     info<Cfg16>("t16x16x64"),
     info<Cfg32k4>("t32x32x64k4"),
     info<Cfg32k8>("t32x32x64k8"),
+    info<Cfg64k4>("t64x64x64k4"),
 };
 }  // namespace
 
@@ -29,6 +30,7 @@ hipError_t launch_mfma(int tile, int dtype, bool ta, bool tb, bool masked, const
     case TILE_16x16: return launch_mfma_16(dtype, ta, tb, masked, a, s);
     case TILE_32x32K4: return launch_mfma_32k4(dtype, ta, tb, masked, a, s);
     case TILE_32x32K8: return launch_mfma_32k8(dtype, ta, tb, masked, a, s);
+    case TILE_64x64K4: return launch_mfma_64k4(dtype, ta, tb, masked, a, s);
     default: return hipErrorInvalidValue;
   }
 }

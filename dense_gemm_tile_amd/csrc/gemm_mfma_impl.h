@@ -890,14 +890,19 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
   }
 }
 
-// MASKED_ONLY: only the masked kernels are compiled (the configuration's
-// unmasked calls run elsewhere); an unmasked launch request then fails.
-template <class Cfg, bool MASKED_ONLY = false>
+// Forms compiled: FORMS_BOTH, FORMS_MASKED (the configuration's unmasked
+// calls run elsewhere) or FORMS_WHOLE (whole tiles only: the masked form
+// would not fit the registers the configuration leaves); a launch request
+// for a form not compiled fails.
+enum CfgForms : int { FORMS_BOTH = 0, FORMS_MASKED = 1, FORMS_WHOLE = 2 };
+template <class Cfg, int FORMS = FORMS_BOTH>
 hipError_t launch_mfma_cfg(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a,
                            hipStream_t s) {
-  if (MASKED_ONLY && !masked) return hipErrorInvalidValue;
+  if ((FORMS == FORMS_MASKED && !masked) || (FORMS == FORMS_WHOLE && masked))
+    return hipErrorInvalidValue;
 #define DGT_LAUNCH_MASK(TAG, TA_, TB_)                                                \
-  if constexpr (MASKED_ONLY) return launch_epi<Cfg, TAG, TA_, TB_, true>(a, s);       \
+  if constexpr (FORMS == FORMS_MASKED) return launch_epi<Cfg, TAG, TA_, TB_, true>(a, s);  \
+  else if constexpr (FORMS == FORMS_WHOLE) return launch_epi<Cfg, TAG, TA_, TB_, false>(a, s); \
   else return masked ? launch_epi<Cfg, TAG, TA_, TB_, true>(a, s)                     \
                      : launch_epi<Cfg, TAG, TA_, TB_, false>(a, s)
 #define DGT_LAUNCH_T(TAG)                                   \
@@ -921,6 +926,9 @@ using Cfg16 = TileCfg<16, 16, 1, 1, 16>;
 // one-wave groups.
 using Cfg32k4 = TileCfg<32, 32, 1, 1, 32, 4>;
 using Cfg32k8 = TileCfg<32, 32, 1, 1, 32, 8>;
+// Skinny grids with a long K: 64x64 tiles (2x2 waves), K split over four
+// groups of four waves.
+using Cfg64k4 = TileCfg<64, 64, 2, 2, 16, 4>;
 
 hipError_t launch_mfma_256(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mfma_128(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
@@ -928,5 +936,6 @@ hipError_t launch_mfma_64(int dtype, bool ta, bool tb, bool masked, const GemmAr
 hipError_t launch_mfma_16(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mfma_32k4(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mfma_32k8(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mfma_64k4(int dtype, bool ta, bool tb, bool masked, const GemmArgs& a, hipStream_t s);
 
 }  // namespace dgt

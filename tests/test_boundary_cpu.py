@@ -505,11 +505,19 @@ def test_k_split_tile_choice(lib):
     # too little K for four groups of 64
     assert _v(lib, M=512, N=512, K=255) == lib.GEMM_OK
     assert lib.gemm_last_path().startswith("mfma t64x64x64 ")
-    # 256 tiles of 64x64 already fill the chip (unless K is long)
+    # 256 tiles of 64x64 fill the chip: with K >= 2048 and whole tiles, K is
+    # split over four groups of 2x2 waves; with edges, 64x64 tiles (K < 4096)
+    # or 32x32 tiles in four K groups (K >= 4096); with a short K, 64x64
     assert _v(lib, M=1024, N=1024, K=2048) == lib.GEMM_OK
-    assert lib.gemm_last_path().startswith("mfma t64x64x64 ")
-    assert _v(lib, M=1024, N=1024, K=4096) == lib.GEMM_OK
-    assert lib.gemm_last_path().startswith("mfma t32x32x64k4 ")
+    assert lib.gemm_last_path() == "mfma t64x64x64k4 w2x2 a16x16x32 NN epi=beta0 ksplit4"
+    assert _v(lib, M=128, N=8192, K=8192, tB=1) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma t64x64x64k4 "), lib.gemm_last_path()
+    assert _v(lib, M=1000, N=1024, K=2048) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma t64x64x64 "), lib.gemm_last_path()
+    assert _v(lib, M=1000, N=1024, K=4096) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma t32x32x64k4 "), lib.gemm_last_path()
+    assert _v(lib, M=1024, N=1024, K=1024) == lib.GEMM_OK
+    assert lib.gemm_last_path().startswith("mfma t64x64x64 "), lib.gemm_last_path()
     # whole tiles, but K not a multiple of 4 x 64: the groups' last steps are masked
     assert _v(lib, M=512, N=512, K=512 + 64) == lib.GEMM_OK
     assert lib.gemm_last_path().endswith("ksplit4 masked"), lib.gemm_last_path()
