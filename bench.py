@@ -531,9 +531,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(output-tile sharding needs no collective; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(an M-split of the output tiles needs no collective, only a "
+              "broadcast of op(B)). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
