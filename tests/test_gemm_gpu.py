@@ -423,7 +423,8 @@ def test_exact_permutations_pin_lane_ownership(path, tA, tB, monkeypatch):
     wrong lane/row/column ownership in a fragment or accumulator shows up."""
     monkeypatch.setenv("GEMM_FORCE_PATH", path)
     rng = np.random.default_rng(11 + tA + 2 * tB)
-    for tile in (["t256x256x64", "t64x64x64", "t16x16x64"] if path == "mfma" else [None]):
+    for tile in (["t256x256x64", "t64x64x64", "t64x64x64k4", "t16x16x64"] if path == "mfma"
+                 else [None]):
         if tile:
             monkeypatch.setenv("GEMM_FORCE_TILE", tile)
         M = K = N = 256
@@ -634,6 +635,20 @@ def test_pingpong_path_slice_counts(dtype, layout, monkeypatch):
             assert "pingpong" in r.path, r.path
             r.check()
             r.check_padding_untouched()
+
+
+def test_pingpong_grid_walks_tiles_unevenly():
+    """Whole 256x256 tiles run on a grid of at most 256 workgroups, each
+    walking tiles blockIdx.x, + 256, ...: with 289 tiles the first 33
+    workgroups take two tiles and the rest one. Rows touching every tile band
+    and one element in every 64x64 block against the oracle; C == D."""
+    M = N = 17 * 256
+    cfg = workloads.Config("ppwalk", M, N, 256, "bf16", 0, 1, 1.0, 1.0, "uniform", 4352,
+                           inplace=True)
+    r = run(cfg)
+    assert r.path == "mfma t256x256x64 w2x4 a16x16x32 NT epi=acc+c pingpong", r.path
+    r.check(rows=sample_rows(M, 256, 1))
+    r.check_elements(block=64, seed=cfg.seed)
 
 
 PP_EDGE_SHAPES = {
