@@ -92,3 +92,26 @@ def test_random_large_calls(block, monkeypatch):
         rows = np.unique(np.concatenate([sample_rows(M, 256, 1, seed=i), np.arange(M - 8, M)]))
         r.check(rows=rows)
         r.check_padding_untouched()
+
+
+TILES = ["t16x16x64", "t64x64x64", "t128x128x64", "t256x256x64", "t32x32x64k4", "t32x32x64k8",
+         "t64x64x64k4"]
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_random_calls_on_each_tile(tile, monkeypatch):
+    """The same draws with the tile forced, so every tile's kernels (whole,
+    masked, staged, K-split) meet shapes the planner would not give them."""
+    for var in ("GEMM_FORCE_PATH", "GEMM_RING_MODE", "GEMM_STAGE_DEPTH"):
+        monkeypatch.delenv(var, raising=False)
+    monkeypatch.setenv("GEMM_FORCE_TILE", tile)
+    need_gpu()
+    rng = np.random.default_rng(3131 + TILES.index(tile))
+    for i in range(8):
+        M, N, K, dtype, tA, tB, alpha, beta, lda, ldb, ld, inplace = _draw(rng, "small")
+        cfg = workloads.Config(f"randT{tile}_{i}", M, N, K, dtype, tA, tB, alpha, beta,
+                               "uniform", 900 + 10 * TILES.index(tile) + i, lda=lda, ldb=ldb,
+                               ldc=ld, ldd=ld, inplace=inplace)
+        r = run(cfg)
+        r.check()
+        r.check_padding_untouched()
