@@ -115,3 +115,23 @@ def test_random_calls_on_each_tile(tile, monkeypatch):
         r = run(cfg)
         r.check()
         r.check_padding_untouched()
+
+
+def test_random_calls_forced_fma(monkeypatch):
+    """The same draws on the VALU-FMA fallback (16-bit operands; it has no
+    float32-operand form), which must meet the same bound."""
+    for var in ("GEMM_FORCE_TILE", "GEMM_RING_MODE", "GEMM_STAGE_DEPTH"):
+        monkeypatch.delenv(var, raising=False)
+    monkeypatch.setenv("GEMM_FORCE_PATH", "fma")
+    need_gpu()
+    rng = np.random.default_rng(2727)
+    for i in range(12):
+        M, N, K, dtype, tA, tB, alpha, beta, lda, ldb, ld, inplace = _draw(rng, "small")
+        dtype = dtype[4:] if dtype.startswith("f32_") else dtype  # 16-bit operands only
+        cfg = workloads.Config(f"randF_{i}", M, N, K, dtype, tA, tB, alpha, beta,
+                               "uniform", 1000 + i, lda=lda, ldb=ldb, ldc=ld, ldd=ld,
+                               inplace=inplace)
+        r = run(cfg)
+        assert r.path.startswith("fma"), r.path
+        r.check()
+        r.check_padding_untouched()
